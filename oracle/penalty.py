@@ -1,0 +1,102 @@
+"""Oracle for the contextual-penalty logit pass (penalty, temperature, top-p, min-p).
+
+Test infrastructure only (see the package docstring).
+
+Definition: TokenSwift summary §3.4 "Contextual Penalty and Random N-gram
+Selection" (a penalty on the tokens of the most recent W positions, instead of
+on every generated token), Appendix D.1 "Introduction of Different Sampling
+Algorithms" (top-p keeps the smallest set whose cumulative probability exceeds
+p, renormalised; min-p keeps tokens whose probability reaches p_base times the
+largest probability), Appendix F.1 (temperature). Hyper-parameters from the
+TokenSwift reproducibility checklist, Table 11 (penalty 1.2, penalty length
+1024, temperature 1.0, top-p 0.9, min-p 0.05).
+
+Readings taken where the pages are silent:
+
+* Penalty form (repetition penalty of the CTRL line of work, listed in the
+  citation map): for each DISTINCT id w in the window, a positive logit is
+  divided by theta and a non-positive one multiplied by theta. Ids outside
+  [0, V) are padding and ignored.
+* Order: penalty, then temperature, then the top-p and min-p masks, which
+  are intersected (min-p is scale-free, so applying it to the top-p
+  renormalised distribution gives the same set).
+* Top-p boundary: with tokens ordered by (probability desc, id asc) and E(i)
+  the mass strictly before token i, keep i iff E(i) <= top_p.
+* Min-p boundary is inclusive: keep i iff p_i >= min_p * max(p).
+* Sampling: with caller-supplied u in [0,1), the token is the smallest id t
+  whose cumulative renormalised probability (ascending ids) exceeds u.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass
+class PenaltyResult:
+    z: np.ndarray        # float64 [rows][V]; penalised, tempered logits
+    p: np.ndarray        # float64 [rows][V]; softmax(z)
+    keep: np.ndarray     # bool [rows][V]
+    probs: np.ndarray    # float64 [rows][V]; renormalised kept probabilities
+    token: np.ndarray    # int64 [rows]; -1 when no u was given
+    excl_mass: np.ndarray  # float64 [rows][V]; E(i), mass strictly before i
+    ratio: np.ndarray    # float64 [rows][V]; p_i / max p
+
+
+def apply_penalty(x, window_ids, V, theta):
+    """Windowed repetition penalty on one row (float64)."""
+    y = np.array(x, dtype=np.float64)
+    ids = np.asarray(window_ids, dtype=np.int64)
+    ids = ids[(ids >= 0) & (ids < V)]
+    w = np.unique(ids)
+    vals = y[w]
+    y[w] = np.where(vals > 0, vals / theta, vals * theta)
+    return y
+
+
+def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None):
+    """Run the logit pass on every row.
+
+    logits: float [rows][V]. window: int [rows][W] or [W] (shared by all rows).
+    u: optional float [rows] in [0, 1).
+    """
+    x = np.asarray(logits, dtype=np.float64)
+    rows, V = x.shape
+    win = np.asarray(window, dtype=np.int64)
+    if win.ndim == 1:
+        win = np.broadcast_to(win, (rows, win.shape[0]))
+    if not (penalty > 0 and temperature > 0 and 0 <= top_p <= 1 and 0 <= min_p <= 1):
+        raise ValueError("parameter out of range")
+
+    z = np.empty_like(x)
+    p = np.empty_like(x)
+    keep = np.zeros(x.shape, dtype=bool)
+    probs = np.zeros_like(x)
+    token = np.full(rows, -1, dtype=np.int64)
+    excl = np.empty_like(x)
+    ratio = np.empty_like(x)
+    ids = np.arange(V, dtype=np.int64)
+    for r in range(rows):
+        y = apply_penalty(x[r], win[r], V, float(penalty))
+        zr = y / float(temperature)
+        e = np.exp(zr - zr.max())
+        pr = e / e.sum()
+        # (p desc, id asc) order; E(i) = mass strictly before i in that order.
+        order = np.lexsort((ids, -pr))
+        csum = np.cumsum(pr[order])
+        e_sorted = np.concatenate([[0.0], csum[:-1]])
+        er = np.empty(V)
+        er[order] = e_sorted
+        keep_top = er <= top_p
+        keep_min = pr >= min_p * pr.max()
+        kr = keep_top & keep_min
+        qr = np.where(kr, pr, 0.0)
+        qr = qr / qr.sum()
+        z[r], p[r], keep[r], probs[r], excl[r] = zr, pr, kr, qr, er
+        ratio[r] = pr / pr.max()
+        if u is not None:
+            cdf = np.cumsum(qr)
+            hits = np.nonzero(cdf > float(u[r]))[0]
+            # u < 1 and the kept mass sums to 1; the guard covers rounding.
+            token[r] = int(hits[0]) if len(hits) else int(np.nonzero(kr)[0][-1])
+    return PenaltyResult(z=z, p=p, keep=keep, probs=probs, token=token, excl_mass=excl, ratio=ratio)
