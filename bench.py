@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-step hot path on one MI355X.
+
+A step is one pass of the whole hot path over every layer of the model shape,
+each layer on its own buffers (so the 256 MB last-level cache cannot hold the
+working set):
+    tree verification attention (full cache)   x layers
+    draft attention (partial cache)            x layers
+    partial-KV selection (score/select/gather) x layers
+    penalty / temperature / top-p / min-p over the step's logits rows
+The headline value is the verification attention time per layer-step,
+measured with HIP events around the layers' verification launches on the
+stream the library launches on. Inputs are seeded synthetic tensors of the
+model's shapes, resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8b] [--T 24] [--n-ctx 100000]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="8b")
+    ap.add_argument("--T", type=int, default=None, help="tree nodes (default: the workload's)")
+    ap.add_argument("--n-ctx", type=int, default=None)
+    ap.add_argument("--n-split", type=int, default=0)
+    ap.add_argument("--verify-only", action="store_true", help="time only the verification launches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def verify_bytes(Hq, Hkv, d, n_ctx, T):
+    """Algorithmic bytes of one verification launch: K and V over n_ctx + T rows
+    (bf16), the queries (bf16) and the fp32 output."""
+    return 2 * Hkv * (n_ctx + T) * d * 2 + Hq * T * d * 2 + Hq * T * d * 4
+
+
+def cpu_baseline(cfg, T, n_ctx, budget_s):
+    """Time the float64 oracle on the host on a bounded sample of one layer:
+    as many KV-head groups as fit in ~budget_s, scaled to the whole layer."""
+    import numpy as np
+    from oracle import bf16_to_f64, verify_attention
+    from synth import attention_inputs, tree_parent
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - reporting only
+        threads = len(os.sched_getaffinity(0))
+    parent = tree_parent("tokenswift" if T > 4 else "chain", T)
+    G = cfg["Hq"] // cfg["Hkv"]
+    x = attention_inputs(cfg["seed"], G, 1, cfg["d"], n_ctx, T)  # one KV head and its query group
+    per_group = []
+    t_start = time.perf_counter()
+    while not per_group or (time.perf_counter() - t_start < budget_s and len(per_group) < cfg["Hkv"]):
+        t0 = time.perf_counter()
+        verify_attention(bf16_to_f64(x["q"]), bf16_to_f64(x["k"]), bf16_to_f64(x["v"]), n_ctx, parent)
+        per_group.append(time.perf_counter() - t0)
+    us_layer = float(np.mean(per_group)) * cfg["Hkv"] * 1e6
+    return {
+        "value": round(us_layer, 1),
+        "unit": "us/layer-step",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(per_group)} KV-head group(s) of one layer (G={G} query heads x T={T}, {n_ctx} context rows, "
+                  f"float64 NumPy), mean time per group x {cfg['Hkv']} groups",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of this path "
+              "is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_kv_attention_amd as ts
+    from synth import CONFIGS, tree_parent
+
+    cfg = dict(CONFIGS[args.config])
+    T = args.T or cfg["T"]
+    n_ctx = args.n_ctx or cfg["n_ctx"]
+    Hq, Hkv, d, layers = cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["layers"]
+    Tq = 4                                   # drafting: the accepted token + 3 heads' tokens
+    n_sink, budget, n_recent = cfg["n_sink"], cfg["budget"], cfg["n_recent"]
+    n_part = n_sink + budget + n_recent
+    V, W = cfg["V"], cfg["W"]
+    rows_logits = T + Tq
+    parent = tree_parent("chain" if T <= 4 else "tokenswift", T)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg["seed"] * 1000)
+
+    def randn(shape, dtype=torch.bfloat16):
+        return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(dtype)
+
+    L = []
+    for _ in range(layers):
+        k = randn((Hkv, n_ctx + T, d))
+        if "k_scale" in cfg:
+            lo, hi = cfg["k_scale"]
+            k = (k.float() * (lo + (hi - lo) * torch.rand((Hkv, 1, d), generator=gen, device=dev))).to(torch.bfloat16)
+        L.append(dict(
+            q=randn((Hq, T, d)), k=k, v=randn((Hkv, n_ctx + T, d)),
+            qd=randn((Hq, Tq, d)),
+            kp=randn((Hkv, n_part + Tq, d)), vp=randn((Hkv, n_part + Tq, d)),
+            kp2=torch.empty((Hkv, n_part + Tq, d), dtype=torch.bfloat16, device=dev),
+            vp2=torch.empty((Hkv, n_part + Tq, d), dtype=torch.bfloat16, device=dev),
+            out=torch.empty((Hq, T, d), dtype=torch.float32, device=dev),
+            outd=torch.empty((Hq, Tq, d), dtype=torch.float32, device=dev),
+            sel=torch.empty((Hkv, budget), dtype=torch.int32, device=dev),
+        ))
+    logits = randn((rows_logits, V), torch.float32) * cfg.get("sigma", 2.0)
+    window = torch.randint(0, V, (rows_logits, W), generator=gen, device=dev, dtype=torch.int32)
+    u = torch.rand(rows_logits, generator=gen, device=dev)
+    lib = ts.lib()
+    ws_v = torch.empty(max(1, lib.ts_verify_attn_workspace_size(n_ctx, T, Hq, Hkv, d, args.n_split)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, lib.ts_draft_attn_workspace_size(n_part, Tq, Hq, Hkv, d, 0)), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(1, lib.ts_partial_kv_select_workspace_size(n_ctx, T, Hq, Hkv, d, budget)), dtype=torch.uint8, device=dev)
+    z_out = torch.empty_like(logits)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record(stream)
+        for Ld in L:
+            ts.verify_attn(Ld["q"], Ld["k"], Ld["v"], n_ctx, parent, n_split=args.n_split, out=Ld["out"], ws=ws_v)
+        if e:
+            e[1].record(stream)
+        if not args.verify_only:
+            for Ld in L:
+                ts.draft_attn(Ld["qd"], Ld["kp"], Ld["vp"], n_part, out=Ld["outd"], ws=ws_d)
+        if e:
+            e[2].record(stream)
+        if not args.verify_only:
+            for Ld in L:
+                ts.partial_kv_select(Ld["q"], Ld["k"], Ld["v"], n_ctx, n_sink, budget, n_recent, k_part=Ld["kp2"],
+                                     v_part=Ld["vp2"], sel_idx=Ld["sel"], ws=ws_s)
+        if e:
+            e[3].record(stream)
+        if not args.verify_only:
+            ts.penalty_sample(logits, window, 1.2, 1.0, 0.9, 0.05, u=u, out=z_out)
+        if e:
+            e[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def avg(i, j):
+        return sum(ev[s][i].elapsed_time(ev[s][j]) for s in range(args.steps)) / args.steps * 1e3  # us
+
+    verify_us = avg(0, 1) / layers
+    draft_us = avg(1, 2) / layers
+    select_us = avg(2, 3) / layers
+    penalty_us = avg(3, 4)
+    step_ms = avg(0, 4) / 1e3
+    vb = verify_bytes(Hq, Hkv, d, n_ctx, T)
+    achieved = vb / (verify_us * 1e-6) / 1e9
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "verify_attn_traffic.json")
+    if os.path.exists(tpath):
+        try:
+            tj = json.load(open(tpath))
+            key = f"{args.config}_L{n_ctx}_T{T}"
+            if tj.get("kernel_source_sha") == _attn_source_sha() and key in tj.get("bytes_per_launch", {}):
+                traffic = tj["bytes_per_launch"][key]
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": "tree-verify attn us/layer-step @100K ctx (8B GQA); achieved HBM GB/s vs peak",
+        "value": round(verify_us, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}-class {'GQA' if Hq != Hkv else 'MHA'} tree verification, "
+                               f"{Hq} q / {Hkv} kv heads, d={d}, {n_ctx} context rows, T={T} tree nodes, {layers} layers",
+                   "global_batch": 1, "seq_len": n_ctx, "tree_nodes": T, "layers": layers,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "kernels_us": {"verify_per_layer": round(verify_us, 3), "draft_per_layer": round(draft_us, 3),
+                       "select_per_layer": round(select_us, 3), "penalty_per_step": round(penalty_us, 3),
+                       "verify_bytes_per_launch": vb},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, T, n_ctx, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def _attn_source_sha():
+    import hashlib
+    p = os.path.join(ROOT, "long_kv_attention_amd", "csrc", "attn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * tokenswift.h -- C ABI of the MI355X (gfx950) hot-path library libtokenswift.so.
+ *
+ * The library runs the per-step, data-parallel work of TokenSwift-style
+ * lossless ultra-long generation on one GPU: tree-masked verification
+ * attention over the full KV cache, draft attention over the partial cache,
+ * the dynamic partial-KV update, and the contextual-penalty logit pass.
+ *
+ * Citations name pages and sections, not files:
+ *   "TokenSwift summary"  = the paperlayer.ai source-linked summary of
+ *                           "TokenSwift: Lossless Acceleration of Ultra Long
+ *                           Sequence Generation" (arXiv 2502.18890v2);
+ *                           section numbers are the paper's.
+ *   "Reproducibility checklist" = the acmrep2026 page on the same paper.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers are caller-owned DEVICE memory unless marked (host). The library
+ *   never allocates, frees or synchronises device memory and keeps no mutable
+ *   global state except a per-device property cache; calls on different
+ *   streams may run concurrently as long as their buffers do not overlap.
+ * - bf16 tensors are passed as uint16_t bit patterns.
+ * - A KV cache element (g, j, c) -- KV head g, cache row j, channel c -- sits
+ *   at  base[g * s_head + j * s_pos + c]  (strides in elements; channels
+ *   contiguous). s_pos >= d, s_head >= rows * s_pos is not required but the
+ *   rows of different heads must not overlap. Base pointers and strides must
+ *   keep every row 16-byte aligned.
+ * - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *   default stream) and runs asynchronously; the return code reports only
+ *   host-side validation and launch errors.
+ * - Every argument is validated on the host BEFORE anything is launched; on
+ *   error nothing is enqueued, outputs are untouched, and ts_last_error()
+ *   returns a message for the calling thread.
+ * - Workspace: each entry point has a *_workspace_size() query that depends
+ *   on shapes only (no device needed). Pass at least that many bytes, 256-byte
+ *   aligned. Workspace contents need not be initialised and are scratch.
+ */
+#ifndef TOKENSWIFT_H
+#define TOKENSWIFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define TS_OK          0
+#define TS_EINVAL     (-1) /* null pointer, bad stride/alignment/shape/parameter, bad parent[] */
+#define TS_ENOTSUP    (-2) /* a shape the kernels do not handle (d not 64/128, T > 64, ...)   */
+#define TS_EWORKSPACE (-3) /* workspace smaller than the *_workspace_size() query            */
+#define TS_EHIP       (-4) /* the HIP runtime reported an error while launching               */
+
+/* Largest tree / draft-chain size: one 64-bit ancestor mask per node. */
+#define TS_MAX_TREE 64
+
+/*
+ * ts_verify_attn -- tree-masked verification attention over the FULL cache.
+ *
+ * TokenSwift summary §3.1 (with Figure 2): the target model checks the whole
+ * draft in one forward pass using the full KV cache; Appendix E "Tree-Based
+ * Attention": the draft is a tree of candidate continuations and each tree
+ * token attends only to its predecessors; §3.3: under GQA the query heads of
+ * one KV head form a group.
+ *
+ * For every query head h (KV head g = h / (Hq/Hkv)) and tree node i:
+ *   out[h][i][:] = sum_{j in Vis(i)} softmax_j(scale * q[h][i] . k[g][j]) * v[g][j]
+ *   Vis(i) = committed rows 0..n_ctx-1  U  {n_ctx + a : a is i or an ancestor of i}
+ *
+ *   q       [Hq][T][d] bf16, contiguous.
+ *   k, v    caches (layout above) holding n_ctx committed rows followed by the
+ *           T tree nodes' own keys/values at rows n_ctx..n_ctx+T-1 (the caller
+ *           writes them before the call, as in any decode step).
+ *   parent  (host) [T] int32: parent[0] = -1 (root), 0 <= parent[i] < i.
+ *   Hq, Hkv Hq % Hkv == 0.      d: 64 or 128.      1 <= T <= 64.  n_ctx >= 0.
+ *   scale   softmax scale; <= 0 selects 1/sqrt(d).
+ *   out     [Hq][T][d] float32, contiguous (row (h, i) at (h*T + i)*d).
+ *   n_split number of cache chunks per KV head processed in parallel before
+ *           a log-sum-exp merge; 0 = automatic. Results agree for every value
+ *           up to float rounding.
+ *   ws      workspace of ts_verify_attn_workspace_size(...) bytes.
+ *
+ * Precision: q.k in bf16 x bf16 with float32 accumulation; softmax in
+ * float32; probabilities and v enter the p.v product as float16 with float32
+ * accumulation, so |v| must stay below 65504 (bf16 values beyond the float16
+ * range are not supported).
+ */
+int ts_verify_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                   int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t T,
+                   const int32_t* parent, int32_t Hq, int32_t Hkv, int32_t d,
+                   float scale, float* out, int32_t n_split,
+                   void* ws, size_t ws_bytes, void* stream);
+
+size_t ts_verify_attn_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv,
+                                     int32_t d, int32_t n_split);
+
+/*
+ * ts_draft_attn -- draft attention over the PARTIAL cache.
+ *
+ * TokenSwift summary §3.1 and §3.3: drafting runs the target model with a
+ * partial KV cache of fixed budget. The Tq new tokens of a drafting pass form
+ * a chain: token t sees the n_part partial rows and its own rows
+ * n_part..n_part+t. This is ts_verify_attn with parent[t] = t-1.
+ *
+ *   q               [Hq][Tq][d] bf16.
+ *   k_part, v_part  partial caches (layout above; strides s_head, s_pos) with
+ *                   n_part rows then the Tq new tokens' rows.
+ *   1 <= Tq <= 64.  Other arguments as for ts_verify_attn.
+ */
+int ts_draft_attn(const uint16_t* q, const uint16_t* k_part, const uint16_t* v_part,
+                  int64_t s_head, int64_t s_pos, int32_t n_part, int32_t Tq,
+                  int32_t Hq, int32_t Hkv, int32_t d, float scale, float* out,
+                  int32_t n_split, void* ws, size_t ws_bytes, void* stream);
+
+size_t ts_draft_attn_workspace_size(int32_t n_part, int32_t Tq, int32_t Hq, int32_t Hkv,
+                                    int32_t d, int32_t n_split);
+
+/*
+ * ts_partial_kv_select -- dynamic partial-KV update: score, select, gather.
+ *
+ * TokenSwift summary §3.3 "Dynamic KV Cache Management" (and §2): the
+ * drafting cache has a fixed budget, always keeps the initial |S| pairs, and
+ * replaces less important pairs as generation proceeds; importance is a
+ * query-key dot product, and under GQA the queries of a group are kept apart
+ * (keys are not replicated) and their scores added up.
+ *
+ *   score   sigma[g][j] = sum_{h in group g} sum_{t<T} q[h][t] . k[g][j]
+ *           for committed rows j < n_ctx (float32 accumulation).
+ *   C       candidates = rows [n_sink, n_ctx - n_recent) (empty if n_ctx <=
+ *           n_sink + n_recent). B' = min(budget, |C|).
+ *   select  per KV head, the B' candidates first in (score desc, row asc).
+ *   sel_idx [Hkv][budget] int32: selected rows, ascending, then -1 padding.
+ *   gather  partial rows = [0, min(n_sink, n_ctx)) U selected U
+ *           [max(n_sink, n_ctx - n_recent), n_ctx), ascending; row r of the
+ *           partial cache of head g (k_part/v_part, strides sp_head, sp_pos)
+ *           receives that row's key and value.
+ *   n_part_out (host) receives the number of partial rows (the same for every
+ *           head); it is computed on the host from the scalars.
+ *   scores  optional [Hkv][n_ctx] float32 output of sigma (NULL = not written).
+ *
+ *   q [Hq][T][d] bf16 contiguous, 1 <= T <= 64; d 64 or 128; n_sink, budget,
+ *   n_recent >= 0. The partial cache must not overlap the full cache.
+ */
+int ts_partial_kv_select(const uint16_t* q, int32_t T, const uint16_t* k, const uint16_t* v,
+                         int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t Hq, int32_t Hkv,
+                         int32_t d, int32_t n_sink, int32_t budget, int32_t n_recent,
+                         int32_t* sel_idx, uint16_t* k_part, uint16_t* v_part,
+                         int64_t sp_head, int64_t sp_pos, int32_t* n_part_out, float* scores,
+                         void* ws, size_t ws_bytes, void* stream);
+
+size_t ts_partial_kv_select_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv,
+                                           int32_t d, int32_t budget);
+
+/*
+ * ts_penalty_sample -- contextual penalty, temperature, min-p and top-p.
+ *
+ * TokenSwift summary §3.4: a repetition penalty restricted to the tokens of
+ * the most recent W positions; Appendix D.1: top-p keeps the smallest set of
+ * tokens whose cumulative probability exceeds top_p, min-p keeps tokens whose
+ * probability reaches min_p times the largest; Reproducibility checklist,
+ * Table 11: penalty 1.2, penalty length 1024, temperature 1.0, top-p 0.9,
+ * min-p 0.05.
+ *
+ * Per row r of logits [rows][V] float32:
+ *   1. for each DISTINCT id w of window[r] with 0 <= w < V (other ids are
+ *      padding): x_w <- x_w / penalty if x_w > 0, else x_w * penalty;
+ *   2. z = x / temperature  -> logits_out (may alias logits);
+ *   3. p = softmax(z);
+ *   4. keep_top(i) <=> mass of the tokens before i in (p desc, id asc) order
+ *      <= top_p;  keep_min(i) <=> p_i >= min_p * max(p);  keep = both;
+ *   5. probs = p * keep / sum(p * keep)          (optional output);
+ *   6. token = smallest id t with sum_{i<=t} probs_i > u[r]  (optional; needs u).
+ *
+ *   window  [rows][W] int32 with row stride window_stride, or one row shared by
+ *           every row when window_stride == 0. W may be 0.
+ *   penalty > 0, temperature > 0, 0 <= top_p <= 1, 0 <= min_p <= 1.
+ *   keep    [rows][V] uint8 (1 = kept) or NULL.    probs [rows][V] float32 or NULL.
+ *   u       [rows] float32 in [0, 1) or NULL.       token [rows] int32 or NULL
+ *           (token requires u).
+ *   1 <= V <= 262144; rows >= 1.
+ */
+int ts_penalty_sample(const float* logits, int32_t rows, int32_t V,
+                      const int32_t* window, int32_t W, int64_t window_stride,
+                      float penalty, float temperature, float top_p, float min_p,
+                      float* logits_out, uint8_t* keep, float* probs,
+                      const float* u, int32_t* token,
+                      void* ws, size_t ws_bytes, void* stream);
+
+size_t ts_penalty_sample_workspace_size(int32_t rows, int32_t V);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* ts_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int ts_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENSWIFT_H */

@@ -1,0 +1,28 @@
+"""MI355X (gfx950) hot path of TokenSwift-style ultra-long generation.
+
+A thin ctypes binding over the C ABI of ``libtokenswift.so`` (declared in
+``include/tokenswift.h``): it marshals torch tensors (device memory and the
+current stream) into pointers and sizes. Every step of the computation runs in
+the library's HIP kernels; nothing here computes, and there is no fallback: if
+the library is missing, every call raises.
+"""
+
+from .binding import (
+    TSError,
+    draft_attn,
+    lib,
+    lib_path,
+    partial_kv_select,
+    penalty_sample,
+    verify_attn,
+)
+
+__all__ = [
+    "TSError",
+    "lib",
+    "lib_path",
+    "verify_attn",
+    "draft_attn",
+    "partial_kv_select",
+    "penalty_sample",
+]

@@ -1,0 +1,199 @@
+"""ctypes binding of libtokenswift.so (argument marshalling only).
+
+Tensors are torch tensors on the GPU; bf16 tensors are handed to the library
+as their raw 16-bit patterns. Outputs and workspaces are allocated here with
+torch (device memory plumbing) unless the caller passes them in.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libtokenswift.so"
+TS_OK = 0
+CODES = {-1: "TS_EINVAL", -2: "TS_ENOTSUP", -3: "TS_EWORKSPACE", -4: "TS_EHIP"}
+
+_lib = None
+
+c_i32, c_i64, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+_SIGNATURES = {
+    "ts_verify_attn": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32p, c_i32, c_i32, c_i32,
+                               c_f32, c_vp, c_i32, c_vp, c_sz, c_vp]),
+    "ts_verify_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "ts_draft_attn": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp,
+                              c_i32, c_vp, c_sz, c_vp]),
+    "ts_draft_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "ts_partial_kv_select": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                     c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32p, c_vp, c_vp, c_sz,
+                                     c_vp]),
+    "ts_partial_kv_select_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "ts_penalty_sample": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_i32, c_i64, c_f32, c_f32, c_f32, c_f32, c_vp, c_vp,
+                                  c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "ts_penalty_sample_workspace_size": (c_sz, [c_i32, c_i32]),
+    "ts_last_error": (ctypes.c_char_p, []),
+    "ts_abi_version": (c_i32, []),
+}
+
+
+class TSError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} returned {code} ({CODES.get(code, '?')}): {msg}")
+        self.code = code
+
+
+def lib_path():
+    return os.path.join(HERE, LIB_NAME)
+
+
+def lib():
+    """Load libtokenswift.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m long_kv_attention_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, rc):
+    if rc != TS_OK:
+        raise TSError(fn, rc, lib().ts_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _cache_strides(k, v):
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("caches must be bfloat16")
+    if k.dim() != 3 or k.stride() != v.stride() or k.stride(2) != 1:
+        raise ValueError("caches must be [Hkv][rows][d] with contiguous channels and equal strides")
+    return k.stride(0), k.stride(1)
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes, need {nbytes}")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def verify_attn(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, ws=None, stream=None):
+    """Tree verification attention (ts_verify_attn). q [Hq][T][d] bf16; k, v [Hkv][rows][d] bf16."""
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    s_head, s_pos = _cache_strides(k, v)
+    par = (ctypes.c_int32 * T)(*[int(x) for x in parent])
+    if out is None:
+        out = torch.empty((Hq, T, d), dtype=torch.float32, device=q.device)
+    L = lib()
+    need = L.ts_verify_attn_workspace_size(n_ctx, T, Hq, Hkv, d, n_split)
+    wst = _workspace(need, q.device, ws)
+    rc = L.ts_verify_attn(_ptr(q), _ptr(k), _ptr(v), s_head, s_pos, n_ctx, T, par, Hq, Hkv, d, float(scale),
+                          _ptr(out), n_split, _ptr(wst), need, _stream(stream))
+    _check("ts_verify_attn", rc)
+    return out
+
+
+def draft_attn(q, k_part, v_part, n_part, scale=0.0, n_split=0, out=None, ws=None, stream=None):
+    """Draft attention over the partial cache (ts_draft_attn)."""
+    Hq, Tq, d = q.shape
+    Hkv = k_part.shape[0]
+    s_head, s_pos = _cache_strides(k_part, v_part)
+    if out is None:
+        out = torch.empty((Hq, Tq, d), dtype=torch.float32, device=q.device)
+    L = lib()
+    need = L.ts_draft_attn_workspace_size(n_part, Tq, Hq, Hkv, d, n_split)
+    wst = _workspace(need, q.device, ws)
+    rc = L.ts_draft_attn(_ptr(q), _ptr(k_part), _ptr(v_part), s_head, s_pos, n_part, Tq, Hq, Hkv, d,
+                         float(scale), _ptr(out), n_split, _ptr(wst), need, _stream(stream))
+    _check("ts_draft_attn", rc)
+    return out
+
+
+def partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, k_part=None, v_part=None, want_scores=False,
+                      sel_idx=None, scores=None, extra_rows=0, ws=None, stream=None):
+    """Score, select and gather the partial cache (ts_partial_kv_select).
+
+    Freshly allocated partial caches hold n_sink + budget + n_recent rows plus
+    ``extra_rows`` (room for the draft tokens' own keys/values).
+    Returns (sel_idx [Hkv][budget] int32, k_part, v_part, n_part, scores or None).
+    """
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    s_head, s_pos = _cache_strides(k, v)
+    dev = q.device
+    if k_part is None:
+        k_part = torch.empty((Hkv, max(n_sink + budget + n_recent + extra_rows, 1), d), dtype=torch.bfloat16,
+                             device=dev)
+    if v_part is None:
+        v_part = torch.empty_like(k_part)
+    sp_head, sp_pos = _cache_strides(k_part, v_part)
+    if sel_idx is None:
+        sel_idx = torch.empty((Hkv, max(budget, 1)), dtype=torch.int32, device=dev)
+    if want_scores and scores is None:
+        scores = torch.empty((Hkv, max(n_ctx, 1)), dtype=torch.float32, device=dev)
+    L = lib()
+    need = L.ts_partial_kv_select_workspace_size(n_ctx, T, Hq, Hkv, d, budget)
+    wst = _workspace(need, dev, ws)
+    n_part = ctypes.c_int32(-1)
+    rc = L.ts_partial_kv_select(_ptr(q), T, _ptr(k), _ptr(v), s_head, s_pos, n_ctx, Hq, Hkv, d, n_sink, budget,
+                                n_recent, _ptr(sel_idx), _ptr(k_part), _ptr(v_part), sp_head, sp_pos,
+                                ctypes.byref(n_part), _ptr(scores if want_scores else None), _ptr(wst), need,
+                                _stream(stream))
+    _check("ts_partial_kv_select", rc)
+    return sel_idx[:, :budget], k_part, v_part, n_part.value, (scores if want_scores else None)
+
+
+def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None, want_keep=True, want_probs=True,
+                   want_token=None, out=None, ws=None, stream=None):
+    """Contextual penalty + temperature + top-p + min-p (ts_penalty_sample).
+
+    logits [rows][V] fp32; window [rows][W] or [W] int32 (shared). Returns
+    (z, keep or None, probs or None, token or None).
+    """
+    rows, V = logits.shape
+    dev = logits.device
+    if window is None or window.numel() == 0:
+        W, wstride, wptr = 0, 0, None
+    elif window.dim() == 1:
+        W, wstride, wptr = window.shape[0], 0, window
+    else:
+        if window.shape[0] != rows:
+            raise ValueError("window must have one row per logits row, or be 1-D (shared)")
+        W, wstride, wptr = window.shape[1], window.stride(0), window
+    if wptr is not None and (wptr.dtype != torch.int32 or wptr.stride(-1) != 1):
+        raise ValueError("window must be int32 with contiguous rows")
+    want_token = (u is not None) if want_token is None else want_token
+    z = torch.empty_like(logits) if out is None else out
+    keep = torch.empty((rows, V), dtype=torch.uint8, device=dev) if want_keep else None
+    probs = torch.empty((rows, V), dtype=torch.float32, device=dev) if want_probs else None
+    token = torch.empty(rows, dtype=torch.int32, device=dev) if want_token else None
+    L = lib()
+    need = L.ts_penalty_sample_workspace_size(rows, V)
+    wst = _workspace(need, dev, ws)
+    rc = L.ts_penalty_sample(_ptr(logits), rows, V, _ptr(wptr), W, wstride, float(penalty), float(temperature),
+                             float(top_p), float(min_p), _ptr(z), _ptr(keep), _ptr(probs), _ptr(u), _ptr(token),
+                             _ptr(wst), need, _stream(stream))
+    _check("ts_penalty_sample", rc)
+    return z, keep, probs, token

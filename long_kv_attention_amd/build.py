@@ -1,0 +1,63 @@
+"""Build libtokenswift.so in-tree with hipcc for gfx950.
+
+Usage: python -m long_kv_attention_amd.build [-v]
+"""
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_NAME = "libtokenswift.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = ["csrc/api.cpp", "csrc/attn.hip", "csrc/select.hip", "csrc/penalty.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+# Packed fp32 VALU instructions stay disabled (the compiler would otherwise
+# form them from scalar or float2 code).
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the softmax rescale touches the accumulators with
+    # VALU ops, which would otherwise force AGPR<->VGPR copies every tile.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def _compile(src, obj):
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    return r.returncode, " ".join(cmd), err
+
+
+def build(verbose=False, jobs=None):
+    out_dir = os.path.join(ROOT, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = [os.path.join(out_dir, os.path.basename(s) + ".o") for s in SOURCES]
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda so: _compile(*so), zip(SOURCES, objs)))
+    for rc, cmd, err in results:
+        if verbose or rc:
+            print(cmd)
+            if err.strip():
+                print(err)
+        if rc:
+            raise RuntimeError(f"compilation failed: {cmd}")
+    tmp = LIB_PATH + ".tmp"
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError(f"link failed: {' '.join(link)}\n{r.stderr}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,549 @@
+// Split-KV tree-masked attention for CDNA4 (gfx950): verification over the
+// full cache and drafting over the partial cache share these kernels.
+//
+// What is computed (TokenSwift summary §3.1 with Figure 2, §3.3, Appendix E
+// "Tree-Based Attention"): for every query head h of KV head g and every tree
+// node i, softmax-weighted values over the committed rows plus the node's own
+// ancestors-or-self among the tree rows appended after the context.
+//
+// Work decomposition
+//   grid.x  = cache chunk ("split") of one KV head, grid.y = KV head,
+//   grid.z  = block of query rows when a group has more rows than one
+//             workgroup holds.
+//   The M = G*T query rows of a KV head (G query heads x T tree nodes) are
+//   cut into 16-row MFMA tiles; wave w owns TPW consecutive row tiles, so the
+//   K/V tile staged in LDS once serves every head of the group and every node.
+//   Per KV tile of TN positions:
+//     S^T = K Q^T     v_mfma_f32_16x16x32_bf16 (A = K rows from LDS,
+//                     B = Q kept in registers); lane holds 4 positions of one
+//                     query row, so row statistics are lane-local plus two
+//                     cross-lane steps.
+//     online softmax  base-2, scale folded into one FMA before exp2.
+//     O^T += V^T P^T  v_mfma_f32_16x16x32_f16; P is packed to f16 straight
+//                     from the S^T accumulators (no shuffles); V^T comes from
+//                     LDS with ds_read_b64_tr_b16 (V stored as f16, converted
+//                     once per tile while staging).
+//   K/V tiles are double-buffered in LDS; the next tile's global loads are in
+//   flight while the current one is computed. One barrier per tile.
+//   Splits write (max, sum, unnormalised output) partials; a combine kernel
+//   merges them with the log-sum-exp rule. A single split normalises in place.
+#include "ts_internal.h"
+
+#include <cmath>
+
+namespace ts {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+template <int D, int RG, int PG, int TPW, int STAGES>
+struct Cfg {
+  static constexpr int NCH = D / 8;                       // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;                      // bytes per staged row
+  static constexpr int NW = RG * PG;                      // waves
+  static constexpr int NT = NW * 64;                      // threads
+  static constexpr int KSTEPS = D / 32;                   // MFMA k-steps over channels
+  static constexpr int TN = 32 * PG;                      // positions per KV tile (32 per wave)
+  static constexpr int CT = D / 16;                       // 16-channel output tiles
+  static constexpr int TILE_BYTES = TN * ROWB;            // per tensor
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // K then V
+  static constexpr int ROWS_PER_DMA = 1024 / ROWB;        // one wave-wide 16 B/lane DMA = 1 KB
+  static constexpr int LANES_PER_ROW = ROWB / 16;
+  static constexpr int DMA_PER_TENSOR = TN / ROWS_PER_DMA;
+  static constexpr int DMA_PER_STAGE = 2 * DMA_PER_TENSOR;
+  static constexpr int DMA_MIN_PER_WAVE = DMA_PER_STAGE / NW;  // every wave issues at least this many
+  static constexpr int ROWS_PER_BLOCK = RG * TPW * 16;
+  // keep Q in LDS when registers are short (two waves per SIMD above 4 waves)
+  static constexpr bool Q_LDS = TPW >= 4 || (NW > 4 && TPW >= 3);
+  static constexpr int KV_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int Q_BYTES = Q_LDS ? ROWS_PER_BLOCK * ROWB : 0;
+  static constexpr int MERGE_BYTES = (PG - 1) * RG * (64 * CT * 16 + 2 * 16 * 4);
+  static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES;
+  static_assert(MERGE_BYTES <= KV_BYTES, "split-local merge reuses the K/V ring");
+  static_assert(DMA_MIN_PER_WAVE >= 1, "every wave takes part in staging");
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+};
+
+// Reference-max slack of the online softmax, in log2 units.
+constexpr float LAZY_LOG2 = 8.0f;
+
+__device__ inline float lane_max4(float a, float b, float c, float d) {
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// bf16 pair (low, high halves of a 32-bit word) -> f16 pair. Exact for
+// |x| < 65504; larger magnitudes saturate to +-65504 (round toward zero).
+__device__ inline unsigned int bf16x2_to_f16x2(unsigned int w) {
+  float lo = __uint_as_float(w << 16);
+  float hi = __uint_as_float(w & 0xffff0000u);
+  auto h = __builtin_amdgcn_cvt_pkrtz(lo, hi);
+  return __builtin_bit_cast(unsigned int, h);
+}
+
+// One wave-wide asynchronous copy global -> LDS (16 B per lane): lane l's
+// 16 bytes land at LDS byte offset lds_off + 16 * l. The compiler does not
+// see the LDS write; callers order it with explicit vmcnt waits and barriers.
+// One wait state separates the M0 write from the DMA that reads it.
+__device__ inline void dma16(const void* g, unsigned int lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"((unsigned long long)g) : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
+}
+
+__device__ inline unsigned int lds_offset(const void* p) {
+  return (unsigned int)(uintptr_t)(const LDS_AS void*)p;
+}
+
+template <int D, int RG, int PG, int TPW, int STAGES>
+__global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnParams p) {
+  using C = Cfg<D, RG, PG, TPW, STAGES>;
+  constexpr int TN = C::TN;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int rg = wave / PG;   // row group: which row tiles
+  const int pg = wave % PG;   // position group: which 32 positions of each KV tile
+  const int l16 = lane & 15;
+  const int kg = lane >> 4;
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int M = p.M;
+  const int T = p.T;
+  const int n_ctx = p.n_ctx;
+  const int rows_total = n_ctx + T;
+  const int ntiles_total = (rows_total + TN - 1) / TN;
+  const int tiles_per_split = p.rows_per_split / TN;   // rows_per_split is a multiple of 64
+  const int t_begin = split * tiles_per_split;
+  const int t_end = min(t_begin + tiles_per_split, ntiles_total);
+  const float c = p.scale_log2e;
+
+  const uint16_t* __restrict__ kbase = p.k + (int64_t)g * p.s_head;
+  const uint16_t* __restrict__ vbase = p.v + (int64_t)g * p.s_head;
+  unsigned char* const qlds = lds + C::KV_BYTES;
+  const unsigned int ring_off = lds_offset(lds);
+
+  // ---- DMA staging of one KV tile into ring slot tile % STAGES ----
+  // Instruction j of a stage covers ROWS_PER_DMA rows of K (j < DMA_PER_TENSOR)
+  // or V. Lane l writes physical chunk l % LANES_PER_ROW of its row; it fetches
+  // the logical chunk that the swizzle maps there (K: chunk ^ row, V: chunk ^
+  // 2*row, both mod NCH), which keeps the later fragment reads conflict-free.
+  // Rows past the cache are clamped to the last row (their scores are masked).
+  const int dma_row = lane / C::LANES_PER_ROW;
+  const int dma_pc = lane % C::LANES_PER_ROW;
+  auto issue_tile = [&](int tile) {
+    const unsigned int slot = ring_off + (unsigned int)((tile % STAGES) * C::STAGE_BYTES);
+#pragma unroll
+    for (int jj = 0; jj < (C::DMA_PER_STAGE + C::NW - 1) / C::NW; ++jj) {
+      const int j = wave + jj * C::NW;
+      if (C::DMA_PER_STAGE % C::NW == 0 || j < C::DMA_PER_STAGE) {
+        const bool is_v = j >= C::DMA_PER_TENSOR;
+        const int r = (is_v ? j - C::DMA_PER_TENSOR : j) * C::ROWS_PER_DMA + dma_row;
+        const int ch = dma_pc ^ (is_v ? ((2 * r) & (C::NCH - 1)) : (r & (C::NCH - 1)));
+        const int pos = min(tile * TN + r, rows_total - 1);
+        dma16((is_v ? vbase : kbase) + (int64_t)pos * p.s_pos + ch * 8, slot + j * 1024);
+      }
+    }
+  };
+
+  // ---- queries: B operand of S^T = K Q^T (registers, or LDS for large TPW) ----
+  const int rt_blk = blockIdx.z * (RG * TPW);   // first row tile of this block
+  const int rt0 = rt_blk + rg * TPW;            // first row tile of this wave
+  bf16x8 qf[C::Q_LDS ? 1 : TPW][C::KSTEPS];
+  uint64_t anc_row[TPW];
+  bool tile_on[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int row = (rt0 + t) * 16 + l16;
+    tile_on[t] = (rt0 + t) * 16 < M;
+    const bool row_ok = row < M;
+    anc_row[t] = p.anc[row_ok ? row % T : 0];
+    if constexpr (!C::Q_LDS) {
+      const uint16_t* qrow = p.q + ((int64_t)g * M + (row_ok ? row : 0)) * D;
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(qrow + (4 * s + kg) * 8);
+        if (!row_ok) w = u32x4{0u, 0u, 0u, 0u};
+        qf[t][s] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
+  if constexpr (C::Q_LDS) {
+    // rows of this block, chunk-swizzled like K so B-fragment reads are conflict-free
+    for (int id = tid; id < C::ROWS_PER_BLOCK * C::NCH; id += C::NT) {
+      const int r = id / C::NCH, ch = id % C::NCH;
+      const int row = rt_blk * 16 + r;
+      u32x4 w = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)g * M + (row < M ? row : 0)) * D + ch * 8);
+      if (row >= M) w = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(qlds + r * C::ROWB + ((ch ^ (r & (C::NCH - 1))) << 4)) = w;
+    }
+  }
+
+  f32x4 o[TPW][C::CT];
+  float m_run[TPW], l_run[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) o[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // prologue: STAGES-1 tiles in flight
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (t_begin + st < t_end) issue_tile(t_begin + st);
+
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    // Wait for this wave's part of `tile`; the DMAs of later tiles may stay in
+    // flight (at least DMA_MIN_PER_WAVE per later tile were issued by this wave).
+    const int later = min(STAGES - 2, t_end - 1 - tile);
+    if constexpr (STAGES >= 4) {
+      if (later >= 2) wait_vm<2 * C::DMA_MIN_PER_WAVE>();
+      else if (later == 1) wait_vm<C::DMA_MIN_PER_WAVE>();
+      else wait_vm<0>();
+    } else if constexpr (STAGES == 3) {
+      if (later >= 1) wait_vm<C::DMA_MIN_PER_WAVE>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();  // every wave's part landed; slot (tile-1) % STAGES is free
+    if (tile + STAGES - 1 < t_end) issue_tile(tile + STAGES - 1);
+
+    const unsigned char* kl = lds + (tile % STAGES) * C::STAGE_BYTES;
+    const unsigned char* vl = kl + C::TILE_BYTES;
+
+    // ---- S^T = K Q^T over this wave's 32 positions ----
+    f32x4 s[TPW][2];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      bf16x8 kf[2];
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const int row = 32 * pg + 16 * pt + l16;
+        kf[pt] = *reinterpret_cast<const bf16x8*>(kl + row * C::ROWB + (((4 * ks + kg) ^ (row & (C::NCH - 1))) << 4));
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        if (!tile_on[t]) continue;
+        bf16x8 qv;
+        if constexpr (C::Q_LDS) {
+          const int r = (rg * TPW + t) * 16 + l16;
+          qv = *reinterpret_cast<const bf16x8*>(qlds + r * C::ROWB + (((4 * ks + kg) ^ (r & (C::NCH - 1))) << 4));
+        } else {
+          qv = qf[t][ks];
+        }
+        s[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qv, s[t][0], 0, 0, 0);
+        s[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qv, s[t][1], 0, 0, 0);
+      }
+    }
+
+    // ---- tree mask and tail (only tiles reaching past the context) ----
+    if ((tile + 1) * TN > n_ctx) {
+      // a = offset into the tree rows; visible iff a committed row (a < 0)
+      // or an ancestor-or-self tree node. Branch-free selects.
+      const int a0 = tile * TN + 32 * pg + 4 * kg - n_ctx;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const uint64_t m = anc_row[t];
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int a = a0 + 16 * pt + i;
+            const unsigned int bit = (unsigned int)(m >> ((unsigned int)a & 63u)) & 1u;
+            const unsigned int vis = (unsigned int)(a < 0) | ((unsigned int)(a < T) & bit);
+            s[t][pt][i] = vis ? s[t][pt][i] : -INFINITY;
+          }
+      }
+    }
+
+    // ---- online softmax, P -> f16 B fragments ----
+    f16x8 pfrag[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if (!tile_on[t]) continue;
+      float mx = fmaxf(lane_max4(s[t][0][0], s[t][0][1], s[t][0][2], s[t][0][3]),
+                       lane_max4(s[t][1][0], s[t][1][1], s[t][1][2], s[t][1][3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Lazy rescale: the reference max only moves when the tile max exceeds
+      // it by more than 2^8 in probability (or on the first visible score),
+      // so p = exp2(s*c - m*c) stays <= 256 and the O rescale is rare.
+      const bool bump = (mx - m_run[t]) * c > LAZY_LOG2 || (m_run[t] == -INFINITY && mx != -INFINITY);
+      if (__ballot(bump)) {
+        const float m_new = bump ? mx : m_run[t];
+        const float alpha = (m_run[t] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
+        m_run[t] = m_new;
+        l_run[t] *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) o[t][ct] *= alpha;
+      }
+      const float m_use = (m_run[t] == -INFINITY) ? 0.f : m_run[t];
+      const float nmc = -m_use * c;
+      float psum = 0.f;
+      f16x8 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][0][i], c, nmc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][1][i], c, nmc));
+        psum += p0 + p1;
+        f[i] = (_Float16)p0;
+        f[4 + i] = (_Float16)p1;
+      }
+      pfrag[t] = f;
+      l_run[t] += psum;
+    }
+
+    // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads, bf16 -> f16) ----
+    {
+      const int r_lo = 32 * pg + 4 * kg + (l16 >> 2);
+      const int swz = (2 * r_lo) & (C::NCH - 1);  // same for r_lo + 16
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) {
+        const int chunk = 2 * ct + ((l16 & 3) >> 1);
+        const int off = ((chunk ^ swz) << 4) + ((l16 & 1) << 3);
+        const LDS_AS s16x4* a_lo = (const LDS_AS s16x4*)(const LDS_AS unsigned char*)(vl + r_lo * C::ROWB + off);
+        const LDS_AS s16x4* a_hi = (const LDS_AS s16x4*)(const LDS_AS unsigned char*)(vl + (r_lo + 16) * C::ROWB + off);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)a_lo);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)a_hi);
+        const u32x4 wb = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const u32x4 wh = {bf16x2_to_f16x2(wb.x), bf16x2_to_f16x2(wb.y), bf16x2_to_f16x2(wb.z), bf16x2_to_f16x2(wb.w)};
+        const f16x8 vf = __builtin_bit_cast(f16x8, wh);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          if (tile_on[t]) o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfrag[t], o[t][ct], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- per-row sums across the 4 lane groups ----
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    l_run[t] += __shfl_xor(l_run[t], 16);
+    l_run[t] += __shfl_xor(l_run[t], 32);
+  }
+
+  // ---- merge the PG position groups of each row group through LDS ----
+  if constexpr (PG > 1) {
+    constexpr int OSLOT = 64 * C::CT * 16;            // one wave's O^T fragments of one row tile
+    constexpr int SLOT = OSLOT + 2 * 16 * 4;          // + m and l of its 16 rows
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      __syncthreads();  // the ring (or the previous round) is free
+      if (pg > 0 && tile_on[t]) {
+        unsigned char* slot = lds + ((pg - 1) * RG + rg) * SLOT;
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(slot + (ct * 64 + lane) * 16) = o[t][ct];
+        if (kg == 0) {
+          reinterpret_cast<float*>(slot + OSLOT)[l16] = m_run[t];
+          reinterpret_cast<float*>(slot + OSLOT)[16 + l16] = l_run[t];
+        }
+      }
+      __syncthreads();
+      if (pg == 0 && tile_on[t]) {
+        float mm = m_run[t];
+#pragma unroll
+        for (int q = 1; q < PG; ++q)
+          mm = fmaxf(mm, reinterpret_cast<const float*>(lds + ((q - 1) * RG + rg) * SLOT + OSLOT)[l16]);
+        const float mu = (mm == -INFINITY) ? 0.f : mm;
+        const float w0 = __builtin_amdgcn_exp2f((m_run[t] - mu) * c);
+        float ll = l_run[t] * w0;
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) o[t][ct] *= w0;
+#pragma unroll
+        for (int q = 1; q < PG; ++q) {
+          const unsigned char* slot = lds + ((q - 1) * RG + rg) * SLOT;
+          const float mq = reinterpret_cast<const float*>(slot + OSLOT)[l16];
+          const float wq = __builtin_amdgcn_exp2f((mq - mu) * c);
+          ll += wq * reinterpret_cast<const float*>(slot + OSLOT)[16 + l16];
+#pragma unroll
+          for (int ct = 0; ct < C::CT; ++ct) o[t][ct] += wq * *reinterpret_cast<const f32x4*>(slot + (ct * 64 + lane) * 16);
+        }
+        m_run[t] = mm;
+        l_run[t] = ll;
+      }
+    }
+  }
+
+  // ---- epilogue: normalise (single split) or write partials ----
+  if (pg != 0) return;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (!tile_on[t]) continue;
+    const int row = (rt0 + t) * 16 + l16;
+    if (row >= M) continue;
+    if (p.n_split == 1) {
+      const float inv = 1.0f / l_run[t];
+      float* dst = p.out + ((int64_t)g * M + row) * D + 4 * kg;
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(dst + ct * 16) = o[t][ct] * inv;
+    } else {
+      const int64_t prow = ((int64_t)split * p.Hkv + g) * M + row;
+      float* dst = p.part_acc + prow * D + 4 * kg;
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(dst + ct * 16) = o[t][ct];
+      if (kg == 0) {
+        p.part_ml[prow * 2 + 0] = m_run[t];
+        p.part_ml[prow * 2 + 1] = l_run[t];
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of the split partials: one row per D/4 threads.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int tid = threadIdx.x;
+  const int row_lin = blockIdx.x * RPB + tid / TPR;  // g * M + r
+  const int c4 = tid % TPR;
+  const int nrows = p.Hkv * p.M;
+  if (row_lin >= nrows) return;
+  const float c = p.scale_log2e;
+  const int64_t sstride = (int64_t)nrows;
+  float mmax = -INFINITY;
+  for (int s = 0; s < p.n_split; ++s) mmax = fmaxf(mmax, p.part_ml[(s * sstride + row_lin) * 2]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.n_split; ++s) {
+    const int64_t pr = s * sstride + row_lin;
+    const float ms = p.part_ml[pr * 2];
+    const float w = __builtin_amdgcn_exp2f((ms - mmax) * c);
+    L += w * p.part_ml[pr * 2 + 1];
+    acc += w * *reinterpret_cast<const f32x4*>(p.part_acc + pr * D + 4 * c4);
+  }
+  *reinterpret_cast<f32x4*>(p.out + (int64_t)row_lin * D + 4 * c4) = acc * (1.0f / L);
+}
+
+struct KernelChoice {
+  int rg, pg, tpw;
+};
+
+constexpr int KV_TILE = 64;  // split granularity in positions (a multiple of every kernel's tile)
+
+// Row tiles per KV head -> (row groups, position groups, row tiles per wave).
+// Every choice keeps the wave's accumulators in registers without spilling:
+// up to 4 waves a workgroup may use the whole register file, above that two
+// waves share a SIMD.
+KernelChoice choose(int nrt) {
+  if (nrt <= 1) return {1, 2, 1};
+  if (nrt == 2) return {1, 2, 2};
+  if (nrt == 3) return {1, 2, 3};
+  if (nrt == 4) return {2, 2, 2};
+  if (nrt <= 6) return {2, 2, 3};
+  if (nrt <= 8) return {2, 2, 4};
+  if (nrt == 9) return {3, 2, 3};
+  if (nrt <= 12) return {4, 1, 3};
+  if (nrt <= 16) return {4, 1, 4};
+  return {4, 1, 5};
+}
+
+// K/V ring depth: three tiles (two in flight while one is computed), or two
+// when three would not fit in the 160 KB of LDS next to the queries.
+template <int D, int RG, int PG, int TPW>
+hipError_t launch_split(const AttnParams& p, int nz, hipStream_t stream) {
+  constexpr int STAGES = Cfg<D, RG, PG, TPW, 3>::LDS_BYTES <= 160 * 1024 ? 3 : 2;
+  static_assert(Cfg<D, RG, PG, TPW, STAGES>::LDS_BYTES <= 160 * 1024, "LDS budget");
+  dim3 grid(p.n_split, p.Hkv, nz);
+  hipLaunchKernelGGL((attn_split_kernel<D, RG, PG, TPW, STAGES>), grid, dim3(RG * PG * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split_d(const AttnParams& p, const KernelChoice& kc, int nz, hipStream_t stream) {
+#define TS_CASE(RG_, PG_, TPW_) \
+  if (kc.rg == RG_ && kc.pg == PG_ && kc.tpw == TPW_) return launch_split<D, RG_, PG_, TPW_>(p, nz, stream);
+  TS_CASE(1, 2, 1)
+  TS_CASE(1, 2, 2)
+  TS_CASE(1, 2, 3)
+  TS_CASE(2, 2, 2)
+  TS_CASE(2, 2, 3)
+  TS_CASE(2, 2, 4)
+  TS_CASE(3, 2, 3)
+  TS_CASE(4, 1, 3)
+  TS_CASE(4, 1, 4)
+  TS_CASE(4, 1, 5)
+#undef TS_CASE
+  return hipErrorInvalidValue;
+}
+
+int row_blocks_for(int M) {
+  const int nrt = (M + 15) / 16;
+  const KernelChoice kc = choose(nrt);
+  const int per = kc.rg * kc.tpw;
+  return (nrt + per - 1) / per;
+}
+
+}  // namespace
+
+int attn_auto_split(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d) {
+  (void)d;
+  const int M = (Hq / Hkv) * T;
+  const int ntiles = (rows_total + KV_TILE - 1) / KV_TILE;
+  const int nz = row_blocks_for(M);
+  const int target_wg = 512;  // ~2 resident workgroups on each of 256 compute units
+  int s = (target_wg + Hkv * nz - 1) / (Hkv * nz);
+  if (s > ntiles) s = ntiles;
+  if (s < 1) s = 1;
+  return s;
+}
+
+void attn_split_plan(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                     int32_t n_split_req, int32_t* n_split_eff, int32_t* rows_per_split) {
+  (void)T;
+  (void)Hq;
+  (void)Hkv;
+  const int ntiles = (rows_total + KV_TILE - 1) / KV_TILE;
+  int s = n_split_req > 0 ? n_split_req : attn_auto_split(rows_total, T, Hq, Hkv, d);
+  if (s > ntiles) s = ntiles;
+  if (s < 1) s = 1;
+  const int tps = (ntiles + s - 1) / s;
+  *rows_per_split = tps * KV_TILE;
+  *n_split_eff = (ntiles + tps - 1) / tps;
+}
+
+size_t attn_workspace_bytes(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                            int32_t n_split_req) {
+  int32_t s, tps;
+  attn_split_plan(rows_total, T, Hq, Hkv, d, n_split_req, &s, &tps);
+  if (s <= 1) return 0;
+  const size_t M = (size_t)(Hq / Hkv) * T;
+  return (size_t)s * Hkv * M * ((size_t)d + 2) * sizeof(float);
+}
+
+hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {
+  const int nrt = (p.M + 15) / 16;
+  const KernelChoice kc = choose(nrt);
+  const int nz = row_blocks_for(p.M);
+  hipError_t e = p.d == 128 ? launch_split_d<128>(p, kc, nz, stream) : launch_split_d<64>(p, kc, nz, stream);
+  if (e != hipSuccess || p.n_split == 1) return e;
+  if (p.d == 128) {
+    const int rpb = 256 / 32;
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((p.Hkv * p.M + rpb - 1) / rpb), dim3(256), 0, stream, p);
+  } else {
+    const int rpb = 256 / 16;
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((p.Hkv * p.M + rpb - 1) / rpb), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ts

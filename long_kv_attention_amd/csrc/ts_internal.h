@@ -1,0 +1,78 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the kernel
+// launchers (*.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace ts {
+
+// Launch parameters of the split-KV attention kernels (verification and draft).
+struct AttnParams {
+  const uint16_t* q;     // [Hq][T][d] bf16
+  const uint16_t* k;     // cache, element (g, j, c) at g*s_head + j*s_pos + c
+  const uint16_t* v;
+  float* out;            // [Hq][T][d] fp32
+  float* part_acc;       // [n_split][Hkv][M][d] unnormalised partial outputs
+  float* part_ml;        // [n_split][Hkv][M][2] running max (raw score units) and sum
+  int64_t s_head, s_pos;
+  int32_t n_ctx, T, Hq, Hkv, d;
+  int32_t M;             // rows per KV head = (Hq/Hkv) * T
+  int32_t n_split;       // effective number of chunks per KV head
+  int32_t rows_per_split;  // cache rows per split (a multiple of 64)
+  float scale_log2e;     // softmax scale * log2(e)
+  uint64_t anc[64];      // anc[i] bit a set <=> tree node a is i or an ancestor of i
+};
+
+// Automatic split count: a pure function of the shapes (so the workspace
+// query needs no device), aimed at ~2 resident workgroups per compute unit.
+int attn_auto_split(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d);
+// Effective split count and cache rows per split for a requested count.
+void attn_split_plan(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                     int32_t n_split_req, int32_t* n_split_eff, int32_t* rows_per_split);
+size_t attn_workspace_bytes(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                            int32_t n_split_req);
+hipError_t launch_attention(const AttnParams& p, hipStream_t stream);
+
+// Partial-KV selection.
+struct SelectParams {
+  const uint16_t* q;     // [Hq][T][d]
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t s_head, s_pos;
+  int32_t n_ctx, T, Hq, Hkv, d;
+  int32_t n_sink, budget, n_recent;
+  int32_t cand_lo, cand_hi;   // candidate rows [cand_lo, cand_hi)
+  int32_t b_eff;              // min(budget, |C|)
+  int32_t n_part;
+  int32_t* sel_idx;           // [Hkv][budget]
+  uint16_t* k_part;
+  uint16_t* v_part;
+  int64_t sp_head, sp_pos;
+  float* scores;              // [Hkv][n_ctx] (user buffer or workspace)
+  float* qbar;                // [Hkv][d] workspace
+  int32_t* sel_ws;            // workspace: per-head key histogram of the scoring pass
+};
+size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
+                              int32_t budget);
+hipError_t launch_select(const SelectParams& p, hipStream_t stream);
+
+// Penalty / sampling pass.
+struct PenaltyParams {
+  const float* logits;
+  float* logits_out;
+  const int32_t* window;
+  int64_t window_stride;
+  int32_t rows, V, W;
+  float penalty, inv_temperature, temperature, top_p, min_p;
+  uint8_t* keep;
+  float* probs;
+  const float* u;
+  int32_t* token;
+  void* ws;
+};
+size_t penalty_workspace_bytes(int32_t rows, int32_t V);
+hipError_t launch_penalty(const PenaltyParams& p, hipStream_t stream);
+
+}  // namespace ts

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: exports, workspace queries, host validation.
+
+Every call here is rejected by host-side validation, which runs before any
+HIP call, so fake (aligned, non-null) device pointers are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_kv_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokenswift.h")
+EINVAL, ENOTSUP, EWORKSPACE = -1, -2, -3
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10002)    # misaligned (2-byte)
+
+
+def _lib():
+    if not os.path.exists(binding.lib_path()):
+        pytest.skip("libtokenswift.so not built")
+    return binding.lib()
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ts_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    syms = header_symbols()
+    for name in ("ts_verify_attn", "ts_draft_attn", "ts_partial_kv_select", "ts_penalty_sample"):
+        assert name in syms and name + "_workspace_size" in syms
+
+
+def test_library_exports_every_header_symbol():
+    L = _lib()
+    missing = [s for s in header_symbols() if not hasattr(L, s)]
+    assert not missing, missing
+    assert L.ts_abi_version() == 100
+
+
+def test_workspace_queries_depend_on_shapes_only():
+    L = _lib()
+    a = L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 0)
+    assert a > 0 and a == L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 0)
+    assert L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 1) == 0   # one split: no partials
+    forced = L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 7)
+    assert forced == 7 * 8 * 96 * 130 * 4
+    assert L.ts_verify_attn_workspace_size(100_000, 65, 32, 8, 128, 0) == 0   # unsupported -> 0
+    assert L.ts_draft_attn_workspace_size(4164, 4, 32, 8, 128, 0) == L.ts_verify_attn_workspace_size(4164, 4, 32, 8, 128, 0)
+    assert L.ts_partial_kv_select_workspace_size(100_000, 24, 32, 8, 128, 4096) >= 8 * 100_000 * 4
+    assert L.ts_penalty_sample_workspace_size(1, 128256) == 0
+
+
+def _verify(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, s_head=128 * 200, s_pos=128, n_ctx=100, T=3, parent=[-1, 0, 1], Hq=8, Hkv=2,
+             d=128, scale=0.0, out=FAKE, n_split=0, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    par = (ctypes.c_int32 * max(1, len(a["parent"])))(*a["parent"]) if a["parent"] is not None else None
+    return L.ts_verify_attn(a["q"], a["k"], a["v"], a["s_head"], a["s_pos"], a["n_ctx"], a["T"], par, a["Hq"],
+                            a["Hkv"], a["d"], a["scale"], a["out"], a["n_split"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(q=None), EINVAL, "null"),
+    (dict(d=96), ENOTSUP, "head dim"),
+    (dict(T=65, parent=[-1] + list(range(64))), ENOTSUP, "65"),
+    (dict(T=0, parent=[]), EINVAL, "at least one"),
+    (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
+    (dict(parent=[0, 0, 1]), EINVAL, "parent[0]"),
+    (dict(parent=[-1, 0, 2]), EINVAL, "parent[2]"),
+    (dict(parent=[-1, 1, 0]), EINVAL, "parent[1]"),
+    (dict(parent=None), EINVAL, "parent"),
+    (dict(s_pos=64), EINVAL, "s_pos"),
+    (dict(s_pos=130), EINVAL, "s_pos"),
+    (dict(s_head=0), EINVAL, "s_head"),
+    (dict(k=FAKE_ODD), EINVAL, "aligned"),
+    (dict(n_ctx=-1), EINVAL, "negative"),
+    (dict(scale=float("nan")), EINVAL, "scale"),
+    (dict(n_split=-2), EINVAL, "n_split"),
+    (dict(n_ctx=100_000, n_split=0), EWORKSPACE, "workspace"),
+])
+def test_verify_attn_rejects(kw, code, text):
+    L = _lib()
+    assert _verify(L, **kw) == code
+    assert text in L.ts_last_error().decode()
+
+
+def test_draft_attn_rejects():
+    L = _lib()
+    assert L.ts_draft_attn(FAKE, FAKE, FAKE, 128 * 100, 128, 50, 65, 8, 2, 128, 0.0, FAKE, 0, None, 0, None) == ENOTSUP
+    assert L.ts_draft_attn(FAKE, FAKE, None, 128 * 100, 128, 50, 4, 8, 2, 128, 0.0, FAKE, 0, None, 0, None) == EINVAL
+    assert L.ts_draft_attn(FAKE, FAKE, FAKE, 128 * 100, 128, 50_000, 4, 8, 2, 128, 0.0, FAKE, 0, None, 0, None) == EWORKSPACE
+
+
+def _select(L, **kw):
+    a = dict(q=FAKE, T=4, k=FAKE, v=FAKE, s_head=128 * 1000, s_pos=128, n_ctx=1000, Hq=8, Hkv=2, d=128, n_sink=4,
+             budget=100, n_recent=8, sel=FAKE, kp=FAKE, vp=FAKE, sp_head=128 * 112, sp_pos=128, ws=None, ws_bytes=0)
+    a.update(kw)
+    n_part = ctypes.c_int32(-7)
+    rc = L.ts_partial_kv_select(a["q"], a["T"], a["k"], a["v"], a["s_head"], a["s_pos"], a["n_ctx"], a["Hq"], a["Hkv"],
+                                a["d"], a["n_sink"], a["budget"], a["n_recent"], a["sel"], a["kp"], a["vp"],
+                                a["sp_head"], a["sp_pos"], ctypes.byref(n_part), None, a["ws"], a["ws_bytes"], None)
+    return rc, n_part.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sel=None), EINVAL), (dict(budget=-1), EINVAL), (dict(n_sink=-1), EINVAL), (dict(d=80), ENOTSUP),
+    (dict(T=70), ENOTSUP), (dict(Hq=7), EINVAL), (dict(sp_head=128 * 50), EINVAL), (dict(kp=FAKE_ODD), EINVAL),
+    (dict(), EWORKSPACE),
+])
+def test_partial_kv_select_rejects(kw, code):
+    L = _lib()
+    rc, n_part = _select(L, **kw)
+    assert rc == code
+    assert n_part == -7  # nothing written on error
+
+
+def _penalty(L, **kw):
+    a = dict(logits=FAKE, rows=2, V=1000, window=FAKE, W=16, wstride=16, penalty=1.2, temp=1.0, top_p=0.9,
+             min_p=0.05, out=FAKE, keep=FAKE, probs=FAKE, u=FAKE, token=FAKE, ws=None, ws_bytes=0)
+    a.update(kw)
+    return L.ts_penalty_sample(a["logits"], a["rows"], a["V"], a["window"], a["W"], a["wstride"], a["penalty"],
+                               a["temp"], a["top_p"], a["min_p"], a["out"], a["keep"], a["probs"], a["u"], a["token"],
+                               a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), EINVAL), (dict(rows=0), EINVAL), (dict(V=0), EINVAL), (dict(V=300_000), ENOTSUP),
+    (dict(W=-1), EINVAL), (dict(window=None), EINVAL), (dict(wstride=8), EINVAL), (dict(penalty=0.0), EINVAL),
+    (dict(penalty=-1.2), EINVAL), (dict(temp=0.0), EINVAL), (dict(top_p=1.5), EINVAL), (dict(top_p=-0.1), EINVAL),
+    (dict(min_p=float("nan")), EINVAL), (dict(u=None), EINVAL), (dict(out=FAKE_ODD), EINVAL),
+])
+def test_penalty_sample_rejects(kw, code):
+    L = _lib()
+    assert _penalty(L, **kw) == code
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "HERE", str(tmp_path))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()

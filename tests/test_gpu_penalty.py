@@ -1,0 +1,100 @@
+"""GPU parity of ts_penalty_sample against the float64 oracle.
+
+z (penalised, tempered logits): |z_gpu - z_ref| <= 1e-5 |z_ref|.
+keep: bit-exact outside the bands |E(i) - top_p| <= 1e-4 and
+|p_i / p_max - min_p| <= 1e-4 (E(i) = mass before i in (p desc, id asc)).
+probs: |q_gpu - q_ref| <= 1e-5 max(q_ref) (not in the stated bar; derived
+from fp32 softmax error). token: a kept id whose oracle CDF interval
+contains u up to 1e-5.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import long_kv_attention_amd as ts
+from oracle import penalty_sample
+from synth import CONFIGS, penalty_inputs
+from tests.gpu_util import banner
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def _run(x, penalty, temp, top_p, min_p, shared=False):
+    logits = torch.from_numpy(x["logits"]).cuda()
+    window = torch.from_numpy(np.ascontiguousarray(x["window"])).cuda()
+    u = torch.from_numpy(x["u"]).cuda()
+    z, keep, probs, tok = ts.penalty_sample(logits, window, penalty, temp, top_p, min_p, u=u)
+    torch.cuda.synchronize()
+    return z.cpu().numpy(), keep.cpu().numpy().astype(bool), probs.cpu().numpy(), tok.cpu().numpy()
+
+
+def _compare(x, penalty, temp, top_p, min_p):
+    z, keep, probs, tok = _run(x, penalty, temp, top_p, min_p)
+    r = penalty_sample(x["logits"], x["window"], float(F32(penalty)), float(F32(temp)), float(F32(top_p)),
+                       float(F32(min_p)), x["u"])
+    assert np.all(np.abs(z - r.z) <= 1e-5 * np.abs(r.z))
+    band = (np.abs(r.excl_mass - float(F32(top_p))) <= 1e-4) | (np.abs(r.ratio - float(F32(min_p))) <= 1e-4)
+    mism = (keep != r.keep) & ~band
+    assert not mism.any(), np.argwhere(mism)[:10]
+    rows = r.z.shape[0]
+    for i in range(rows):
+        if ((keep[i] != r.keep[i]) & band[i]).any():
+            continue  # a band token changed the kept set: normalisation differs
+        assert np.max(np.abs(probs[i] - r.probs[i])) <= 1e-5 * r.probs[i].max()
+        t = int(tok[i])
+        assert keep[i, t]
+        cdf = np.cumsum(r.probs[i])
+        lo = cdf[t - 1] if t > 0 else 0.0
+        assert lo - 1e-5 <= float(x["u"][i]) < cdf[t] + 1e-5
+    return keep
+
+
+def test_tiny_workload():
+    c = CONFIGS["tiny"]
+    banner("penalty tiny")
+    x = penalty_inputs(c["seed"], 1, c["V"], c["W"], sigma=c["sigma"])
+    _compare(x, 1.2, 1.0, 0.9, 0.05)
+
+
+@pytest.mark.parametrize("name", ["1.5b", "7b", "8b", "14b"])
+def test_vocab_sizes_table11(name):
+    c = CONFIGS[name]
+    banner(f"penalty {name} V={c['V']}")
+    x = penalty_inputs(c["seed"], 2, c["V"], c["W"], sigma=c["sigma"])
+    _compare(x, 1.2, 1.0, 0.9, 0.05)
+
+
+@pytest.mark.parametrize("top_p,min_p,sigma", [(0.5, 0.0, 2.0), (0.9, 0.0, 2.0), (0.99, 0.0, 2.0), (1.0, 0.05, 2.0),
+                                               (1.0, 0.5, 2.0), (0.9, 0.05, 1.4142), (0.0, 0.0, 2.0), (1.0, 1.0, 2.0),
+                                               (1.0, 0.0, 2.0)])
+def test_filter_regimes(top_p, min_p, sigma):
+    banner(f"penalty regimes top_p={top_p} min_p={min_p}")
+    x = penalty_inputs(21, 24, 128256, 1024, sigma=sigma)
+    _compare(x, 1.2, 1.0, top_p, min_p)
+
+
+@pytest.mark.parametrize("temp,penalty", [(0.4, 1.2), (1.2, 1.5), (0.7, 1.0)])
+def test_temperature_and_penalty(temp, penalty):
+    x = penalty_inputs(22, 3, 32000, 1024)
+    _compare(x, penalty, temp, 0.9, 0.05)
+
+
+def test_shared_window_duplicates_and_ragged_vocab():
+    x = penalty_inputs(23, 3, 1001, 300, shared_window=True, dup_window=True)
+    x["window"][:5] = [-1, 1001, 5000, -7, 3]
+    _compare(x, 1.2, 1.0, 0.9, 0.05)
+
+
+def test_exact_logit_ties():
+    x = penalty_inputs(24, 2, 4096, 64, sigma=0.5)
+    x["logits"][:, 100:140] = x["logits"][:, 7:8]    # 41 equal logits per row
+    x["window"][:] = -1
+    _compare(x, 1.2, 1.0, 0.3, 0.0)
+
+
+def test_single_token_vocab_and_empty_window():
+    x = penalty_inputs(25, 1, 1, 0)
+    z, keep, probs, tok = _run(x, 1.2, 1.0, 0.9, 0.05)
+    assert keep.tolist() == [[True]] and probs[0, 0] == 1.0 and tok[0] == 0

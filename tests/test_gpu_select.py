@@ -1,0 +1,102 @@
+"""GPU parity of ts_partial_kv_select against the float64 oracle.
+
+Scores: |s_gpu - s_ref| <= 1e-5 * max|s_ref| (fp32 accumulation of bf16
+products). Selected index set: bit-exact outside the cut band
+|sigma_j - sigma_cut| <= 1e-4 * max(|sigma_cut|, 1); same size, ascending,
+-1 padded. Partial cache: sink U selected U recent rows copied bit-exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import long_kv_attention_amd as ts
+from oracle import bf16_to_f64, draft_attention, partial_kv_select, verify_attention
+from synth import CONFIGS, attention_inputs, tree_parent
+from tests.gpu_util import banner, dev_bf16, rel_max_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x, n_ctx, Hq, Hkv, n_sink, budget, n_recent, heads=None):
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    sel, kp, vp, n_part, sc = ts.partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, want_scores=True)
+    torch.cuda.synchronize()
+    sel, sc = sel.cpu().numpy(), sc.cpu().numpy()[:, :n_ctx]
+    kp = kp.view(torch.int16).cpu().numpy().view(np.uint16)
+    vp = vp.view(torch.int16).cpu().numpy().view(np.uint16)
+    G = Hq // Hkv
+    heads = range(Hkv) if heads is None else heads
+    for g in heads:
+        ref = partial_kv_select(bf16_to_f64(x["q"][g * G:(g + 1) * G]), bf16_to_f64(x["k"][g:g + 1, :n_ctx]),
+                                n_ctx, 1, n_sink, budget, n_recent)
+        assert n_part == ref.n_part
+        s_ref = ref.scores[0]
+        if n_ctx:
+            assert np.max(np.abs(sc[g] - s_ref)) <= 1e-5 * max(np.max(np.abs(s_ref)), 1e-30)
+        got = sel[g]
+        b_eff = int((ref.sel_idx[0] >= 0).sum())
+        assert np.all(got[b_eff:] == -1)
+        gs = got[:b_eff]
+        assert np.all(np.diff(gs) > 0)
+        rs = ref.sel_idx[0][:b_eff]
+        diff = np.setxor1d(gs, rs)
+        if len(diff):
+            cut = ref.cutoff[0]
+            band = 1e-4 * max(abs(cut), 1.0)
+            assert np.all(np.abs(s_ref[diff] - cut) <= band), (g, diff, s_ref[diff], cut)
+        # partial cache rows: sink, the GPU's own selection, recent
+        rows = np.concatenate([np.arange(min(n_sink, n_ctx)), gs, np.arange(max(n_sink, n_ctx - n_recent), n_ctx)])
+        assert len(rows) == n_part
+        np.testing.assert_array_equal(kp[g, :n_part], x["k"][g, rows])
+        np.testing.assert_array_equal(vp[g, :n_part], x["v"][g, rows])
+    return sel, n_part
+
+
+def test_tiny_workload():
+    c = CONFIGS["tiny"]
+    banner("select tiny")
+    x = attention_inputs(c["seed"], c["Hq"], c["Hkv"], c["d"], c["n_ctx"], c["T"])
+    _check(x, c["n_ctx"], c["Hq"], c["Hkv"], c["n_sink"], c["budget"], c["n_recent"])
+    _check(x, c["n_ctx"], c["Hq"], c["Hkv"], 0, c["budget"], 0)
+
+
+@pytest.mark.parametrize("n_ctx,n_sink,budget,n_recent", [
+    (1000, 4, 100, 8), (1000, 0, 1000, 0), (1000, 4, 988, 8), (1000, 4, 5000, 8), (1000, 4, 0, 8), (70, 4, 16, 64),
+    (68, 4, 16, 64), (3, 4, 16, 8), (0, 4, 16, 8), (5000, 4, 1, 64), (33_333, 4, 4096, 64),
+])
+def test_edge_cases(n_ctx, n_sink, budget, n_recent):
+    banner(f"select n_ctx={n_ctx} sink={n_sink} B={budget} recent={n_recent}")
+    x = attention_inputs(n_ctx + 3, 8, 2, 128, max(n_ctx, 1), 4)
+    _check(x, n_ctx, 8, 2, n_sink, budget, n_recent)
+
+
+def test_exact_ties_go_to_earlier_rows():
+    n_ctx = 3000
+    x = attention_inputs(12, 8, 2, 128, n_ctx, 4)
+    x["k"][:, 1500:1600] = x["k"][:, 100:200]    # 100 exact score ties per head
+    _check(x, n_ctx, 8, 2, 4, 150, 64)
+
+
+def test_full_budget_draft_equals_verification():
+    Hq, Hkv, d, n_ctx, Tq = 8, 2, 128, 1234, 4
+    x = attention_inputs(13, Hq, Hkv, d, n_ctx, Tq)
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    sel, kp, vp, n_part, _ = ts.partial_kv_select(q, k, v, n_ctx, 4, 100_000, 64, extra_rows=Tq)
+    assert n_part == n_ctx
+    kp[:, n_part:n_part + Tq] = k[:, n_ctx:n_ctx + Tq]
+    vp[:, n_part:n_part + Tq] = v[:, n_ctx:n_ctx + Tq]
+    draft = ts.draft_attn(q, kp, vp, n_part)
+    full = ts.verify_attn(q, k, v, n_ctx, tree_parent("chain", Tq))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(draft.cpu().numpy(), full.cpu().numpy())
+    ref = verify_attention(bf16_to_f64(x["q"]), bf16_to_f64(x["k"]), bf16_to_f64(x["v"]), n_ctx, tree_parent("chain", Tq))
+    assert rel_max_err(draft.cpu().numpy(), ref) <= 2e-3
+
+
+@pytest.mark.parametrize("name,heads", [("8b", [0, 6]), ("14b", [4]), ("1.5b", [1])])
+def test_full_size_sampled_heads(name, heads):
+    c = CONFIGS[name]
+    banner(f"select full {name}")
+    x = attention_inputs(c["seed"], c["Hq"], c["Hkv"], c["d"], c["n_ctx"], c["T"], k_scale=c.get("k_scale"))
+    _check(x, c["n_ctx"], c["Hq"], c["Hkv"], c["n_sink"], c["budget"], c["n_recent"], heads=heads)
