@@ -79,6 +79,17 @@ __device__ inline float lane_max4(float a, float b, float c, float d) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
+// Max over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
+// gfx950 row-swap permutes: VALU only, no LDS round trip. With both operands
+// holding x, permlane16_swap leaves rows (0,0,2,2) in one result and (1,1,3,3)
+// in the other; permlane32_swap does the same for the two halves.
+__device__ inline float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // bf16 pair (low, high halves of a 32-bit word) -> f16 pair. Exact for
 // |x| < 65504; larger magnitudes saturate to +-65504 (round toward zero).
 __device__ inline unsigned int bf16x2_to_f16x2(unsigned int w) {
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   const int n_ctx = p.n_ctx;
   const int rows_total = n_ctx + T;
   const int ntiles_total = (rows_total + TN - 1) / TN;
-  const int tiles_per_split = p.rows_per_split / TN;   // rows_per_split is a multiple of 64
+  const int tiles_per_split = p.rows_per_split / TN;   // rows_per_split is a multiple of 128
   const int t_begin = split * tiles_per_split;
   const int t_end = min(t_begin + tiles_per_split, ntiles_total);
   const float c = p.scale_log2e;
@@ -282,8 +293,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       if (!tile_on[t]) continue;
       float mx = fmaxf(lane_max4(s[t][0][0], s[t][0][1], s[t][0][2], s[t][0][3]),
                        lane_max4(s[t][1][0], s[t][1][1], s[t][1][2], s[t][1][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = group4_max(mx);
       // Lazy rescale: the reference max only moves when the tile max exceeds
       // it by more than 2^8 in probability (or on the first visible score),
       // so p = exp2(s*c - m*c) stays <= 256 and the O rescale is rare.
@@ -408,49 +418,77 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   }
 }
 
-// Log-sum-exp merge of the split partials: one row per D/4 threads.
+// Log-sum-exp merge of the split partials. One row per block for d=128 (two
+// for d=64): 8 split groups x D/4 float4 lanes, so the per-split loads of a
+// row are issued in parallel; two LDS reductions finish the merge.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
-  constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
+  constexpr int CG = D / 4;                 // float4 channel groups per row
+  constexpr int RPB = 256 / (CG * 8);       // rows per block
+  constexpr int SG = 8;                     // split groups
+  __shared__ float red_m[RPB][SG];
+  __shared__ float red_l[RPB][SG];
+  __shared__ f32x4 red_acc[RPB][SG][CG];
   const int tid = threadIdx.x;
-  const int row_lin = blockIdx.x * RPB + tid / TPR;  // g * M + r
-  const int c4 = tid % TPR;
+  const int r_in = tid / (CG * SG);
+  const int sg = (tid / CG) % SG;
+  const int c4 = tid % CG;
   const int nrows = p.Hkv * p.M;
-  if (row_lin >= nrows) return;
+  const int row = blockIdx.x * RPB + r_in;   // g * M + r
+  const bool ok = row < nrows;
   const float c = p.scale_log2e;
-  const int64_t sstride = (int64_t)nrows;
-  float mmax = -INFINITY;
-  for (int s = 0; s < p.n_split; ++s) mmax = fmaxf(mmax, p.part_ml[(s * sstride + row_lin) * 2]);
+  const int64_t sstride = nrows;
+
+  float mm = -INFINITY;
+  if (ok)
+    for (int s = sg; s < p.n_split; s += SG) mm = fmaxf(mm, p.part_ml[(s * sstride + row) * 2]);
+  if (c4 == 0) red_m[r_in][sg] = mm;
+  __syncthreads();
+  float M = red_m[r_in][0];
+#pragma unroll
+  for (int q = 1; q < SG; ++q) M = fmaxf(M, red_m[r_in][q]);
+  const float mu = (M == -INFINITY) ? 0.f : M;
+
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.n_split; ++s) {
-    const int64_t pr = s * sstride + row_lin;
-    const float ms = p.part_ml[pr * 2];
-    const float w = __builtin_amdgcn_exp2f((ms - mmax) * c);
-    L += w * p.part_ml[pr * 2 + 1];
-    acc += w * *reinterpret_cast<const f32x4*>(p.part_acc + pr * D + 4 * c4);
+  if (ok)
+    for (int s = sg; s < p.n_split; s += SG) {
+      const int64_t pr = s * sstride + row;
+      const float w = __builtin_amdgcn_exp2f((p.part_ml[pr * 2] - mu) * c);
+      L += w * p.part_ml[pr * 2 + 1];
+      acc += w * *reinterpret_cast<const f32x4*>(p.part_acc + pr * D + 4 * c4);
+    }
+  red_acc[r_in][sg][c4] = acc;
+  if (c4 == 0) red_l[r_in][sg] = L;
+  __syncthreads();
+  if (sg == 0 && ok) {
+    f32x4 a = red_acc[r_in][0][c4];
+    float l = red_l[r_in][0];
+#pragma unroll
+    for (int q = 1; q < SG; ++q) {
+      a += red_acc[r_in][q][c4];
+      l += red_l[r_in][q];
+    }
+    *reinterpret_cast<f32x4*>(p.out + (int64_t)row * D + 4 * c4) = a * (1.0f / l);
   }
-  *reinterpret_cast<f32x4*>(p.out + (int64_t)row_lin * D + 4 * c4) = acc * (1.0f / L);
 }
 
 struct KernelChoice {
   int rg, pg, tpw;
 };
 
-constexpr int KV_TILE = 64;  // split granularity in positions (a multiple of every kernel's tile)
+constexpr int KV_TILE = 128;  // split granularity in positions (a multiple of every kernel's tile)
 
 // Row tiles per KV head -> (row groups, position groups, row tiles per wave).
-// Every choice keeps the wave's accumulators in registers without spilling:
-// up to 4 waves a workgroup may use the whole register file, above that two
-// waves share a SIMD.
+// Up to 8 row tiles the workgroup has 8 waves (two per SIMD, 128-position
+// tiles); every choice keeps the accumulators in registers without spilling.
 KernelChoice choose(int nrt) {
-  if (nrt <= 1) return {1, 2, 1};
-  if (nrt == 2) return {1, 2, 2};
-  if (nrt == 3) return {1, 2, 3};
-  if (nrt == 4) return {2, 2, 2};
-  if (nrt <= 6) return {2, 2, 3};
-  if (nrt <= 8) return {2, 2, 4};
+  if (nrt <= 1) return {1, 4, 1};
+  if (nrt == 2) return {1, 4, 2};
+  if (nrt == 3) return {1, 4, 3};
+  if (nrt == 4) return {2, 4, 2};
+  if (nrt <= 6) return {2, 4, 3};
+  if (nrt <= 8) return {4, 2, 2};
   if (nrt == 9) return {3, 2, 3};
   if (nrt <= 12) return {4, 1, 3};
   if (nrt <= 16) return {4, 1, 4};
@@ -472,12 +510,12 @@ template <int D>
 hipError_t launch_split_d(const AttnParams& p, const KernelChoice& kc, int nz, hipStream_t stream) {
 #define TS_CASE(RG_, PG_, TPW_) \
   if (kc.rg == RG_ && kc.pg == PG_ && kc.tpw == TPW_) return launch_split<D, RG_, PG_, TPW_>(p, nz, stream);
-  TS_CASE(1, 2, 1)
-  TS_CASE(1, 2, 2)
-  TS_CASE(1, 2, 3)
-  TS_CASE(2, 2, 2)
-  TS_CASE(2, 2, 3)
-  TS_CASE(2, 2, 4)
+  TS_CASE(1, 4, 1)
+  TS_CASE(1, 4, 2)
+  TS_CASE(1, 4, 3)
+  TS_CASE(2, 4, 2)
+  TS_CASE(2, 4, 3)
+  TS_CASE(4, 2, 2)
   TS_CASE(3, 2, 3)
   TS_CASE(4, 1, 3)
   TS_CASE(4, 1, 4)
@@ -500,7 +538,7 @@ int attn_auto_split(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int3
   const int M = (Hq / Hkv) * T;
   const int ntiles = (rows_total + KV_TILE - 1) / KV_TILE;
   const int nz = row_blocks_for(M);
-  const int target_wg = 512;  // ~2 resident workgroups on each of 256 compute units
+  const int target_wg = 256;  // one resident workgroup on each of 256 compute units
   int s = (target_wg + Hkv * nz - 1) / (Hkv * nz);
   if (s > ntiles) s = ntiles;
   if (s < 1) s = 1;
@@ -537,10 +575,10 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {
   hipError_t e = p.d == 128 ? launch_split_d<128>(p, kc, nz, stream) : launch_split_d<64>(p, kc, nz, stream);
   if (e != hipSuccess || p.n_split == 1) return e;
   if (p.d == 128) {
-    const int rpb = 256 / 32;
+    const int rpb = 1;
     hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((p.Hkv * p.M + rpb - 1) / rpb), dim3(256), 0, stream, p);
   } else {
-    const int rpb = 256 / 16;
+    const int rpb = 2;
     hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((p.Hkv * p.M + rpb - 1) / rpb), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
