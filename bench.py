@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--verify-only", action="store_true", help="time only the verification launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device-to-device copy first (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -137,6 +139,15 @@ def main():
     ws_s = torch.empty(max(1, lib.ts_partial_kv_select_workspace_size(n_ctx, T, Hq, Hkv, d, budget)), dtype=torch.uint8, device=dev)
     z_out = torch.empty_like(logits)
     torch.cuda.synchronize()
+
+    if args.calibrate_copy:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+        # scale between the counters and bytes moved (see the profiles' notes).
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
 

@@ -22,7 +22,7 @@
  * - bf16 tensors are passed as uint16_t bit patterns.
  * - A KV cache element (g, j, c) -- KV head g, cache row j, channel c -- sits
  *   at  base[g * s_head + j * s_pos + c]  (strides in elements; channels
- *   contiguous). s_pos >= d, s_head >= rows * s_pos is not required but the
+ *   contiguous). d <= s_pos <= 2^23; s_head >= rows * s_pos is not required but the
  *   rows of different heads must not overlap. Base pointers and strides must
  *   keep every row 16-byte aligned.
  * - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the

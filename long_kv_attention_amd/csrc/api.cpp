@@ -60,7 +60,8 @@ int check_attention(const char* who, const uint16_t* q, const uint16_t* k, const
   if (Hkv > 65535) return fail(TS_ENOTSUP, "%s: Hkv=%d too large", who, Hkv);
   if (n_ctx < 0) return fail(TS_EINVAL, "%s: n_ctx=%d is negative", who, n_ctx);
   if ((int64_t)n_ctx + T > (int64_t)INT32_MAX) return fail(TS_EINVAL, "%s: cache rows overflow int32", who);
-  if (s_pos < d || s_pos % 8 != 0) return fail(TS_EINVAL, "%s: s_pos=%lld must be >= d and a multiple of 8", who, (long long)s_pos);
+  if (s_pos < d || s_pos % 8 != 0 || s_pos > (1 << 23))
+    return fail(TS_EINVAL, "%s: s_pos=%lld must be >= d, a multiple of 8 and at most 2^23", who, (long long)s_pos);
   if (s_head < 0 || s_head % 8 != 0) return fail(TS_EINVAL, "%s: s_head=%lld must be >= 0 and a multiple of 8", who, (long long)s_head);
   if (Hkv > 1 && s_head == 0) return fail(TS_EINVAL, "%s: s_head=0 with %d KV heads", who, Hkv);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))

@@ -74,6 +74,9 @@ struct Cfg {
 
 // Reference-max slack of the online softmax, in log2 units.
 constexpr float LAZY_LOG2 = 8.0f;
+// Running-max start: finite, so no -inf special cases (masked scores are -inf
+// and give exp2(-inf) = 0; a row with any visible score moves the max).
+constexpr float NEG_BIG = -1.0e30f;
 
 __device__ inline float lane_max4(float a, float b, float c, float d) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
@@ -99,13 +102,23 @@ __device__ inline unsigned int bf16x2_to_f16x2(unsigned int w) {
   return __builtin_bit_cast(unsigned int, h);
 }
 
-// One wave-wide asynchronous copy global -> LDS (16 B per lane): lane l's
-// 16 bytes land at LDS byte offset lds_off + 16 * l. The compiler does not
-// see the LDS write; callers order it with explicit vmcnt waits and barriers.
-// One wait state separates the M0 write from the DMA that reads it.
-__device__ inline void dma16(const void* g, unsigned int lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"((unsigned long long)g) : "memory", "m0");
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (gfx9 layout): 48-bit base, stride 0, num_records bytes.
+// Reads at offsets >= num_records are out of range and do not touch memory.
+__device__ inline i32x4 buffer_desc(const void* base, unsigned int num_records) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  return i32x4{(int)(unsigned int)b, (int)((unsigned int)(b >> 32) & 0xffffu), (int)num_records, 0x00020000};
+}
+
+// One wave-wide asynchronous copy global -> LDS (16 B per lane): lane l's 16
+// bytes come from the buffer at its per-lane byte offset `off` and land at LDS
+// byte offset lds_off + 16 * l. The compiler does not see the LDS write;
+// callers order it with explicit vmcnt waits and barriers. One wait state
+// separates the M0 write from the load that reads it.
+__device__ inline void dma16(i32x4 desc, unsigned int off, unsigned int lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc) : "memory", "m0");
 }
 
 template <int N>
@@ -153,21 +166,34 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   // or V. Lane l writes physical chunk l % LANES_PER_ROW of its row; it fetches
   // the logical chunk that the swizzle maps there (K: chunk ^ row, V: chunk ^
   // 2*row, both mod NCH), which keeps the later fragment reads conflict-free.
-  // Rows past the cache are clamped to the last row (their scores are masked).
+  // The per-lane byte offsets inside a tile are fixed, so they are computed
+  // once; a tile only moves the buffer descriptor (scalar work). The
+  // descriptor ends at the last cache row, so rows past it are never read.
+  constexpr int DMA_PER_WAVE = (C::DMA_PER_STAGE + C::NW - 1) / C::NW;
   const int dma_row = lane / C::LANES_PER_ROW;
   const int dma_pc = lane % C::LANES_PER_ROW;
+  const int64_t row_bytes = p.s_pos * 2;
+  unsigned int dma_off[DMA_PER_WAVE];
+#pragma unroll
+  for (int jj = 0; jj < DMA_PER_WAVE; ++jj) {
+    const int j = wave + jj * C::NW;
+    const bool is_v = j >= C::DMA_PER_TENSOR;
+    const int r = (is_v ? j - C::DMA_PER_TENSOR : j) * C::ROWS_PER_DMA + dma_row;
+    const int ch = dma_pc ^ (is_v ? ((2 * r) & (C::NCH - 1)) : (r & (C::NCH - 1)));
+    dma_off[jj] = (unsigned int)(r * row_bytes) + ch * 16;
+  }
   auto issue_tile = [&](int tile) {
     const unsigned int slot = ring_off + (unsigned int)((tile % STAGES) * C::STAGE_BYTES);
+    const int64_t tile_bytes = (int64_t)tile * TN * row_bytes;
+    const int64_t rem = (int64_t)(rows_total - tile * TN) * row_bytes;
+    const unsigned int nrec = rem > 0xffffffffll ? 0xffffffffu : (unsigned int)rem;
+    const i32x4 kdesc = buffer_desc(reinterpret_cast<const unsigned char*>(kbase) + tile_bytes, nrec);
+    const i32x4 vdesc = buffer_desc(reinterpret_cast<const unsigned char*>(vbase) + tile_bytes, nrec);
 #pragma unroll
-    for (int jj = 0; jj < (C::DMA_PER_STAGE + C::NW - 1) / C::NW; ++jj) {
+    for (int jj = 0; jj < DMA_PER_WAVE; ++jj) {
       const int j = wave + jj * C::NW;
-      if (C::DMA_PER_STAGE % C::NW == 0 || j < C::DMA_PER_STAGE) {
-        const bool is_v = j >= C::DMA_PER_TENSOR;
-        const int r = (is_v ? j - C::DMA_PER_TENSOR : j) * C::ROWS_PER_DMA + dma_row;
-        const int ch = dma_pc ^ (is_v ? ((2 * r) & (C::NCH - 1)) : (r & (C::NCH - 1)));
-        const int pos = min(tile * TN + r, rows_total - 1);
-        dma16((is_v ? vbase : kbase) + (int64_t)pos * p.s_pos + ch * 8, slot + j * 1024);
-      }
+      if (C::DMA_PER_STAGE % C::NW == 0 || j < C::DMA_PER_STAGE)
+        dma16(j >= C::DMA_PER_TENSOR ? vdesc : kdesc, dma_off[jj], slot + j * 1024);
     }
   };
 
@@ -204,15 +230,24 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     }
   }
 
+  // O^T accumulators, plus one more tile per row tile that multiplies P by an
+  // all-ones "value" fragment: every entry of it is the row's running sum of
+  // the (f16-rounded) probabilities, so the sum needs no VALU adds or shuffles.
   f32x4 o[TPW][C::CT];
-  float m_run[TPW], l_run[TPW];
+  f32x4 lsum[TPW];
+  float m_run[TPW], m_thr[TPW];
+  const float lazy_raw = LAZY_LOG2 / c;   // slack in raw score units
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
+    m_run[t] = NEG_BIG;
+    m_thr[t] = NEG_BIG;
+    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ct = 0; ct < C::CT; ++ct) o[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  f16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
 
   // prologue: STAGES-1 tiles in flight
 #pragma unroll
@@ -238,6 +273,22 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 
     const unsigned char* kl = lds + (tile % STAGES) * C::STAGE_BYTES;
     const unsigned char* vl = kl + C::TILE_BYTES;
+
+    // ---- V: bf16 -> f16 in place, once per tile, shared by all row groups ----
+    {
+      unsigned char* vw = lds + (tile % STAGES) * C::STAGE_BYTES + C::TILE_BYTES;
+#pragma unroll
+      for (int it = 0; it < (C::TILE_BYTES / 16 + C::NT - 1) / C::NT; ++it) {
+        const int ch = tid + it * C::NT;
+        if (C::TILE_BYTES / 16 % C::NT == 0 || ch < C::TILE_BYTES / 16) {
+          u32x4 w = *reinterpret_cast<const u32x4*>(vw + ch * 16);
+          w = u32x4{bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z), bf16x2_to_f16x2(w.w)};
+          // rows past the cache were not loaded: zero them (P is 0 there)
+          if (tile * TN + ch / C::NCH >= rows_total) w = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(vw + ch * 16) = w;
+        }
+      }
+    }
 
     // ---- S^T = K Q^T over this wave's 32 positions ----
     f32x4 s[TPW][2];
@@ -295,34 +346,31 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
                        lane_max4(s[t][1][0], s[t][1][1], s[t][1][2], s[t][1][3]));
       mx = group4_max(mx);
       // Lazy rescale: the reference max only moves when the tile max exceeds
-      // it by more than 2^8 in probability (or on the first visible score),
-      // so p = exp2(s*c - m*c) stays <= 256 and the O rescale is rare.
-      const bool bump = (mx - m_run[t]) * c > LAZY_LOG2 || (m_run[t] == -INFINITY && mx != -INFINITY);
+      // it by more than 2^8 in probability, so p = exp2(s*c - m*c) stays <= 256
+      // (exact enough in f16) and the O rescale is rare.
+      const bool bump = mx > m_thr[t];
       if (__ballot(bump)) {
         const float m_new = bump ? mx : m_run[t];
-        const float alpha = (m_run[t] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
+        const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
         m_run[t] = m_new;
-        l_run[t] *= alpha;
+        m_thr[t] = m_new + lazy_raw;
+        lsum[t] *= alpha;
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct) o[t][ct] *= alpha;
       }
-      const float m_use = (m_run[t] == -INFINITY) ? 0.f : m_run[t];
-      const float nmc = -m_use * c;
-      float psum = 0.f;
+      const float nmc = -m_run[t] * c;
       f16x8 f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][0][i], c, nmc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][1][i], c, nmc));
-        psum += p0 + p1;
-        f[i] = (_Float16)p0;
-        f[4 + i] = (_Float16)p1;
+        f[i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[t][0][i], c, nmc));
+        f[4 + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[t][1][i], c, nmc));
       }
       pfrag[t] = f;
-      l_run[t] += psum;
+      lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, f, lsum[t], 0, 0, 0);
     }
 
-    // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads, bf16 -> f16) ----
+    // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads) ----
+    __builtin_amdgcn_s_barrier();  // the tile's V is f16 now (converted below the first barrier)
     {
       const int r_lo = 32 * pg + 4 * kg + (l16 >> 2);
       const int swz = (2 * r_lo) & (C::NCH - 1);  // same for r_lo + 16
@@ -334,9 +382,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         const LDS_AS s16x4* a_hi = (const LDS_AS s16x4*)(const LDS_AS unsigned char*)(vl + (r_lo + 16) * C::ROWB + off);
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)a_lo);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)a_hi);
-        const u32x4 wb = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        const u32x4 wh = {bf16x2_to_f16x2(wb.x), bf16x2_to_f16x2(wb.y), bf16x2_to_f16x2(wb.z), bf16x2_to_f16x2(wb.w)};
-        const f16x8 vf = __builtin_bit_cast(f16x8, wh);
+        const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
           if (tile_on[t]) o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfrag[t], o[t][ct], 0, 0, 0);
@@ -344,12 +390,10 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     }
   }
 
-  // ---- per-row sums across the 4 lane groups ----
+  // ---- per-row probability sums (every entry of lsum holds the full sum) ----
+  float l_run[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    l_run[t] += __shfl_xor(l_run[t], 16);
-    l_run[t] += __shfl_xor(l_run[t], 32);
-  }
+  for (int t = 0; t < TPW; ++t) l_run[t] = lsum[t][0];
 
   // ---- merge the PG position groups of each row group through LDS ----
   if constexpr (PG > 1) {
@@ -373,7 +417,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 #pragma unroll
         for (int q = 1; q < PG; ++q)
           mm = fmaxf(mm, reinterpret_cast<const float*>(lds + ((q - 1) * RG + rg) * SLOT + OSLOT)[l16]);
-        const float mu = (mm == -INFINITY) ? 0.f : mm;
+        const float mu = mm;  // finite: running maxima start at NEG_BIG
         const float w0 = __builtin_amdgcn_exp2f((m_run[t] - mu) * c);
         float ll = l_run[t] * w0;
 #pragma unroll
