@@ -273,21 +273,13 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 
     const unsigned char* kl = lds + (tile % STAGES) * C::STAGE_BYTES;
     const unsigned char* vl = kl + C::TILE_BYTES;
-
-    // ---- V: bf16 -> f16 in place, once per tile, shared by all row groups ----
-    {
+    if ((tile + 1) * TN > rows_total) {
+      // V rows past the cache were not loaded (the descriptor bounds the read)
+      // and hold stale bits; P is exactly 0 there, but 0 * NaN would poison O.
       unsigned char* vw = lds + (tile % STAGES) * C::STAGE_BYTES + C::TILE_BYTES;
-#pragma unroll
-      for (int it = 0; it < (C::TILE_BYTES / 16 + C::NT - 1) / C::NT; ++it) {
-        const int ch = tid + it * C::NT;
-        if (C::TILE_BYTES / 16 % C::NT == 0 || ch < C::TILE_BYTES / 16) {
-          u32x4 w = *reinterpret_cast<const u32x4*>(vw + ch * 16);
-          w = u32x4{bf16x2_to_f16x2(w.x), bf16x2_to_f16x2(w.y), bf16x2_to_f16x2(w.z), bf16x2_to_f16x2(w.w)};
-          // rows past the cache were not loaded: zero them (P is 0 there)
-          if (tile * TN + ch / C::NCH >= rows_total) w = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(vw + ch * 16) = w;
-        }
-      }
+      for (int ch = tid; ch < C::TILE_BYTES / 16; ch += C::NT)
+        if (tile * TN + ch / C::NCH >= rows_total) *reinterpret_cast<u32x4*>(vw + ch * 16) = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
     }
 
     // ---- S^T = K Q^T over this wave's 32 positions ----
@@ -369,8 +361,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, f, lsum[t], 0, 0, 0);
     }
 
-    // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads) ----
-    __builtin_amdgcn_s_barrier();  // the tile's V is f16 now (converted below the first barrier)
+    // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads, bf16 -> f16 in registers) ----
     {
       const int r_lo = 32 * pg + 4 * kg + (l16 >> 2);
       const int swz = (2 * r_lo) & (C::NCH - 1);  // same for r_lo + 16
@@ -382,7 +373,9 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         const LDS_AS s16x4* a_hi = (const LDS_AS s16x4*)(const LDS_AS unsigned char*)(vl + (r_lo + 16) * C::ROWB + off);
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)a_lo);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)a_hi);
-        const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const u32x4 wb = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const f16x8 vf = __builtin_bit_cast(
+            f16x8, u32x4{bf16x2_to_f16x2(wb.x), bf16x2_to_f16x2(wb.y), bf16x2_to_f16x2(wb.z), bf16x2_to_f16x2(wb.w)});
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
           if (tile_on[t]) o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfrag[t], o[t][ct], 0, 0, 0);
