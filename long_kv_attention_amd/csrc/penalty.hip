@@ -47,14 +47,25 @@ __device__ inline float key2f(unsigned int k) {
 }
 __device__ inline unsigned long long to_fix(float e) { return (unsigned long long)(e * FIX_SCALE); }
 
+constexpr int NCAND = MAX_V / 32;  // candidate keys of the cut bin, in the bitmap's space
+
 struct Smem {
-  unsigned int bitmap[MAX_V / 32];
+  union {
+    unsigned int bitmap[MAX_V / 32];   // window ids (passes 0-1)
+    unsigned int cand[NCAND];          // keys of the top-p cut bin (after pass 1)
+  };
   unsigned long long hmass[H1];
   unsigned int hcnt[H1];
   unsigned long long red64[NWAVES];
   float redf[NWAVES];
   unsigned int redu[NWAVES];
-  int bin;
+  float wmass[NWAVES];                 // kept mass of each wave's id segment
+  unsigned int wtie[NWAVES];           // ties at the cut in each wave's segment
+  int lowbin;
+  unsigned long long above;
+  unsigned int ncand;
+  int tok;
+  int last;
 };
 
 __device__ inline float block_max(float x, Smem& s) {
@@ -63,16 +74,6 @@ __device__ inline float block_max(float x, Smem& s) {
   __syncthreads();
   float r = s.redf[0];
   for (int w = 1; w < NWAVES; ++w) r = fmaxf(r, s.redf[w]);
-  __syncthreads();
-  return r;
-}
-
-__device__ inline float block_sum(float x, Smem& s) {
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  if ((threadIdx.x & 63) == 0) s.redf[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float r = 0.f;
-  for (int w = 0; w < NWAVES; ++w) r += s.redf[w];
   __syncthreads();
   return r;
 }
@@ -107,55 +108,106 @@ __device__ inline unsigned long long block_scan64(unsigned long long x, Smem& s,
   return pre + incl - x;
 }
 
-__device__ inline unsigned int block_scan32(unsigned int x, Smem& s, unsigned int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned int incl = x;
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
+__device__ inline unsigned long long lanemask_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
+
+// Lowest non-empty bin of s.hmass/s.hcnt[0, nb) whose mass from the top
+// (exclusive) is <= P; returns it and its exclusive mass above.
+__device__ inline int crossing_bin(int nb, unsigned long long P, Smem& s, unsigned long long* above) {
+  const int tid = threadIdx.x;
+  const int per = nb / PT_THREADS > 0 ? nb / PT_THREADS : 1;
+  const bool owner = tid * per < nb;
+  const int hi_bin = nb - 1 - tid * per;
+  unsigned long long m = 0;
+  if (owner)
+    for (int i = 0; i < per; ++i) m += s.hmass[hi_bin - i];
+  if (tid == 0) s.lowbin = nb;
+  unsigned long long tot;
+  const unsigned long long before = block_scan64(m, s, &tot);  // ends with a barrier
+  if (owner) {
+    unsigned long long acc = before;
+    int best = nb;
+    for (int i = 0; i < per; ++i) {
+      const int b = hi_bin - i;
+      if (s.hcnt[b] && acc <= P) best = b;
+      acc += s.hmass[b];
+    }
+    if (best < nb) atomicMin(&s.lowbin, best);
   }
-  if (lane == 63) s.redu[wave] = incl;
   __syncthreads();
-  unsigned int pre = 0, tot = 0;
-  for (int w = 0; w < NWAVES; ++w) {
-    if (w < wave) pre += s.redu[w];
-    tot += s.redu[w];
+  const int b = s.lowbin;
+  if (owner && b <= hi_bin && b > hi_bin - per) {
+    unsigned long long acc = before;
+    for (int i = 0; i < per && hi_bin - i != b; ++i) acc += s.hmass[hi_bin - i];
+    s.above = acc;
   }
   __syncthreads();
-  *total = tot;
-  return pre + incl - x;
+  *above = s.above;
+  return b;
 }
 
-__device__ inline float block_scanf(float x, Smem& s, float* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float incl = x;
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
+constexpr int UNR = 32;  // loads in flight per thread in every pass (~128 KB per CU)
+
+// Thread-strided pass over n floats with UNR loads issued before any use.
+template <typename F>
+__device__ inline void strided_pass(const float* src, int n, F&& f) {
+  for (int i0 = threadIdx.x; i0 < n; i0 += UNR * PT_THREADS) {
+    float v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = i0 + u * PT_THREADS;
+      v[u] = i < n ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = i0 + u * PT_THREADS;
+      if (i < n) f(i, v[u]);
+    }
   }
-  if (lane == 63) s.redf[wave] = incl;
-  __syncthreads();
-  float pre = 0.f, tot = 0.f;
-  for (int w = 0; w < NWAVES; ++w) {
-    if (w < wave) pre += s.redf[w];
-    tot += s.redf[w];
+}
+
+// Ordered pass of one wave over ids [s0, s1), 64 ids per step in ascending
+// order, UNR steps' loads in flight. f(i, valid, value) is called by all lanes
+// (it may use ballots); wave-uniform bounds.
+template <typename F>
+__device__ inline void wave_pass(const float* src, int s0, int s1, F&& f) {
+  const int lane = threadIdx.x & 63;
+  for (int b0 = s0; b0 < s1; b0 += UNR * 64) {
+    float v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = b0 + u * 64 + lane;
+      v[u] = i < s1 ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = b0 + u * 64 + lane;
+      if (b0 + u * 64 < s1) f(i, i < s1, v[u]);
+    }
   }
-  __syncthreads();
-  *total = tot;
-  return pre + (incl - x);
+}
+
+// Append `key` to s.cand when `take`: one LDS atomic per wave (ballot + rank).
+__device__ inline void append_cand(bool take, unsigned int key, Smem& s) {
+  const unsigned long long m = __ballot(take);
+  if (!m) return;
+  const int leader = __ffsll((long long)m) - 1;
+  unsigned int base = 0;
+  if ((int)(threadIdx.x & 63) == leader) base = atomicAdd(&s.ncand, (unsigned int)__popcll(m));
+  base = __shfl(base, leader);
+  if (take) s.cand[base + (unsigned int)__popcll(m & lanemask_lt())] = key;
 }
 
 __global__ __launch_bounds__(PT_THREADS) void penalty_kernel(const PenaltyParams p) {
   __shared__ Smem s;
-  __shared__ int s_lowbin;
-  __shared__ unsigned long long s_above;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int V = p.V;
   const float* x = p.logits + (int64_t)row * V;
   float* z = p.logits_out + (int64_t)row * V;
 
-  // 0. window bitmap
+  // 0. window bitmap (set semantics: duplicates are harmless)
   const int nwords = (V + 31) / 32;
   for (int w = tid; w < nwords; w += PT_THREADS) s.bitmap[w] = 0u;
   __syncthreads();
@@ -168,218 +220,181 @@ __global__ __launch_bounds__(PT_THREADS) void penalty_kernel(const PenaltyParams
   }
   __syncthreads();
 
-  // 1. penalty, temperature, max
+  // 1. penalty, temperature, row max
   float mx = -INFINITY;
-  for (int i = tid; i < V; i += PT_THREADS) {
-    float v = x[i];
+  strided_pass(x, V, [&](int i, float v) {
     if ((s.bitmap[i >> 5] >> (i & 31)) & 1u) v = v > 0.f ? v / p.penalty : v * p.penalty;
     v = v / p.temperature;
     z[i] = v;
     mx = fmaxf(mx, v);
-  }
-  const float zmax = block_max(mx, s);
+  });
+  const float zmax = block_max(mx, s);  // its barriers also retire the bitmap
   const float ln_min_p = logf(p.min_p);  // -inf for min_p = 0
 
-  // 2. mass histogram over the top 12 key bits, total mass (fixed point)
+  // 2. top-p cut: mass histogram over the top 12 key bits (2^-40 fixed point,
+  // integer LDS atomics), then two 10-bit refinements inside the bin where the
+  // mass counted from the top crosses top_p * total.
   const bool all_top = p.top_p >= 1.0f;
-  unsigned int cut = 0u;          // keys above `cut` are kept by top-p
-  unsigned int cut_ties = 0u;     // ties at `cut` kept, earliest ids first
-  unsigned int cut_count = 0u;    // ties at `cut` in the row
+  unsigned int cut = 0u, cut_ties = 0u, cut_count = 0u;
   if (!all_top) {
     for (int b = tid; b < H1; b += PT_THREADS) {
       s.hmass[b] = 0ull;
       s.hcnt[b] = 0u;
     }
+    if (tid == 0) s.ncand = 0;
     __syncthreads();
     unsigned long long zsum = 0;
-    for (int i = tid; i < V; i += PT_THREADS) {
-      const float v = z[i];
+    strided_pass(z, V, [&](int, float v) {
       const unsigned long long f = to_fix(__expf(v - zmax));
       const unsigned int b = f2key(v) >> (32 - H1_BITS);
       atomicAdd(&s.hmass[b], f);
       atomicAdd(&s.hcnt[b], 1u);
       zsum += f;
-    }
+    });
     const unsigned long long Z = block_sum64(zsum, s);
     unsigned long long P = (unsigned long long)((double)p.top_p * (double)Z);
-
-    // crossing search: digit 1 (12 bits), then 2 x 10 bits
-    unsigned int prefix = 0u;
-    int shift = 32;
-    for (int pass = 0; pass < 3; ++pass) {
-      const int nbits = pass == 0 ? H1_BITS : 10;
-      const int nb = 1 << nbits;
-      const int new_shift = shift - nbits;
-      if (pass > 0) {
-        __syncthreads();
-        for (int b = tid; b < nb; b += PT_THREADS) {
-          s.hmass[b] = 0ull;
-          s.hcnt[b] = 0u;
+    unsigned long long above;
+    unsigned int prefix = (unsigned int)crossing_bin(H1, P, s, &above);
+    P -= above;
+    int shift = 32 - H1_BITS;
+    const bool in_lds = s.hcnt[prefix] <= (unsigned int)NCAND;
+    if (in_lds) {
+      // every wave walks whole 64-id steps so the ballots see all lanes
+      const int seg = ((V + NWAVES - 1) / NWAVES + 63) / 64 * 64;
+      wave_pass(z, wave * seg, min(wave * seg + seg, V), [&](int, bool valid, float v) {
+        const unsigned int key = f2key(v);
+        append_cand(valid && (key >> shift) == prefix, key, s);
+      });
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+      const int nb = 1 << 10;
+      const int new_shift = shift - 10;
+      __syncthreads();
+      for (int b = tid; b < nb; b += PT_THREADS) {
+        s.hmass[b] = 0ull;
+        s.hcnt[b] = 0u;
+      }
+      __syncthreads();
+      if (in_lds) {
+        const unsigned int n = s.ncand;
+        for (unsigned int i = tid; i < n; i += PT_THREADS) {
+          const unsigned int key = s.cand[i];
+          if ((key >> shift) == prefix) {
+            const unsigned int b = (key >> new_shift) & (nb - 1);
+            atomicAdd(&s.hmass[b], to_fix(__expf(key2f(key) - zmax)));
+            atomicAdd(&s.hcnt[b], 1u);
+          }
         }
-        __syncthreads();
-        for (int i = tid; i < V; i += PT_THREADS) {
-          const float v = z[i];
+      } else {
+        strided_pass(z, V, [&](int, float v) {
           const unsigned int key = f2key(v);
           if ((key >> shift) == prefix) {
             const unsigned int b = (key >> new_shift) & (nb - 1);
             atomicAdd(&s.hmass[b], to_fix(__expf(v - zmax)));
             atomicAdd(&s.hcnt[b], 1u);
           }
-        }
-        __syncthreads();
-      }
-      // lowest non-empty bin whose exclusive mass from the top is <= P
-      const int per = nb / PT_THREADS > 0 ? nb / PT_THREADS : 1;
-      const bool owner = tid * per < nb;
-      const int hi_bin = nb - 1 - tid * per;
-      unsigned long long m = 0;
-      if (owner)
-        for (int i = 0; i < per; ++i) m += s.hmass[hi_bin - i];
-      if (tid == 0) s_lowbin = nb;
-      unsigned long long tot;
-      const unsigned long long before = block_scan64(m, s, &tot);
-      if (owner) {
-        unsigned long long acc = before;
-        int best = nb;
-        for (int i = 0; i < per; ++i) {
-          const int b = hi_bin - i;
-          if (s.hcnt[b] && acc <= P) best = b;
-          acc += s.hmass[b];
-        }
-        if (best < nb) atomicMin(&s_lowbin, best);
+        });
       }
       __syncthreads();
-      const int b = s_lowbin;
-      // exclusive mass above bin b (recomputed by the owner of b)
-      if (owner && b <= hi_bin && b > hi_bin - per) {
-        unsigned long long acc = before;
-        for (int i = 0; i < per; ++i) {
-          if (hi_bin - i == b) break;
-          acc += s.hmass[hi_bin - i];
-        }
-        s_above = acc;
-      }
-      __syncthreads();
-      P -= s_above;
-      if (pass == 2) cut_count = s.hcnt[b];
-      prefix = (prefix << nbits) | (unsigned int)b;
+      const int b = crossing_bin(nb, P, s, &above);
+      P -= above;
+      if (pass == 1) cut_count = s.hcnt[b];
+      prefix = (prefix << 10) | (unsigned int)b;
       shift = new_shift;
     }
     cut = prefix;
     const unsigned long long ecut = to_fix(__expf(key2f(cut) - zmax));
-    // ties at the cut: the t-th (0-based, ids ascending) has mass-before = A + t * ecut
-    unsigned long long nt = ecut ? P / ecut + 1ull : (unsigned long long)cut_count;
+    // ties at the cut: the t-th (0-based, ids ascending) has mass before it = above + t * ecut
+    const unsigned long long nt = ecut ? P / ecut + 1ull : (unsigned long long)cut_count;
     cut_ties = nt < cut_count ? (unsigned int)nt : cut_count;
-    __syncthreads();
   }
 
-  // 5./6. keep mask, kept mass, then probabilities and token. Elements are
-  // visited in rounds of 4 consecutive ids per thread so that ties at the cut
-  // are ranked by id with a block scan (only needed when some ties drop out).
+  // 3./4. keep mask, kept mass, probabilities and the token. Each wave owns a
+  // contiguous id segment and walks it in order, so ties at the cut are ranked
+  // by id with ballots, and the inverse CDF needs a single search.
   const bool rank_ties = !all_top && cut_ties < cut_count;
-  auto round_keep = [&](int base, float* ev, unsigned int* kept_bits, unsigned int* tie_run) {
-    unsigned int tflags = 0u, gflags = 0u;
-    float zv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = base + 4 * tid + e;
-      zv[e] = -INFINITY;
-      if (i < V) {
-        zv[e] = z[i];
-        const unsigned int key = f2key(zv[e]);
-        gflags |= (unsigned int)(all_top || key > cut) << e;
-        tflags |= (unsigned int)(!all_top && key == cut) << e;
-      }
-    }
-    unsigned int tie_b = 0u;
-    if (rank_ties) {
-      unsigned int total;
-      tie_b = *tie_run + block_scan32(__popc(tflags), s, &total);
-      *tie_run += total;
-    }
-    unsigned int kb = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = base + 4 * tid + e;
-      bool top = (gflags >> e) & 1u;
-      if ((tflags >> e) & 1u) {
-        top = !rank_ties || tie_b < cut_ties;
-        ++tie_b;
-      }
-      const float d = zv[e] - zmax;
-      const bool k = i < V && top && d >= ln_min_p;
-      ev[e] = k ? __expf(d) : 0.f;
-      kb |= (unsigned int)k << e;
-    }
-    *kept_bits = kb;
+  const int seg = ((V + NWAVES - 1) / NWAVES + 63) / 64 * 64;
+  const int s0 = min(wave * seg, V);
+  const int s1 = min(s0 + seg, V);
+  unsigned int tie_base = 0;
+  if (rank_ties) {
+    unsigned int c = 0;
+    wave_pass(z, s0, s1, [&](int, bool valid, float v) { c += valid && f2key(v) == cut; });
+    for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m);
+    if (lane == 0) s.wtie[wave] = c;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) tie_base += s.wtie[w];
+  }
+  // keep decision of an id (all lanes call it; tie_run counts ties of earlier ids)
+  auto keep_of = [&](bool valid, float zv, unsigned int& tie_run) -> bool {
+    const unsigned int key = f2key(zv);
+    bool top = all_top || key > cut;
+    const bool tie = valid && !all_top && key == cut;
+    const unsigned long long tm = __ballot(tie);
+    if (tie) top = !rank_ties || (tie_run + (unsigned int)__popcll(tm & lanemask_lt())) < cut_ties;
+    tie_run += (unsigned int)__popcll(tm);
+    return valid && top && (zv - zmax >= ln_min_p);
   };
 
-  float kept_sum = 0.f;
+  float wsum = 0.f;
   {
-    unsigned int tie_run = 0u;
-    for (int base = 0; base < V; base += 4 * PT_THREADS) {
-      float ev[4];
-      unsigned int kb;
-      round_keep(base, ev, &kb, &tie_run);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = base + 4 * tid + e;
-        if (i < V && p.keep) p.keep[(int64_t)row * V + i] = (uint8_t)((kb >> e) & 1u);
-        kept_sum += ev[e];
-      }
-    }
+    unsigned int tie_run = tie_base;
+    wave_pass(z, s0, s1, [&](int i, bool valid, float zv) {
+      const bool k = keep_of(valid, zv, tie_run);
+      if (valid && p.keep) p.keep[(int64_t)row * V + i] = (uint8_t)k;
+      wsum += k ? __expf(zv - zmax) : 0.f;
+    });
   }
-  const float S = block_sum(kept_sum, s);
+  for (int m = 32; m >= 1; m >>= 1) wsum += __shfl_xor(wsum, m);
+  if (lane == 0) s.wmass[wave] = wsum;
+  if (tid == 0) {
+    s.tok = -1;
+    s.last = -1;
+  }
+  __syncthreads();
+  float S = 0.f, wbase = 0.f;
+  for (int w = 0; w < NWAVES; ++w) {
+    if (w < wave) wbase += s.wmass[w];
+    S += s.wmass[w];
+  }
   if (!p.probs && !p.token) return;
 
+  const float inv = 1.0f / S;
   const float target = p.u ? p.u[row] * S : 0.f;
-  float run = 0.f;
-  int found = -1;
-  int last_kept = -1;
-  unsigned int tie_run = 0u;
-  __shared__ int s_tok;
-  if (tid == 0) s_tok = 0x7fffffff;
-  for (int base = 0; base < V; base += 4 * PT_THREADS) {
-    float ev[4];
-    unsigned int kb;
-    round_keep(base, ev, &kb, &tie_run);
-    const float inv = 1.0f / S;
-    float local = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = base + 4 * tid + e;
-      if (i < V && p.probs) p.probs[(int64_t)row * V + i] = ev[e] * inv;
-      local += ev[e];
-      if ((kb >> e) & 1u) last_kept = i;
-    }
-    if (p.token && found < 0) {
-      float total;
-      const float before = run + block_scanf(local, s, &total);
-      float acc = before;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc += ev[e];
-        if (((kb >> e) & 1u) && acc > target && before <= target) {
-          // first element of this thread to cross; threads are in id order
-          atomicMin(&s_tok, base + 4 * tid + e);
-          break;
+  const bool mine = p.token && target >= wbase && target < wbase + s.wmass[wave];
+  {
+    unsigned int tie_run = tie_base;
+    float run = wbase;
+    bool done = false;
+    int last_kept = -1;
+    wave_pass(z, s0, s1, [&](int i, bool valid, float zv) {
+      const bool k = keep_of(valid, zv, tie_run);
+      const float e = k ? __expf(zv - zmax) : 0.f;
+      if (valid && p.probs) p.probs[(int64_t)row * V + i] = e * inv;
+      const unsigned long long km = __ballot(k);
+      const int b0 = i - lane;
+      if (km) last_kept = b0 + 63 - __clzll(km);
+      if (mine && !done) {
+        // inclusive prefix of e over the 64 lanes (ids ascending)
+        float incl = e;
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(incl, off);
+          if (lane >= off) incl += y;
         }
+        const unsigned long long hit = __ballot(k && run + incl > target);
+        if (hit) {
+          if (lane == 0) s.tok = b0 + __ffsll((long long)hit) - 1;
+          done = true;
+        }
+        run += __shfl(incl, 63);
       }
-      __syncthreads();
-      if (s_tok != 0x7fffffff) found = s_tok;
-      run += total;
-      __syncthreads();
-    }
+    });
+    if (lane == 0 && last_kept >= 0) atomicMax(&s.last, last_kept);
+    if (mine && !done && lane == 0) s.tok = last_kept;  // rounding left u*S past this wave's sum
   }
-  if (p.token) {
-    // rounding may leave u*S just above the last cumulative sum: take the last kept id
-    __shared__ int s_last;
-    if (tid == 0) s_last = -1;
-    __syncthreads();
-    atomicMax(&s_last, last_kept);
-    __syncthreads();
-    if (tid == 0) p.token[row] = found >= 0 ? found : s_last;
-  }
+  __syncthreads();
+  // u*S may round to (or past) the total: fall back to the last kept id
+  if (p.token && tid == 0) p.token[row] = s.tok >= 0 ? s.tok : s.last;
 }
 
 }  // namespace

@@ -44,21 +44,42 @@ __device__ inline unsigned int f2key(float f) {
 __device__ inline float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
 
-struct SelWs {
-  unsigned int* hist;  // [Hkv][HIST1]
-};
+// Lanes below the caller's in the wave.
+__device__ inline unsigned long long lanemask_lt() {
+  return (1ull << (threadIdx.x & 63)) - 1ull;
+}
+__device__ inline unsigned int popc64(unsigned long long x) { return (unsigned int)__popcll(x); }
 
+// qbar_g[c] = sum over the group's query rows (G heads x T queries) in fp32.
+// Each thread sums 8 channels of every 256/(D/8)-th row, then an LDS
+// reduction over the row slots (fixed order: deterministic).
+template <int D>
 __global__ __launch_bounds__(256) void select_prologue_kernel(const SelectParams p, unsigned int* hist) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RS = 256 / LPR;       // row slots
+  __shared__ float part[RS][D];
   const int g = blockIdx.x;
-  const int G = p.Hq / p.Hkv;
-  const int rows = G * p.T;
-  const uint16_t* qg = p.q + (int64_t)g * rows * p.d;
-  for (int c = threadIdx.x; c < p.d; c += blockDim.x) {
-    float acc = 0.f;
-    for (int r = 0; r < rows; ++r) acc += __uint_as_float(((unsigned int)qg[(int64_t)r * p.d + c]) << 16);
-    p.qbar[g * p.d + c] = acc;
+  const int tid = threadIdx.x;
+  const int cg = tid % LPR, rs = tid / LPR;
+  const int rows = (p.Hq / p.Hkv) * p.T;
+  const uint16_t* qg = p.q + (int64_t)g * rows * D + cg * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = rs; r < rows; r += RS) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(qg + (int64_t)r * D);
+    acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
+    acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
+    acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
+    acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
   }
-  for (int b = threadIdx.x; b < HIST1; b += blockDim.x) hist[g * HIST1 + b] = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rs][cg * 8 + e] = acc[e];
+  for (int b = tid; b < HIST1; b += 256) hist[g * HIST1 + b] = 0u;
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+    for (int q = 0; q < RS; ++q) t += part[q][tid];
+    p.qbar[g * D + tid] = t;
+  }
 }
 
 // LPR lanes per row, each holding 8 channels; a wave covers 64/LPR rows.
@@ -172,13 +193,40 @@ __device__ inline void find_bin(const unsigned int* hist, int nbins, unsigned in
   __syncthreads();
 }
 
+constexpr int CAND_CAP = 16384;  // candidate keys of the cut bin held in LDS
+constexpr int UNR = 32;          // wave steps whose loads are in flight together (~128 KB per CU)
+
+// Ordered pass of one wave over rows [s0, s1), 64 rows per step in ascending
+// order, UNR steps' loads in flight; f(j, valid, key) is called by all lanes.
+template <typename F>
+__device__ inline void wave_pass_keys(const float* sc, int s0, int s1, F&& f) {
+  const int lane = threadIdx.x & 63;
+  for (int b0 = s0; b0 < s1; b0 += UNR * 64) {
+    float v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int j = b0 + u * 64 + lane;
+      v[u] = j < s1 ? sc[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int j = b0 + u * 64 + lane;
+      if (b0 + u * 64 < s1) f(j, j < s1, f2key(v[u]));
+    }
+  }
+}
+
 __global__ __launch_bounds__(SEL_THREADS) void select_topb_kernel(const SelectParams p, const unsigned int* ghist) {
   __shared__ unsigned int hist[HIST1];
+  __shared__ unsigned int cand[CAND_CAP];
   __shared__ unsigned int tmp[SEL_THREADS / 64];
+  __shared__ unsigned int wave_gt[SEL_THREADS / 64], wave_tie[SEL_THREADS / 64];
   __shared__ int s_bin;
-  __shared__ unsigned int s_above;
+  __shared__ unsigned int s_above, s_ncand;
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   int32_t* out = p.sel_idx + (int64_t)g * p.budget;
   const unsigned int k = (unsigned int)p.b_eff;
   for (int i = k + tid; i < p.budget; i += SEL_THREADS) out[i] = -1;
@@ -186,15 +234,42 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topb_kernel(const SelectPa
   const float* sc = p.scores + (int64_t)g * p.n_ctx;
   const int lo = p.cand_lo, hi = p.cand_hi;
 
-  // digit 1: the histogram from the scoring kernel
+  // digit 1 (top 12 key bits): the histogram built by the scoring kernel
   for (int b = tid; b < HIST1; b += SEL_THREADS) hist[b] = ghist[g * HIST1 + b];
+  if (tid == 0) s_ncand = 0;
   __syncthreads();
   find_bin(hist, HIST1, k, tmp, &s_bin, &s_above);
   unsigned int prefix = (unsigned int)s_bin;
-  unsigned int rank = k - s_above;  // rank of the cut key inside the bin (from the top)
+  unsigned int rank = k - s_above;  // rank of the cut key inside the bin, from the top
   int shift = 32 - HIST1_BITS;
+  const unsigned int bin_count = hist[prefix];
+  const bool in_lds = bin_count <= (unsigned int)CAND_CAP;
 
-  // digits 2 and 3: 10 bits each over the candidates matching the prefix
+  // every wave owns a contiguous segment of candidate rows
+  constexpr int NWV = SEL_THREADS / 64;
+  const int n = hi - lo;
+  const int seg = ((n + NWV - 1) / NWV + 63) / 64 * 64;
+  const int s0 = min(lo + wave * seg, hi);
+  const int s1 = min(s0 + seg, hi);
+
+  // gather the cut bin's keys into LDS (order irrelevant: only counted); one
+  // LDS atomic per wave step (ballot + in-wave rank)
+  if (in_lds) {
+    wave_pass_keys(sc, s0, s1, [&](int, bool valid, unsigned int key) {
+      const bool take = valid && (key >> shift) == prefix;
+      const unsigned long long m = __ballot(take);
+      if (m) {
+        const int leader = __ffsll((long long)m) - 1;
+        unsigned int base = 0;
+        if (lane == leader) base = atomicAdd(&s_ncand, (unsigned int)__popcll(m));
+        base = __shfl(base, leader);
+        if (take) cand[base + popc64(m & lanemask_lt())] = key;
+      }
+    });
+    __syncthreads();
+  }
+
+  // digits 2 and 3 (10 bits each) over the keys matching the prefix
   for (int pass = 0; pass < 2; ++pass) {
     const int nbits = 10;
     const int nb = 1 << nbits;
@@ -202,9 +277,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topb_kernel(const SelectPa
     for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0u;
     __syncthreads();
     const int new_shift = shift - nbits;
-    for (int j = lo + tid; j < hi; j += SEL_THREADS) {
-      const unsigned int key = f2key(sc[j]);
-      if ((key >> shift) == prefix) atomicAdd(&hist[(key >> new_shift) & (nb - 1)], 1u);
+    if (in_lds) {
+      const unsigned int n = s_ncand;
+      for (unsigned int i = tid; i < n; i += SEL_THREADS) {
+        const unsigned int key = cand[i];
+        if ((key >> shift) == prefix) atomicAdd(&hist[(key >> new_shift) & (nb - 1)], 1u);
+      }
+    } else {
+      for (int j = lo + tid; j < hi; j += SEL_THREADS) {
+        const unsigned int key = f2key(sc[j]);
+        if ((key >> shift) == prefix) atomicAdd(&hist[(key >> new_shift) & (nb - 1)], 1u);
+      }
     }
     __syncthreads();
     find_bin(hist, nb, rank, tmp, &s_bin, &s_above);
@@ -215,64 +298,73 @@ __global__ __launch_bounds__(SEL_THREADS) void select_topb_kernel(const SelectPa
   const unsigned int cut = prefix;        // exact key of the B'-th candidate
   const unsigned int need_ties = rank;    // ties at the cut to take, earliest rows first
 
-  // ordered emission: rows ascending, 4 per thread per round
-  unsigned int gt_run = 0, tie_run = 0;
-  for (int base = lo; base < hi; base += 4 * SEL_THREADS) {
-    unsigned int gt_flags = 0, tie_flags = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = base + 4 * tid + e;
-      if (j < hi) {
-        const unsigned int key = f2key(sc[j]);
-        gt_flags |= (key > cut) << e;
-        tie_flags |= (key == cut) << e;
-      }
-    }
-    const unsigned int packed = __popc(gt_flags) | (__popc(tie_flags) << 16);
-    unsigned int total;
-    const unsigned int before = block_exclusive_scan(packed, tmp, &total);
-    unsigned int gt_b = gt_run + (before & 0xffffu);
-    unsigned int tie_b = tie_run + (before >> 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = base + 4 * tid + e;
-      const bool gt = (gt_flags >> e) & 1u;
-      const bool tie = (tie_flags >> e) & 1u;
-      if (gt || (tie && tie_b < need_ties)) {
-        const unsigned int idx = gt_b + (tie_b < need_ties ? tie_b : need_ties);
-        if (idx < k) out[idx] = j;
-      }
-      gt_b += gt;
-      tie_b += tie;
-    }
-    gt_run += total & 0xffffu;
-    tie_run += total >> 16;
+  // ordered emission: each wave owns a contiguous segment of candidate rows;
+  // pass 1 counts, one scan over the waves gives each segment's offsets, pass 2
+  // writes in row order using ballots for the in-wave ranks.
+  unsigned int cgt = 0, ctie = 0;
+  wave_pass_keys(sc, s0, s1, [&](int, bool valid, unsigned int key) {
+    cgt += valid && key > cut;
+    ctie += valid && key == cut;
+  });
+  for (int m = 32; m >= 1; m >>= 1) {
+    cgt += __shfl_xor(cgt, m);
+    ctie += __shfl_xor(ctie, m);
   }
+  if (lane == 0) {
+    wave_gt[wave] = cgt;
+    wave_tie[wave] = ctie;
+  }
+  __syncthreads();
+  unsigned int gt_run = 0, tie_run = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_run += wave_gt[w];
+    tie_run += wave_tie[w];
+  }
+  wave_pass_keys(sc, s0, s1, [&](int j, bool valid, unsigned int key) {
+    const bool gt = valid && key > cut;
+    const bool tie = valid && key == cut;
+    const unsigned long long tie_mask = __ballot(tie);
+    const unsigned int tie_rank = tie_run + popc64(tie_mask & lanemask_lt());
+    const bool take = gt || (tie && tie_rank < need_ties);
+    const unsigned long long gt_mask = __ballot(gt);
+    const unsigned int gt_before = gt_run + popc64(gt_mask & lanemask_lt());
+    if (take) {
+      const unsigned int idx = gt_before + min(tie_rank, need_ties);
+      if (idx < k) out[idx] = j;
+    }
+    gt_run += popc64(gt_mask);
+    tie_run += popc64(tie_mask);
+  });
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void select_gather_kernel(const SelectParams p, int rows_per_block) {
   constexpr int NCH = D / 8;
+  __shared__ int src_row[256];
   const int g = blockIdx.y;
   const int n_sink_eff = min(p.n_sink, p.n_ctx);
   const int rec_lo = max(p.n_sink, p.n_ctx - p.n_recent);
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(r0 + rows_per_block, p.n_part);
   const int32_t* sel = p.sel_idx + (int64_t)g * p.budget;
-  const int nchunks = (r1 - r0) * NCH * 2;
-  for (int id = threadIdx.x; id < nchunks; id += 256) {
-    const bool is_v = id >= (r1 - r0) * NCH;
-    const int cid = is_v ? id - (r1 - r0) * NCH : id;
-    const int r = r0 + cid / NCH;
-    const int ch = cid % NCH;
+  if (threadIdx.x < r1 - r0) {
+    const int r = r0 + threadIdx.x;
     int src;
     if (r < n_sink_eff) src = r;
     else if (r < n_sink_eff + p.b_eff) src = sel[r - n_sink_eff];
     else src = rec_lo + (r - n_sink_eff - p.b_eff);
-    src = min(max(src, 0), p.n_ctx - 1);  // the selection only emits rows in [0, n_ctx)
-    const uint16_t* s = (is_v ? p.v : p.k) + (int64_t)g * p.s_head + (int64_t)src * p.s_pos + ch * 8;
-    uint16_t* d = (is_v ? p.v_part : p.k_part) + (int64_t)g * p.sp_head + (int64_t)r * p.sp_pos + ch * 8;
-    *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
+    src_row[threadIdx.x] = min(max(src, 0), p.n_ctx - 1);  // the selection only emits rows in [0, n_ctx)
+  }
+  __syncthreads();
+  const int nchunks = (r1 - r0) * NCH * 2;
+  for (int id = threadIdx.x; id < nchunks; id += 256) {
+    const bool is_v = id >= (r1 - r0) * NCH;
+    const int cid = is_v ? id - (r1 - r0) * NCH : id;
+    const int rl = cid / NCH;
+    const int ch = cid % NCH;
+    const uint16_t* s = (is_v ? p.v : p.k) + (int64_t)g * p.s_head + (int64_t)src_row[rl] * p.s_pos + ch * 8;
+    uint16_t* d = (is_v ? p.v_part : p.k_part) + (int64_t)g * p.sp_head + (int64_t)(r0 + rl) * p.sp_pos + ch * 8;
+    *reinterpret_cast<u32x4*>(d) = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s));
   }
 }
 
@@ -290,7 +382,10 @@ size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv,
 
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   unsigned int* hist = reinterpret_cast<unsigned int*>(p.sel_ws);
-  hipLaunchKernelGGL(select_prologue_kernel, dim3(p.Hkv), dim3(256), 0, stream, p, hist);
+  if (p.d == 128)
+    hipLaunchKernelGGL(select_prologue_kernel<128>, dim3(p.Hkv), dim3(256), 0, stream, p, hist);
+  else
+    hipLaunchKernelGGL(select_prologue_kernel<64>, dim3(p.Hkv), dim3(256), 0, stream, p, hist);
   if (p.n_ctx > 0) {
     // ~1024 scoring blocks over all heads, at least 256 rows each
     int chunks = (1024 + p.Hkv - 1) / p.Hkv;
@@ -304,7 +399,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   }
   hipLaunchKernelGGL(select_topb_kernel, dim3(p.Hkv), dim3(SEL_THREADS), 0, stream, p, hist);
   if (p.n_part > 0) {
-    const int rpb = 64;
+    const int rpb = 32;
     const int chunks = (p.n_part + rpb - 1) / rpb;
     if (p.d == 128)
       hipLaunchKernelGGL(select_gather_kernel<128>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, rpb);
