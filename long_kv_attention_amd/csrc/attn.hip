@@ -30,6 +30,7 @@
 #include "ts_internal.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace ts {
 namespace {
@@ -60,14 +61,17 @@ struct Cfg {
   static constexpr int DMA_PER_TENSOR = TN / ROWS_PER_DMA;
   static constexpr int DMA_PER_STAGE = 2 * DMA_PER_TENSOR;
   static constexpr int DMA_MIN_PER_WAVE = DMA_PER_STAGE / NW;  // every wave issues at least this many
+  static constexpr int DMA_T_PER_WAVE = (DMA_PER_TENSOR + NW - 1) / NW;  // per tensor, at most
+  static constexpr int DMA_T_MIN = DMA_PER_TENSOR / NW;                  // per tensor, at least
   static constexpr int ROWS_PER_BLOCK = RG * TPW * 16;
-  // keep Q in LDS when registers are short (two waves per SIMD above 4 waves)
-  static constexpr bool Q_LDS = TPW >= 4 || (NW > 4 && TPW >= 3);
   static constexpr int KV_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int Q_BYTES = Q_LDS ? ROWS_PER_BLOCK * ROWB : 0;
-  static constexpr int MERGE_BYTES = (PG - 1) * RG * (64 * CT * 16 + 2 * 16 * 4);
-  static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES;
+  static constexpr int Q_BYTES = ROWS_PER_BLOCK * ROWB;    // the block's query rows
+  static constexpr int ANC_BYTES = 1024;  // ancestor words of the tree nodes (one full 64-lane copy)
+  static constexpr int MSLOT = 64 * CT * 16 + 2 * 16 * 4;   // one wave's O^T of a row tile + m, l
+  static constexpr int MERGE_BYTES = PG * RG * MSLOT;
+  static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES + ANC_BYTES;
   static_assert(MERGE_BYTES <= KV_BYTES, "split-local merge reuses the K/V ring");
+  static_assert(CT % PG == 0, "merge splits the channel tiles evenly over position groups");
   static_assert(DMA_MIN_PER_WAVE >= 1, "every wave takes part in staging");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 };
@@ -131,6 +135,8 @@ __device__ inline unsigned int lds_offset(const void* p) {
   return (unsigned int)(uintptr_t)(const LDS_AS void*)p;
 }
 
+static_assert(std::is_standard_layout<AttnParams>::value, "kernarg offsets via offsetof");
+
 template <int D, int RG, int PG, int TPW, int STAGES>
 __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnParams p) {
   using C = Cfg<D, RG, PG, TPW, STAGES>;
@@ -161,72 +167,71 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   unsigned char* const qlds = lds + C::KV_BYTES;
   const unsigned int ring_off = lds_offset(lds);
 
-  // ---- DMA staging of one KV tile into ring slot tile % STAGES ----
-  // Instruction j of a stage covers ROWS_PER_DMA rows of K (j < DMA_PER_TENSOR)
-  // or V. Lane l writes physical chunk l % LANES_PER_ROW of its row; it fetches
-  // the logical chunk that the swizzle maps there (K: chunk ^ row, V: chunk ^
-  // 2*row, both mod NCH), which keeps the later fragment reads conflict-free.
-  // The per-lane byte offsets inside a tile are fixed, so they are computed
-  // once; a tile only moves the buffer descriptor (scalar work). The
-  // descriptor ends at the last cache row, so rows past it are never read.
-  constexpr int DMA_PER_WAVE = (C::DMA_PER_STAGE + C::NW - 1) / C::NW;
+  // ---- DMA staging of K and V tiles into ring slot tile % STAGES ----
+  // Instruction j of a tensor covers ROWS_PER_DMA rows (j < DMA_PER_TENSOR),
+  // wave w issuing j = w, w + NW, ... Lane l writes physical chunk
+  // l % LANES_PER_ROW of its row; it fetches the logical chunk that the
+  // swizzle maps there (K: chunk ^ row, V: chunk ^ 2*row, both mod NCH), which
+  // keeps the later fragment reads conflict-free. The per-lane byte offsets
+  // inside a tile are fixed, so they are computed once; a tile only moves the
+  // buffer descriptor (scalar work). The descriptor ends at the last cache
+  // row, so rows past it are never read.
   const int dma_row = lane / C::LANES_PER_ROW;
   const int dma_pc = lane % C::LANES_PER_ROW;
   const int64_t row_bytes = p.s_pos * 2;
-  unsigned int dma_off[DMA_PER_WAVE];
+  unsigned int koff[C::DMA_T_PER_WAVE], voff[C::DMA_T_PER_WAVE];
 #pragma unroll
-  for (int jj = 0; jj < DMA_PER_WAVE; ++jj) {
-    const int j = wave + jj * C::NW;
-    const bool is_v = j >= C::DMA_PER_TENSOR;
-    const int r = (is_v ? j - C::DMA_PER_TENSOR : j) * C::ROWS_PER_DMA + dma_row;
-    const int ch = dma_pc ^ (is_v ? ((2 * r) & (C::NCH - 1)) : (r & (C::NCH - 1)));
-    dma_off[jj] = (unsigned int)(r * row_bytes) + ch * 16;
+  for (int jj = 0; jj < C::DMA_T_PER_WAVE; ++jj) {
+    const int r = (wave + jj * C::NW) * C::ROWS_PER_DMA + dma_row;
+    koff[jj] = (unsigned int)(r * row_bytes) + ((dma_pc ^ (r & (C::NCH - 1))) << 4);
+    voff[jj] = (unsigned int)(r * row_bytes) + ((dma_pc ^ ((2 * r) & (C::NCH - 1))) << 4);
   }
-  auto issue_tile = [&](int tile) {
-    const unsigned int slot = ring_off + (unsigned int)((tile % STAGES) * C::STAGE_BYTES);
+  auto issue = [&](int tile, bool is_v) {
+    const unsigned int slot = ring_off + (unsigned int)((tile % STAGES) * C::STAGE_BYTES + (is_v ? C::TILE_BYTES : 0));
     const int64_t tile_bytes = (int64_t)tile * TN * row_bytes;
     const int64_t rem = (int64_t)(rows_total - tile * TN) * row_bytes;
     const unsigned int nrec = rem > 0xffffffffll ? 0xffffffffu : (unsigned int)rem;
-    const i32x4 kdesc = buffer_desc(reinterpret_cast<const unsigned char*>(kbase) + tile_bytes, nrec);
-    const i32x4 vdesc = buffer_desc(reinterpret_cast<const unsigned char*>(vbase) + tile_bytes, nrec);
+    const i32x4 desc = buffer_desc(reinterpret_cast<const unsigned char*>(is_v ? vbase : kbase) + tile_bytes, nrec);
 #pragma unroll
-    for (int jj = 0; jj < DMA_PER_WAVE; ++jj) {
+    for (int jj = 0; jj < C::DMA_T_PER_WAVE; ++jj) {
       const int j = wave + jj * C::NW;
-      if (C::DMA_PER_STAGE % C::NW == 0 || j < C::DMA_PER_STAGE)
-        dma16(j >= C::DMA_PER_TENSOR ? vdesc : kdesc, dma_off[jj], slot + j * 1024);
+      if (C::DMA_PER_TENSOR % C::NW == 0 || j < C::DMA_PER_TENSOR)
+        dma16(desc, is_v ? voff[jj] : koff[jj], slot + j * 1024);
     }
   };
 
-  // ---- queries: B operand of S^T = K Q^T (registers, or LDS for large TPW) ----
+  // ---- queries: B operand of S^T = K Q^T, from LDS ----
   const int rt_blk = blockIdx.z * (RG * TPW);   // first row tile of this block
   const int rt0 = rt_blk + rg * TPW;            // first row tile of this wave
-  bf16x8 qf[C::Q_LDS ? 1 : TPW][C::KSTEPS];
-  uint64_t anc_row[TPW];
+  // The block's query rows and the tree's ancestor words go to LDS by the
+  // same asynchronous copy as K and V, before the K/V prologue: the first
+  // tile's wait covers them, and no vector load is left pending into the loop
+  // (the compiler would wait for such a load, and with it for every copy in
+  // flight, before entering the loop). Queries are chunk-swizzled like K so
+  // the B-fragment reads are conflict-free; rows past M are outside the
+  // descriptor and are zeroed here instead (the copy skips them).
+  unsigned char* const alds = qlds + C::Q_BYTES;
   bool tile_on[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int row = (rt0 + t) * 16 + l16;
-    tile_on[t] = (rt0 + t) * 16 < M;
-    const bool row_ok = row < M;
-    anc_row[t] = p.anc[row_ok ? row % T : 0];
-    if constexpr (!C::Q_LDS) {
-      const uint16_t* qrow = p.q + ((int64_t)g * M + (row_ok ? row : 0)) * D;
+  for (int t = 0; t < TPW; ++t) tile_on[t] = (rt0 + t) * 16 < M;
+  {
+    // p is the kernel's only argument, so it starts the kernarg segment; its
+    // ancestor words are read there (taking p's address would copy it to scratch)
+    const unsigned char* kargs = (const unsigned char*)__builtin_amdgcn_kernarg_segment_ptr();
+    if (wave == 0)
+      dma16(buffer_desc(kargs + offsetof(AttnParams, anc), (unsigned int)(T * 8)), (unsigned int)(lane * 16),
+            ring_off + C::KV_BYTES + C::Q_BYTES);
+    constexpr int QD = C::ROWS_PER_BLOCK / C::ROWS_PER_DMA;   // copies of 1 KB
+    const int q_rows = M - rt_blk * 16;
+    for (int id = tid; id < C::ROWS_PER_BLOCK * C::NCH; id += C::NT)
+      if (id / C::NCH >= q_rows) *reinterpret_cast<u32x4*>(qlds + id * 16) = u32x4{0u, 0u, 0u, 0u};
+    const i32x4 qdesc = buffer_desc(p.q + ((int64_t)g * M + rt_blk * 16) * D, (unsigned int)(q_rows * C::ROWB));
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
-        u32x4 w = *reinterpret_cast<const u32x4*>(qrow + (4 * s + kg) * 8);
-        if (!row_ok) w = u32x4{0u, 0u, 0u, 0u};
-        qf[t][s] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-  }
-  if constexpr (C::Q_LDS) {
-    // rows of this block, chunk-swizzled like K so B-fragment reads are conflict-free
-    for (int id = tid; id < C::ROWS_PER_BLOCK * C::NCH; id += C::NT) {
-      const int r = id / C::NCH, ch = id % C::NCH;
-      const int row = rt_blk * 16 + r;
-      u32x4 w = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)g * M + (row < M ? row : 0)) * D + ch * 8);
-      if (row >= M) w = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(qlds + r * C::ROWB + ((ch ^ (r & (C::NCH - 1))) << 4)) = w;
+    for (int jj = 0; jj < (QD + C::NW - 1) / C::NW; ++jj) {
+      const int j = wave + jj * C::NW;
+      const int r = j * C::ROWS_PER_DMA + dma_row;
+      if (QD % C::NW == 0 || j < QD)
+        dma16(qdesc, (unsigned int)(r * C::ROWB + ((dma_pc ^ (r & (C::NCH - 1))) << 4)), ring_off + C::KV_BYTES + j * 1024);
     }
   }
 
@@ -249,38 +254,36 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
 
-  // prologue: STAGES-1 tiles in flight
+  // Ring schedule. K of tile i+STAGES is issued as soon as every wave has
+  // finished S = K Q^T of tile i; V of tile i+STAGES-1 once every wave has
+  // finished P V of tile i-1. Issue order per wave is therefore
+  //   K(t0) V(t0) ... K(t0+S-2) V(t0+S-2) K(t0+S-1) | V(t0+S-1) K(t0+S) | V(t0+S) K(t0+S+1) | ...
+  // K(i) is waited for before S of tile i, V(i) only before P V, so V(i)
+  // lands while S is computed. Copies issued after K(i): at most S-1 K tiles
+  // and S-1 V tiles (V(i) among them); after V(i): S-1 of each. A wave issues
+  // at least DMA_T_MIN copies per tensor tile, so waiting down to that many
+  // per later tile lands the tile while the later copies stay in flight.
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
-    if (t_begin + st < t_end) issue_tile(t_begin + st);
-
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    // Wait for this wave's part of `tile`; the DMAs of later tiles may stay in
-    // flight (at least DMA_MIN_PER_WAVE per later tile were issued by this wave).
-    const int later = min(STAGES - 2, t_end - 1 - tile);
-    if constexpr (STAGES >= 4) {
-      if (later >= 2) wait_vm<2 * C::DMA_MIN_PER_WAVE>();
-      else if (later == 1) wait_vm<C::DMA_MIN_PER_WAVE>();
-      else wait_vm<0>();
-    } else if constexpr (STAGES == 3) {
-      if (later >= 1) wait_vm<C::DMA_MIN_PER_WAVE>();
-      else wait_vm<0>();
-    } else {
-      wait_vm<0>();
+    if (t_begin + st < t_end) {
+      issue(t_begin + st, false);
+      issue(t_begin + st, true);
     }
-    __builtin_amdgcn_s_barrier();  // every wave's part landed; slot (tile-1) % STAGES is free
-    if (tile + STAGES - 1 < t_end) issue_tile(tile + STAGES - 1);
+  if (t_begin + STAGES - 1 < t_end) issue(t_begin + STAGES - 1, false);
+
+  constexpr int NK = C::DMA_T_MIN, VS = STAGES - 2;
+  for (int tile = t_begin; tile < t_end; ++tile) {
+    const int later = min(STAGES - 1, t_end - 1 - tile);   // tiles issued after this one
+    // K(i): later K tiles, plus V(i) and min(S-2, later) more V tiles
+    if (later == 0) wait_vm<NK>();
+    else if (later == 1) wait_vm<(2 + (VS < 1 ? VS : 1)) * NK>();
+    else if (later == 2) wait_vm<(3 + (VS < 2 ? VS : 2)) * NK>();
+    else wait_vm<(4 + (VS < 3 ? VS : 3)) * NK>();
+    __builtin_amdgcn_s_barrier();  // K(tile) landed for every wave; P V of tile-1 done everywhere
+    if (tile + STAGES - 1 < t_end) issue(tile + STAGES - 1, true);
 
     const unsigned char* kl = lds + (tile % STAGES) * C::STAGE_BYTES;
     const unsigned char* vl = kl + C::TILE_BYTES;
-    if ((tile + 1) * TN > rows_total) {
-      // V rows past the cache were not loaded (the descriptor bounds the read)
-      // and hold stale bits; P is exactly 0 there, but 0 * NaN would poison O.
-      unsigned char* vw = lds + (tile % STAGES) * C::STAGE_BYTES + C::TILE_BYTES;
-      for (int ch = tid; ch < C::TILE_BYTES / 16; ch += C::NT)
-        if (tile * TN + ch / C::NCH >= rows_total) *reinterpret_cast<u32x4*>(vw + ch * 16) = u32x4{0u, 0u, 0u, 0u};
-      __syncthreads();
-    }
 
     // ---- S^T = K Q^T over this wave's 32 positions ----
     f32x4 s[TPW][2];
@@ -296,17 +299,27 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        if (!tile_on[t]) continue;
-        bf16x8 qv;
-        if constexpr (C::Q_LDS) {
-          const int r = (rg * TPW + t) * 16 + l16;
-          qv = *reinterpret_cast<const bf16x8*>(qlds + r * C::ROWB + (((4 * ks + kg) ^ (r & (C::NCH - 1))) << 4));
-        } else {
-          qv = qf[t][ks];
-        }
+        const int r = (rg * TPW + t) * 16 + l16;
+        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qlds + r * C::ROWB + (((4 * ks + kg) ^ (r & (C::NCH - 1))) << 4));
         s[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qv, s[t][0], 0, 0, 0);
         s[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qv, s[t][1], 0, 0, 0);
       }
+    }
+    // V(tile): later tiles of both tensors may stay in flight. After the
+    // barrier every wave's K reads of this tile are done: refill its K slot.
+    if (later == 0) wait_vm<0>();
+    else if (later == 1) wait_vm<2 * NK>();
+    else if (later == 2) wait_vm<4 * NK>();
+    else wait_vm<6 * NK>();
+    __builtin_amdgcn_s_barrier();
+    if (tile + STAGES < t_end) issue(tile + STAGES, false);
+    if ((tile + 1) * TN > rows_total) {
+      // V rows past the cache were not loaded (the descriptor bounds the read)
+      // and hold stale bits; P is exactly 0 there, but 0 * NaN would poison O.
+      unsigned char* vw = lds + (tile % STAGES) * C::STAGE_BYTES + C::TILE_BYTES;
+      for (int ch = tid; ch < C::TILE_BYTES / 16; ch += C::NT)
+        if (tile * TN + ch / C::NCH >= rows_total) *reinterpret_cast<u32x4*>(vw + ch * 16) = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
     }
 
     // ---- tree mask and tail (only tiles reaching past the context) ----
@@ -316,7 +329,8 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       const int a0 = tile * TN + 32 * pg + 4 * kg - n_ctx;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const uint64_t m = anc_row[t];
+        const int row = (rt0 + t) * 16 + l16;
+        const uint64_t m = reinterpret_cast<const uint64_t*>(alds)[row < M ? row % T : 0];
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
@@ -330,26 +344,36 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     }
 
     // ---- online softmax, P -> f16 B fragments ----
-    f16x8 pfrag[TPW];
+    // Row tiles past M hold zero queries and are computed like the others (their
+    // results are never stored), so the tile body has no per-tile branches and
+    // the scheduler can overlap one tile's exponentials with another's MFMAs.
+    float mx[TPW];
+    bool bump_any = false;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      if (!tile_on[t]) continue;
-      float mx = fmaxf(lane_max4(s[t][0][0], s[t][0][1], s[t][0][2], s[t][0][3]),
-                       lane_max4(s[t][1][0], s[t][1][1], s[t][1][2], s[t][1][3]));
-      mx = group4_max(mx);
-      // Lazy rescale: the reference max only moves when the tile max exceeds
-      // it by more than 2^8 in probability, so p = exp2(s*c - m*c) stays <= 256
-      // (exact enough in f16) and the O rescale is rare.
-      const bool bump = mx > m_thr[t];
-      if (__ballot(bump)) {
-        const float m_new = bump ? mx : m_run[t];
+      mx[t] = group4_max(fmaxf(lane_max4(s[t][0][0], s[t][0][1], s[t][0][2], s[t][0][3]),
+                               lane_max4(s[t][1][0], s[t][1][1], s[t][1][2], s[t][1][3])));
+      bump_any |= mx[t] > m_thr[t];
+    }
+    // Lazy rescale: the reference max only moves when the tile max exceeds it
+    // by more than 2^8 in probability, so p = exp2(s*c - m*c) stays <= 256
+    // (exact enough in f16) and the O rescale is rare.
+    if (__ballot(bump_any)) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const bool bump = mx[t] > m_thr[t];
+        const float m_new = bump ? mx[t] : m_run[t];
         const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
         m_run[t] = m_new;
-        m_thr[t] = m_new + lazy_raw;
+        m_thr[t] = bump ? m_new + lazy_raw : m_thr[t];
         lsum[t] *= alpha;
 #pragma unroll
         for (int ct = 0; ct < C::CT; ++ct) o[t][ct] *= alpha;
       }
+    }
+    f16x8 pfrag[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
       const float nmc = -m_run[t] * c;
       f16x8 f;
 #pragma unroll
@@ -378,7 +402,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
             f16x8, u32x4{bf16x2_to_f16x2(wb.x), bf16x2_to_f16x2(wb.y), bf16x2_to_f16x2(wb.z), bf16x2_to_f16x2(wb.w)});
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
-          if (tile_on[t]) o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfrag[t], o[t][ct], 0, 0, 0);
+          o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfrag[t], o[t][ct], 0, 0, 0);
       }
     }
   }
@@ -388,81 +412,82 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 #pragma unroll
   for (int t = 0; t < TPW; ++t) l_run[t] = lsum[t][0];
 
-  // ---- merge the PG position groups of each row group through LDS ----
-  if constexpr (PG > 1) {
-    constexpr int OSLOT = 64 * C::CT * 16;            // one wave's O^T fragments of one row tile
-    constexpr int SLOT = OSLOT + 2 * 16 * 4;          // + m and l of its 16 rows
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      __syncthreads();  // the ring (or the previous round) is free
-      if (pg > 0 && tile_on[t]) {
-        unsigned char* slot = lds + ((pg - 1) * RG + rg) * SLOT;
-#pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(slot + (ct * 64 + lane) * 16) = o[t][ct];
-        if (kg == 0) {
-          reinterpret_cast<float*>(slot + OSLOT)[l16] = m_run[t];
-          reinterpret_cast<float*>(slot + OSLOT)[16 + l16] = l_run[t];
-        }
-      }
-      __syncthreads();
-      if (pg == 0 && tile_on[t]) {
-        float mm = m_run[t];
-#pragma unroll
-        for (int q = 1; q < PG; ++q)
-          mm = fmaxf(mm, reinterpret_cast<const float*>(lds + ((q - 1) * RG + rg) * SLOT + OSLOT)[l16]);
-        const float mu = mm;  // finite: running maxima start at NEG_BIG
-        const float w0 = __builtin_amdgcn_exp2f((m_run[t] - mu) * c);
-        float ll = l_run[t] * w0;
-#pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) o[t][ct] *= w0;
-#pragma unroll
-        for (int q = 1; q < PG; ++q) {
-          const unsigned char* slot = lds + ((q - 1) * RG + rg) * SLOT;
-          const float mq = reinterpret_cast<const float*>(slot + OSLOT)[l16];
-          const float wq = __builtin_amdgcn_exp2f((mq - mu) * c);
-          ll += wq * reinterpret_cast<const float*>(slot + OSLOT)[16 + l16];
-#pragma unroll
-          for (int ct = 0; ct < C::CT; ++ct) o[t][ct] += wq * *reinterpret_cast<const f32x4*>(slot + (ct * 64 + lane) * 16);
-        }
-        m_run[t] = mm;
-        l_run[t] = ll;
-      }
-    }
-  }
-
-  // ---- epilogue: normalise (single split) or write partials ----
-  if (pg != 0) return;
+  // ---- merge the PG position groups of each row group, then store ----
+  // Every wave parks its O^T fragments and (m, l) of row tile t in LDS; wave
+  // (rg, pg) then merges channel tiles pg, pg + PG, ... of its row group over
+  // the PG slots and stores them: all waves share the merge and the stores.
+  // Output: normalised rows (single split) or the split's partial (O^T, m, l).
+  constexpr int CTW = C::CT / PG;   // channel tiles merged and stored per wave
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    if (!tile_on[t]) continue;
+    float mu = m_run[t], wsum = l_run[t];
+    f32x4 om[CTW];
+    if constexpr (PG > 1) {
+      __syncthreads();  // the ring (or the previous round) is free
+      unsigned char* my = lds + (rg * PG + pg) * C::MSLOT;
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(my + (ct * 64 + lane) * 16) = o[t][ct];
+      if (kg == 0) {
+        reinterpret_cast<float*>(my + 64 * C::CT * 16)[l16] = m_run[t];
+        reinterpret_cast<float*>(my + 64 * C::CT * 16)[16 + l16] = l_run[t];
+      }
+      __syncthreads();
+      const unsigned char* grp = lds + rg * PG * C::MSLOT;
+      float mq[PG], wq[PG];
+      mu = NEG_BIG;
+#pragma unroll
+      for (int q = 0; q < PG; ++q) {
+        mq[q] = reinterpret_cast<const float*>(grp + q * C::MSLOT + 64 * C::CT * 16)[l16];
+        mu = fmaxf(mu, mq[q]);
+      }
+      wsum = 0.f;
+#pragma unroll
+      for (int q = 0; q < PG; ++q) {
+        wq[q] = __builtin_amdgcn_exp2f((mq[q] - mu) * c);
+        wsum += wq[q] * reinterpret_cast<const float*>(grp + q * C::MSLOT + 64 * C::CT * 16)[16 + l16];
+      }
+#pragma unroll
+      for (int i = 0; i < CTW; ++i) {
+        const int ct = pg + i * PG;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < PG; ++q) acc += wq[q] * *reinterpret_cast<const f32x4*>(grp + q * C::MSLOT + (ct * 64 + lane) * 16);
+        om[i] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CTW; ++i) om[i] = o[t][i];
+    }
     const int row = (rt0 + t) * 16 + l16;
-    if (row >= M) continue;
+    if (!tile_on[t] || row >= M) continue;
     if (p.n_split == 1) {
-      const float inv = 1.0f / l_run[t];
+      const float inv = 1.0f / wsum;
       float* dst = p.out + ((int64_t)g * M + row) * D + 4 * kg;
 #pragma unroll
-      for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(dst + ct * 16) = o[t][ct] * inv;
+      for (int i = 0; i < CTW; ++i) *reinterpret_cast<f32x4*>(dst + (pg + i * PG) * 16) = om[i] * inv;
     } else {
       const int64_t prow = ((int64_t)split * p.Hkv + g) * M + row;
       float* dst = p.part_acc + prow * D + 4 * kg;
 #pragma unroll
-      for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(dst + ct * 16) = o[t][ct];
-      if (kg == 0) {
-        p.part_ml[prow * 2 + 0] = m_run[t];
-        p.part_ml[prow * 2 + 1] = l_run[t];
+      for (int i = 0; i < CTW; ++i) *reinterpret_cast<f32x4*>(dst + (pg + i * PG) * 16) = om[i];
+      if (pg == 0 && kg == 0) {
+        p.part_ml[prow * 2 + 0] = mu;
+        p.part_ml[prow * 2 + 1] = wsum;
       }
     }
   }
 }
 
 // Log-sum-exp merge of the split partials. One row per block for d=128 (two
-// for d=64): 8 split groups x D/4 float4 lanes, so the per-split loads of a
-// row are issued in parallel; two LDS reductions finish the merge.
+// for d=64): 8 split groups x D/4 float4 lanes. Each thread merges its splits
+// in one pass (U splits' loads issued together, online max), then one LDS
+// round merges the 8 split groups in a fixed order (bitwise repeatable).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int CG = D / 4;                 // float4 channel groups per row
-  constexpr int RPB = 256 / (CG * 8);       // rows per block
   constexpr int SG = 8;                     // split groups
+  constexpr int RPB = 256 / (CG * SG);      // rows per block
+  constexpr int U = 4;                      // splits in flight per thread
   __shared__ float red_m[RPB][SG];
   __shared__ float red_l[RPB][SG];
   __shared__ f32x4 red_acc[RPB][SG][CG];
@@ -476,35 +501,55 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   const float c = p.scale_log2e;
   const int64_t sstride = nrows;
 
-  float mm = -INFINITY;
+  // Partial maxima are finite (running maxima start at a finite floor); -inf
+  // marks "no split here" and gets weight exp2(-inf) = 0.
+  float m_loc = -INFINITY, l_loc = 0.f;
+  f32x4 a_loc = {0.f, 0.f, 0.f, 0.f};
   if (ok)
-    for (int s = sg; s < p.n_split; s += SG) mm = fmaxf(mm, p.part_ml[(s * sstride + row) * 2]);
-  if (c4 == 0) red_m[r_in][sg] = mm;
-  __syncthreads();
-  float M = red_m[r_in][0];
+    for (int s0 = sg; s0 < p.n_split; s0 += SG * U) {
+      float mv[U], lv[U];
+      f32x4 av[U];
 #pragma unroll
-  for (int q = 1; q < SG; ++q) M = fmaxf(M, red_m[r_in][q]);
-  const float mu = (M == -INFINITY) ? 0.f : M;
-
-  float L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (ok)
-    for (int s = sg; s < p.n_split; s += SG) {
-      const int64_t pr = s * sstride + row;
-      const float w = __builtin_amdgcn_exp2f((p.part_ml[pr * 2] - mu) * c);
-      L += w * p.part_ml[pr * 2 + 1];
-      acc += w * *reinterpret_cast<const f32x4*>(p.part_acc + pr * D + 4 * c4);
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u * SG;
+        const bool in = s < p.n_split;
+        const int64_t pr = (int64_t)(in ? s : s0) * sstride + row;
+        const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + pr * 2);
+        mv[u] = in ? ml.x : -INFINITY;
+        lv[u] = in ? ml.y : 0.f;
+        av[u] = *reinterpret_cast<const f32x4*>(p.part_acc + pr * D + 4 * c4);
+      }
+      float mn = m_loc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mn = fmaxf(mn, mv[u]);
+      const float sc = __builtin_amdgcn_exp2f((m_loc - mn) * c);   // 0 on the first round
+      l_loc *= sc;
+      a_loc *= sc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = __builtin_amdgcn_exp2f((mv[u] - mn) * c);
+        l_loc += w * lv[u];
+        a_loc += w * av[u];
+      }
+      m_loc = mn;
     }
-  red_acc[r_in][sg][c4] = acc;
-  if (c4 == 0) red_l[r_in][sg] = L;
+  red_acc[r_in][sg][c4] = a_loc;
+  if (c4 == 0) {
+    red_m[r_in][sg] = m_loc;
+    red_l[r_in][sg] = l_loc;
+  }
   __syncthreads();
   if (sg == 0 && ok) {
-    f32x4 a = red_acc[r_in][0][c4];
-    float l = red_l[r_in][0];
+    float mu = red_m[r_in][0];
 #pragma unroll
-    for (int q = 1; q < SG; ++q) {
-      a += red_acc[r_in][q][c4];
-      l += red_l[r_in][q];
+    for (int q = 1; q < SG; ++q) mu = fmaxf(mu, red_m[r_in][q]);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+#pragma unroll
+    for (int q = 0; q < SG; ++q) {
+      const float w = __builtin_amdgcn_exp2f((red_m[r_in][q] - mu) * c);
+      a += w * red_acc[r_in][q][c4];
+      l += w * red_l[r_in][q];
     }
     *reinterpret_cast<f32x4*>(p.out + (int64_t)row * D + 4 * c4) = a * (1.0f / l);
   }
