@@ -131,6 +131,13 @@ __device__ inline void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
 }
 
+// Workgroup barrier that orders LDS accesses only (no wait for global stores).
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ inline unsigned int lds_offset(const void* p) {
   return (unsigned int)(uintptr_t)(const LDS_AS void*)p;
 }
@@ -423,7 +430,9 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     float mu = m_run[t], wsum = l_run[t];
     f32x4 om[CTW];
     if constexpr (PG > 1) {
-      __syncthreads();  // the ring (or the previous round) is free
+      // LDS-only barriers: the partial stores of the previous round may stay
+      // in flight (__syncthreads would wait for them).
+      lds_barrier();  // the ring (or the previous round) is free
       unsigned char* my = lds + (rg * PG + pg) * C::MSLOT;
 #pragma unroll
       for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(my + (ct * 64 + lane) * 16) = o[t][ct];
@@ -431,7 +440,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         reinterpret_cast<float*>(my + 64 * C::CT * 16)[l16] = m_run[t];
         reinterpret_cast<float*>(my + 64 * C::CT * 16)[16 + l16] = l_run[t];
       }
-      __syncthreads();
+      lds_barrier();
       const unsigned char* grp = lds + rg * PG * C::MSLOT;
       float mq[PG], wq[PG];
       mu = NEG_BIG;
