@@ -9,19 +9,21 @@
 // sink U selected U recent.
 //
 // Kernels (one stream, in order):
-//   1. prologue  grid Hkv:  qbar_g in fp32, clear the per-head histogram.
+//   1. prologue  grid Hkv:  qbar_g in fp32; clear the head's histogram.
 //   2. score     grid (chunks, Hkv): one HBM pass over K. 16 lanes x 16 B per
 //                row (d=128), lane-local FMAs then a 16-lane reduction; the
 //                block also histograms the top 12 bits of each candidate's
 //                order-preserving key and adds its non-empty bins to the
 //                head's global histogram.
-//   3. select    grid Hkv, 1024 threads: the top-12-bit bin holding the B'-th
-//                key comes from the histogram; two more radix passes (10 + 10
-//                bits) over the L2-resident scores fix the exact cut key;
-//                a block-wide ordered scan then emits the rows above the cut
-//                plus the earliest ties, ascending.
-//   4. gather    grid (row chunks, Hkv): copy sink, selected and recent rows of
-//                K and V into the partial cache.
+//   3. cutbin    grid (nb, Hkv): every block finds the top-12-bit bin holding
+//                the B'-th key, lists its chunk's keys in that bin and counts
+//                its keys in higher bins.
+//   4. emit      grid (nb, Hkv): every block refines the lists to the exact
+//                cut (two more radix digits), counts the rows taken by earlier
+//                blocks, writes its selected rows in ascending order and
+//                copies their K and V rows into the partial cache; block 0
+//                also copies the sink and recent rows.
+// Passes 3 and 4 read the L2-resident scores, not K.
 #include "ts_internal.h"
 
 #include <cmath>
@@ -33,8 +35,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int HIST1_BITS = 12;
 constexpr int HIST1 = 1 << HIST1_BITS;  // bins of the first radix digit
-constexpr int SEL_THREADS = 1024;
-
 // Order-preserving map from float to uint32 (larger float -> larger key).
 __device__ inline unsigned int f2key(float f) {
   const unsigned int u = __float_as_uint(f);
@@ -64,12 +64,21 @@ __global__ __launch_bounds__(256) void select_prologue_kernel(const SelectParams
   const int rows = (p.Hq / p.Hkv) * p.T;
   const uint16_t* qg = p.q + (int64_t)g * rows * D + cg * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = rs; r < rows; r += RS) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(qg + (int64_t)r * D);
-    acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
-    acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
-    acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
-    acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
+  constexpr int QB = 8;   // rows whose loads are in flight together
+  for (int r0 = rs; r0 < rows; r0 += RS * QB) {
+    u32x4 w[QB];
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+      const int r = r0 + u * RS;
+      w[u] = r < rows ? *reinterpret_cast<const u32x4*>(qg + (int64_t)r * D) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+      acc[0] += bf16_lo(w[u].x); acc[1] += bf16_hi(w[u].x);
+      acc[2] += bf16_lo(w[u].y); acc[3] += bf16_hi(w[u].y);
+      acc[4] += bf16_lo(w[u].z); acc[5] += bf16_hi(w[u].z);
+      acc[6] += bf16_lo(w[u].w); acc[7] += bf16_hi(w[u].w);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[rs][cg * 8 + e] = acc[e];
@@ -142,8 +151,41 @@ __global__ __launch_bounds__(256) void select_score_kernel(const SelectParams p,
   }
 }
 
-// Block-wide exclusive scan over SEL_THREADS threads; returns the prefix and
-// the total. `tmp` holds one slot per wave.
+// Workspace after the scores and qbar (all 256-byte aligned):
+//   hist   [Hkv][HIST1]     first-digit histogram (filled by the scoring pass)
+//   ccnt   [Hkv][NB_MAX][2] per block: cut-bin keys collected, keys in higher bins
+//   cand   [Hkv][n_ctx]     the cut-bin keys, block b's at its chunk's rows
+constexpr int NB_MAX = 64;   // blocks per head in the parallel passes
+constexpr int PT = 256;      // threads per block of the parallel passes
+
+__host__ __device__ inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct SelWs {
+  unsigned int* hist;
+  unsigned int* ccnt;
+  unsigned int* cand;
+};
+
+__host__ __device__ inline SelWs carve(int32_t* base, int Hkv, int n_ctx) {
+  char* w = reinterpret_cast<char*>(base);
+  SelWs s;
+  s.hist = reinterpret_cast<unsigned int*>(w);
+  w += round256((size_t)Hkv * HIST1 * 4);
+  s.ccnt = reinterpret_cast<unsigned int*>(w);
+  w += round256((size_t)Hkv * NB_MAX * 2 * 4);
+  s.cand = reinterpret_cast<unsigned int*>(w);
+  (void)n_ctx;
+  return s;
+}
+
+size_t sel_ws_bytes(int Hkv, int n_ctx) {
+  return round256((size_t)Hkv * HIST1 * 4) + round256((size_t)Hkv * NB_MAX * 2 * 4) +
+         round256((size_t)Hkv * (n_ctx > 0 ? n_ctx : 1) * 4);
+}
+
+// Block-wide exclusive scan over NT threads; returns the prefix and the total.
+// `tmp` holds one slot per wave.
+template <int NT>
 __device__ inline unsigned int block_exclusive_scan(unsigned int x, unsigned int* tmp, unsigned int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -156,7 +198,8 @@ __device__ inline unsigned int block_exclusive_scan(unsigned int x, unsigned int
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
   unsigned int wave_prefix = 0, tot = 0;
-  for (int w = 0; w < SEL_THREADS / 64; ++w) {
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
     const unsigned int t = tmp[w];
     if (w < wave) wave_prefix += t;
     tot += t;
@@ -168,16 +211,16 @@ __device__ inline unsigned int block_exclusive_scan(unsigned int x, unsigned int
 
 // Find, scanning bins from the top, the bin holding the k-th largest key
 // (k >= 1). hist has nbins entries in LDS; sets *bin and *above (the count in
-// higher bins). Each thread owns nbins / SEL_THREADS consecutive bins.
+// higher bins). Each thread owns nbins / NT consecutive bins.
+template <int NT>
 __device__ inline void find_bin(const unsigned int* hist, int nbins, unsigned int k, unsigned int* tmp, int* bin_out,
                                 unsigned int* above_out) {
-  const int per = nbins / SEL_THREADS;
-  // thread t covers the t-th group of bins counted from the top
-  const int hi_bin = nbins - 1 - threadIdx.x * per;
+  const int per = nbins / NT;
+  const int hi_bin = nbins - 1 - threadIdx.x * per;   // thread t covers the t-th group from the top
   unsigned int s = 0;
   for (int i = 0; i < per; ++i) s += hist[hi_bin - i];
   unsigned int total;
-  const unsigned int before = block_exclusive_scan(s, tmp, &total);
+  const unsigned int before = block_exclusive_scan<NT>(s, tmp, &total);
   if (before < k && k <= before + s) {
     unsigned int acc = before;
     for (int i = 0; i < per; ++i) {
@@ -193,199 +236,337 @@ __device__ inline void find_bin(const unsigned int* hist, int nbins, unsigned in
   __syncthreads();
 }
 
-constexpr int CAND_CAP = 16384;  // candidate keys of the cut bin held in LDS
-constexpr int UNR = 32;          // wave steps whose loads are in flight together (~128 KB per CU)
+// Candidate rows [lo, hi) are cut into NB chunks of `chunk` rows (a multiple
+// of 64); block b of a head owns chunk b.
+__device__ inline void chunk_of(const SelectParams& p, int nb, int b, int* c0, int* c1) {
+  const int n = p.cand_hi - p.cand_lo;
+  const int chunk = ((n + nb - 1) / nb + 63) / 64 * 64;
+  *c0 = min(p.cand_lo + b * chunk, p.cand_hi);
+  *c1 = min(*c0 + chunk, p.cand_hi);
+}
 
-// Ordered pass of one wave over rows [s0, s1), 64 rows per step in ascending
-// order, UNR steps' loads in flight; f(j, valid, key) is called by all lanes.
-template <typename F>
-__device__ inline void wave_pass_keys(const float* sc, int s0, int s1, F&& f) {
-  const int lane = threadIdx.x & 63;
-  for (int b0 = s0; b0 < s1; b0 += UNR * 64) {
-    float v[UNR];
+constexpr int RPT = 16;        // consecutive rows per thread in one sub-chunk of a parallel pass
+constexpr int SUB = PT * RPT;  // rows per sub-chunk
+
+// hist (HIST1 u32 in LDS) <- src, with every thread's 16-byte loads issued together.
+template <int NT>
+__device__ inline void load_hist(unsigned int* hist, const unsigned int* src) {
+  constexpr int PER = HIST1 / 4 / NT;
+  u32x4 v[PER];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int j = b0 + u * 64 + lane;
-      v[u] = j < s1 ? sc[j] : 0.f;
-    }
+  for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const u32x4*>(src)[threadIdx.x + i * NT];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int j = b0 + u * 64 + lane;
-      if (b0 + u * 64 < s1) f(j, j < s1, f2key(v[u]));
+  for (int i = 0; i < PER; ++i) reinterpret_cast<u32x4*>(hist)[threadIdx.x + i * NT] = v[i];
+}
+
+// Keys of rows j0 .. j0+RPT-1 (rows at or past c1 read as key 0 and are invalid).
+__device__ inline void load_keys(const float* sc, int j0, int c1, unsigned int (&key)[RPT]) {
+  float v[RPT];
+#pragma unroll
+  for (int e = 0; e < RPT; ++e) v[e] = j0 + e < c1 ? sc[j0 + e] : 0.f;
+#pragma unroll
+  for (int e = 0; e < RPT; ++e) key[e] = f2key(v[e]);
+}
+
+// Pass 1 of the selection: the first-digit bin holding the B'-th key (from the
+// scoring histogram; every block finds the same one) and the collection of
+// that bin's keys of the block's chunk into cand[g] at the chunk's own rows
+// (unordered: they are only counted later). The slots come from an LDS
+// counter, so no global atomic is contended.
+__global__ __launch_bounds__(PT) void select_cutbin_kernel(const SelectParams p, int nb) {
+  __shared__ __attribute__((aligned(16))) unsigned int hist[HIST1];
+  __shared__ unsigned int tmp[PT / 64];
+  __shared__ int s_bin;
+  __shared__ unsigned int s_above, s_n, s_hi;
+  const int g = blockIdx.y;
+  const unsigned int k = (unsigned int)p.b_eff;
+  if (k == 0) return;
+  const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
+  const int tid = threadIdx.x, lane = tid & 63;
+  int c0, c1;
+  chunk_of(p, nb, blockIdx.x, &c0, &c1);
+  const float* sc = p.scores + (int64_t)g * p.n_ctx;
+  unsigned int* cand = ws.cand + (int64_t)g * p.n_ctx + c0;
+  // the first sub-chunk's keys are loaded together with the histogram
+  unsigned int key[RPT];
+  load_keys(sc, c0 + RPT * tid, c1, key);
+  load_hist<PT>(hist, ws.hist + g * HIST1);
+  if (tid == 0) s_n = s_hi = 0;
+  __syncthreads();
+  find_bin<PT>(hist, HIST1, k, tmp, &s_bin, &s_above);
+  const unsigned int bin = (unsigned int)s_bin;
+  unsigned int n_hi = 0;   // this thread's keys in higher first-digit bins
+  for (int s0 = c0; s0 < c1; s0 += SUB) {
+    const int j0 = s0 + RPT * tid;
+    if (s0 != c0) load_keys(sc, j0, c1, key);
+    unsigned int nc = 0;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      const unsigned int kb = key[e] >> (32 - HIST1_BITS);
+      nc += j0 + e < c1 && kb == bin;
+      n_hi += j0 + e < c1 && kb > bin;
     }
+    // in-wave exclusive prefix of the list lengths; one LDS atomic per wave
+    unsigned int incl = nc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    unsigned int base = 0;
+    if (lane == 63 && incl) base = atomicAdd(&s_n, incl);
+    base = __shfl(base, 63) + incl - nc;
+    if (nc) {
+#pragma unroll
+      for (int e = 0; e < RPT; ++e)
+        if (j0 + e < c1 && (key[e] >> (32 - HIST1_BITS)) == bin) cand[base++] = key[e];
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) n_hi += __shfl_xor(n_hi, m);
+  if (lane == 0) atomicAdd(&s_hi, n_hi);
+  __syncthreads();
+  if (tid == 0) {
+    ws.ccnt[(g * NB_MAX + blockIdx.x) * 2 + 0] = s_n;
+    ws.ccnt[(g * NB_MAX + blockIdx.x) * 2 + 1] = s_hi;
   }
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_topb_kernel(const SelectParams p, const unsigned int* ghist) {
-  __shared__ unsigned int hist[HIST1];
-  __shared__ unsigned int cand[CAND_CAP];
-  __shared__ unsigned int tmp[SEL_THREADS / 64];
-  __shared__ unsigned int wave_gt[SEL_THREADS / 64], wave_tie[SEL_THREADS / 64];
-  __shared__ int s_bin;
-  __shared__ unsigned int s_above, s_ncand;
-  const int g = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  int32_t* out = p.sel_idx + (int64_t)g * p.budget;
-  const unsigned int k = (unsigned int)p.b_eff;
-  for (int i = k + tid; i < p.budget; i += SEL_THREADS) out[i] = -1;
-  if (k == 0) return;
-  const float* sc = p.scores + (int64_t)g * p.n_ctx;
-  const int lo = p.cand_lo, hi = p.cand_hi;
+constexpr int CAND_CAP = 8192;   // cut-bin keys refined in LDS (more are refined from L2)
 
-  // digit 1 (top 12 key bits): the histogram built by the scoring kernel
-  for (int b = tid; b < HIST1; b += SEL_THREADS) hist[b] = ghist[g * HIST1 + b];
-  if (tid == 0) s_ncand = 0;
-  __syncthreads();
-  find_bin(hist, HIST1, k, tmp, &s_bin, &s_above);
-  unsigned int prefix = (unsigned int)s_bin;
-  unsigned int rank = k - s_above;  // rank of the cut key inside the bin, from the top
-  int shift = 32 - HIST1_BITS;
-  const unsigned int bin_count = hist[prefix];
-  const bool in_lds = bin_count <= (unsigned int)CAND_CAP;
-
-  // every wave owns a contiguous segment of candidate rows
-  constexpr int NWV = SEL_THREADS / 64;
-  const int n = hi - lo;
-  const int seg = ((n + NWV - 1) / NWV + 63) / 64 * 64;
-  const int s0 = min(lo + wave * seg, hi);
-  const int s1 = min(s0 + seg, hi);
-
-  // gather the cut bin's keys into LDS (order irrelevant: only counted); one
-  // LDS atomic per wave step (ballot + in-wave rank)
-  if (in_lds) {
-    wave_pass_keys(sc, s0, s1, [&](int, bool valid, unsigned int key) {
-      const bool take = valid && (key >> shift) == prefix;
-      const unsigned long long m = __ballot(take);
-      if (m) {
-        const int leader = __ffsll((long long)m) - 1;
-        unsigned int base = 0;
-        if (lane == leader) base = atomicAdd(&s_ncand, (unsigned int)__popcll(m));
-        base = __shfl(base, leader);
-        if (take) cand[base + popc64(m & lanemask_lt())] = key;
-      }
-    });
-    __syncthreads();
-  }
-
-  // digits 2 and 3 (10 bits each) over the keys matching the prefix
-  for (int pass = 0; pass < 2; ++pass) {
-    const int nbits = 10;
-    const int nb = 1 << nbits;
-    __syncthreads();
-    for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0u;
-    __syncthreads();
-    const int new_shift = shift - nbits;
-    if (in_lds) {
-      const unsigned int n = s_ncand;
-      for (unsigned int i = tid; i < n; i += SEL_THREADS) {
-        const unsigned int key = cand[i];
-        if ((key >> shift) == prefix) atomicAdd(&hist[(key >> new_shift) & (nb - 1)], 1u);
-      }
-    } else {
-      for (int j = lo + tid; j < hi; j += SEL_THREADS) {
-        const unsigned int key = f2key(sc[j]);
-        if ((key >> shift) == prefix) atomicAdd(&hist[(key >> new_shift) & (nb - 1)], 1u);
+// Copy rows of K and V of head g into the partial cache: item i of `n` is
+// 16-byte chunk i % RCH of pair i / RCH, pairs (src, dst) given by `pair`.
+// CP copies per thread are in flight together (loads first, then stores).
+template <int D, typename F>
+__device__ inline void copy_rows(const SelectParams& p, int g, int n, F&& pair) {
+  constexpr int NCH = D / 8, RCH = 2 * NCH, CP = 16;
+  for (int base = threadIdx.x; base < n * RCH; base += PT * CP) {
+    u32x4 val[CP];
+    uint16_t* dst[CP];
+#pragma unroll
+    for (int u = 0; u < CP; ++u) {
+      const int id = base + u * PT;
+      dst[u] = nullptr;
+      if (id < n * RCH) {
+        int src_row, dst_row;
+        pair(id / RCH, &src_row, &dst_row);
+        const int c = id % RCH;
+        const bool is_v = c >= NCH;
+        const int ch = is_v ? c - NCH : c;
+        const uint16_t* s = (is_v ? p.v : p.k) + (int64_t)g * p.s_head + (int64_t)src_row * p.s_pos + ch * 8;
+        dst[u] = (is_v ? p.v_part : p.k_part) + (int64_t)g * p.sp_head + (int64_t)dst_row * p.sp_pos + ch * 8;
+        val[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s));
       }
     }
+#pragma unroll
+    for (int u = 0; u < CP; ++u)
+      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
+  }
+}
+
+// Pass 2: exact cut, ordered emission and gather; grid (nb, Hkv).
+// Every block of a head derives the same cut: the first-digit bin of the
+// B'-th key from the histogram, then two more radix digits (10 + 10 bits)
+// over the lists of that bin's keys (blocks' lists back to back, in LDS when
+// they fit) give the exact cut key and how many keys equal to it are taken
+// (the earliest rows). The rows above the cut and at the cut in earlier
+// blocks follow from those blocks' higher-bin counts and lists. Inside its
+// chunk, sub-chunks of SUB rows are ranked by one block scan (rows above and
+// at the cut, packed 16 + 16 bits), so selected rows come out ascending with
+// consecutive output slots; the block copies their K and V rows into the
+// partial cache. Block 0 also copies the sink and recent rows and pads
+// sel_idx with -1.
+template <int D>
+__global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, int nb) {
+  __shared__ __attribute__((aligned(16))) unsigned int hist[HIST1];
+  __shared__ unsigned int cand_l[CAND_CAP];
+  __shared__ int srcs[SUB];
+  __shared__ unsigned int tmp[PT / 64];
+  __shared__ unsigned int seg_off[NB_MAX + 1], seg_c0[NB_MAX], seg_hi[NB_MAX];
+  __shared__ int s_bin;
+  __shared__ unsigned int s_above, s_gt, s_tie;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int k = p.b_eff;
+  const int n_sink_eff = min(p.n_sink, p.n_ctx);
+  int32_t* out = p.sel_idx + (int64_t)g * p.budget;
+  if (blockIdx.x == 0) {
+    for (int i = k + tid; i < p.budget; i += PT) out[i] = -1;
+    const int rec_lo = max(p.n_sink, p.n_ctx - p.n_recent);
+    const int n_rec = p.n_ctx - rec_lo > 0 ? p.n_ctx - rec_lo : 0;
+    copy_rows<D>(p, g, n_sink_eff + n_rec, [&](int r, int* src, int* dst) {
+      *src = r < n_sink_eff ? r : rec_lo + (r - n_sink_eff);
+      *dst = r < n_sink_eff ? r : n_sink_eff + k + (r - n_sink_eff);
+    });
+  }
+  if (k == 0) return;
+  const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
+  int c0, c1;
+  chunk_of(p, nb, blockIdx.x, &c0, &c1);
+  const float* sc = p.scores + (int64_t)g * p.n_ctx;
+  unsigned int key[RPT];
+  load_keys(sc, c0 + RPT * tid, c1, key);   // in flight with the loads below
+  load_hist<PT>(hist, ws.hist + g * HIST1);
+  if (tid < 64) {   // list offsets: one wave scans the per-block list lengths
+    unsigned int c = 0;
+    if (lane < nb) {
+      int b0, b1;
+      chunk_of(p, nb, lane, &b0, &b1);
+      seg_c0[lane] = (unsigned int)b0;
+      c = ws.ccnt[(g * NB_MAX + lane) * 2 + 0];
+      seg_hi[lane] = ws.ccnt[(g * NB_MAX + lane) * 2 + 1];
+    }
+    unsigned int incl = c;
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane < nb) seg_off[lane] = incl - c;
+    if (lane == 63) seg_off[nb] = incl;
+    if (lane == 0) s_gt = s_tie = 0;
+  }
+  __syncthreads();
+  const unsigned int n = seg_off[nb];
+  const unsigned int* cand_g = ws.cand + (int64_t)g * p.n_ctx;
+  auto seg_of = [&](unsigned int i) {   // list owning key i: the last b with seg_off[b] <= i
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto key_at = [&](unsigned int i) {
+    const int b = seg_of(i);
+    return cand_g[seg_c0[b] + (i - seg_off[b])];
+  };
+  const bool in_lds = n <= (unsigned int)CAND_CAP;
+  if (in_lds) {
+    constexpr int BATCH = 8;
+    for (unsigned int i0 = tid; i0 < n; i0 += PT * BATCH) {
+      unsigned int v[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const unsigned int i = i0 + u * PT;
+        v[u] = i < n ? key_at(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        if (i0 + u * PT < n) cand_l[i0 + u * PT] = v[u];
+    }
+  }
+  __syncthreads();
+  find_bin<PT>(hist, HIST1, (unsigned int)k, tmp, &s_bin, &s_above);
+  unsigned int prefix = (unsigned int)s_bin;
+  unsigned int rank = (unsigned int)k - s_above;   // rank of the cut key inside the bin, from the top
+  int shift = 32 - HIST1_BITS;
+  for (int pass = 0; pass < 2; ++pass) {
+    constexpr int nbits = 10, nbins = 1 << nbits;
     __syncthreads();
-    find_bin(hist, nb, rank, tmp, &s_bin, &s_above);
+    for (int b = tid; b < nbins; b += PT) hist[b] = 0u;
+    __syncthreads();
+    const int new_shift = shift - nbits;
+    for (unsigned int i = tid; i < n; i += PT) {
+      const unsigned int kk = in_lds ? cand_l[i] : key_at(i);
+      if ((kk >> shift) == prefix) atomicAdd(&hist[(kk >> new_shift) & (nbins - 1)], 1u);
+    }
+    __syncthreads();
+    find_bin<PT>(hist, nbins, rank, tmp, &s_bin, &s_above);
     prefix = (prefix << nbits) | (unsigned int)s_bin;
     rank -= s_above;
     shift = new_shift;
   }
-  const unsigned int cut = prefix;        // exact key of the B'-th candidate
-  const unsigned int need_ties = rank;    // ties at the cut to take, earliest rows first
-
-  // ordered emission: each wave owns a contiguous segment of candidate rows;
-  // pass 1 counts, one scan over the waves gives each segment's offsets, pass 2
-  // writes in row order using ballots for the in-wave ranks.
-  unsigned int cgt = 0, ctie = 0;
-  wave_pass_keys(sc, s0, s1, [&](int, bool valid, unsigned int key) {
-    cgt += valid && key > cut;
-    ctie += valid && key == cut;
-  });
-  for (int m = 32; m >= 1; m >>= 1) {
-    cgt += __shfl_xor(cgt, m);
-    ctie += __shfl_xor(ctie, m);
-  }
-  if (lane == 0) {
-    wave_gt[wave] = cgt;
-    wave_tie[wave] = ctie;
-  }
-  __syncthreads();
-  unsigned int gt_run = 0, tie_run = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_run += wave_gt[w];
-    tie_run += wave_tie[w];
-  }
-  wave_pass_keys(sc, s0, s1, [&](int j, bool valid, unsigned int key) {
-    const bool gt = valid && key > cut;
-    const bool tie = valid && key == cut;
-    const unsigned long long tie_mask = __ballot(tie);
-    const unsigned int tie_rank = tie_run + popc64(tie_mask & lanemask_lt());
-    const bool take = gt || (tie && tie_rank < need_ties);
-    const unsigned long long gt_mask = __ballot(gt);
-    const unsigned int gt_before = gt_run + popc64(gt_mask & lanemask_lt());
-    if (take) {
-      const unsigned int idx = gt_before + min(tie_rank, need_ties);
-      if (idx < k) out[idx] = j;
+  const unsigned int cut = prefix, need = rank;
+  // rows above / at the cut in earlier blocks: their higher-bin counts plus
+  // their listed keys above / equal to the cut
+  {
+    unsigned int gt = 0, tie = 0;
+    const unsigned int n_before = seg_off[blockIdx.x];
+    for (unsigned int i = tid; i < n_before; i += PT) {
+      const unsigned int kk = in_lds ? cand_l[i] : key_at(i);
+      gt += kk > cut;
+      tie += kk == cut;
     }
-    gt_run += popc64(gt_mask);
-    tie_run += popc64(tie_mask);
-  });
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void select_gather_kernel(const SelectParams p, int rows_per_block) {
-  constexpr int NCH = D / 8;
-  __shared__ int src_row[256];
-  const int g = blockIdx.y;
-  const int n_sink_eff = min(p.n_sink, p.n_ctx);
-  const int rec_lo = max(p.n_sink, p.n_ctx - p.n_recent);
-  const int r0 = blockIdx.x * rows_per_block;
-  const int r1 = min(r0 + rows_per_block, p.n_part);
-  const int32_t* sel = p.sel_idx + (int64_t)g * p.budget;
-  if (threadIdx.x < r1 - r0) {
-    const int r = r0 + threadIdx.x;
-    int src;
-    if (r < n_sink_eff) src = r;
-    else if (r < n_sink_eff + p.b_eff) src = sel[r - n_sink_eff];
-    else src = rec_lo + (r - n_sink_eff - p.b_eff);
-    src_row[threadIdx.x] = min(max(src, 0), p.n_ctx - 1);  // the selection only emits rows in [0, n_ctx)
+    if (tid < (int)blockIdx.x) gt += seg_hi[tid];
+    for (int m = 32; m >= 1; m >>= 1) {
+      gt += __shfl_xor(gt, m);
+      tie += __shfl_xor(tie, m);
+    }
+    if (lane == 0) {
+      atomicAdd(&s_gt, gt);
+      atomicAdd(&s_tie, tie);
+    }
   }
   __syncthreads();
-  const int nchunks = (r1 - r0) * NCH * 2;
-  for (int id = threadIdx.x; id < nchunks; id += 256) {
-    const bool is_v = id >= (r1 - r0) * NCH;
-    const int cid = is_v ? id - (r1 - r0) * NCH : id;
-    const int rl = cid / NCH;
-    const int ch = cid % NCH;
-    const uint16_t* s = (is_v ? p.v : p.k) + (int64_t)g * p.s_head + (int64_t)src_row[rl] * p.s_pos + ch * 8;
-    uint16_t* d = (is_v ? p.v_part : p.k_part) + (int64_t)g * p.sp_head + (int64_t)(r0 + rl) * p.sp_pos + ch * 8;
-    *reinterpret_cast<u32x4*>(d) = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s));
+  unsigned int gt_run = s_gt, tie_run = s_tie;
+  for (int s0 = c0; s0 < c1; s0 += SUB) {
+    const int j0 = s0 + RPT * tid;
+    if (s0 != c0) load_keys(sc, j0, c1, key);
+    unsigned int ngt = 0, ntie = 0;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      const int j = j0 + e;
+      ngt += j < c1 && key[e] > cut;
+      ntie += j < c1 && key[e] == cut;
+    }
+    unsigned int tot;
+    const unsigned int pre = block_exclusive_scan<PT>(ngt | (ntie << 16), tmp, &tot);
+    const unsigned int base = gt_run + min(tie_run, need);   // output slot of this sub-chunk's first take
+    unsigned int gt_i = gt_run + (pre & 0xffffu), tie_i = tie_run + (pre >> 16);
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      const int j = j0 + e;
+      const bool gt = j < c1 && key[e] > cut;
+      const bool tie = j < c1 && key[e] == cut;
+      if (gt || (tie && tie_i < need)) {
+        const unsigned int idx = gt_i + min(tie_i, need);
+        if (idx < (unsigned int)k) {
+          out[idx] = j;
+          srcs[idx - base] = j;
+        }
+      }
+      gt_i += gt;
+      tie_i += tie;
+    }
+    gt_run += tot & 0xffffu;
+    tie_run += tot >> 16;
+    const unsigned int end = min(gt_run + min(tie_run, need), (unsigned int)k);
+    __syncthreads();
+    copy_rows<D>(p, g, (int)(end - base), [&](int i, int* src, int* dst) {
+      *src = srcs[i];
+      *dst = n_sink_eff + (int)base + i;
+    });
+    __syncthreads();
   }
 }
-
-size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
+
+int select_blocks_per_head(int32_t n_ctx, int32_t Hkv, int32_t n_sink, int32_t n_recent) {
+  const int lo = n_sink < n_ctx ? n_sink : n_ctx;
+  const int hi = n_ctx - n_recent > lo ? n_ctx - n_recent : lo;
+  const int n = hi - lo;
+  int nb = (256 + Hkv - 1) / Hkv;           // about one block per compute unit over all heads
+  const int by_rows = (n + 1023) / 1024;    // at least 1024 rows per block
+  if (nb > by_rows) nb = by_rows;
+  if (nb > NB_MAX) nb = NB_MAX;
+  if (nb < 1) nb = 1;
+  return nb;
+}
 
 size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t budget) {
   (void)T;
   (void)Hq;
   (void)budget;
   return round256((size_t)Hkv * n_ctx * sizeof(float)) + round256((size_t)Hkv * d * sizeof(float)) +
-         round256((size_t)Hkv * HIST1 * sizeof(unsigned int));
+         sel_ws_bytes(Hkv, n_ctx);
 }
 
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
-  unsigned int* hist = reinterpret_cast<unsigned int*>(p.sel_ws);
+  const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
   if (p.d == 128)
-    hipLaunchKernelGGL(select_prologue_kernel<128>, dim3(p.Hkv), dim3(256), 0, stream, p, hist);
+    hipLaunchKernelGGL(select_prologue_kernel<128>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist);
   else
-    hipLaunchKernelGGL(select_prologue_kernel<64>, dim3(p.Hkv), dim3(256), 0, stream, p, hist);
+    hipLaunchKernelGGL(select_prologue_kernel<64>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist);
   if (p.n_ctx > 0) {
     // ~1024 scoring blocks over all heads, at least 256 rows each
     int chunks = (1024 + p.Hkv - 1) / p.Hkv;
@@ -393,19 +574,18 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
     if (rpb < 256) rpb = 256;
     chunks = (p.n_ctx + rpb - 1) / rpb;
     if (p.d == 128)
-      hipLaunchKernelGGL(select_score_kernel<128>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, hist, rpb);
+      hipLaunchKernelGGL(select_score_kernel<128>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, ws.hist, rpb);
     else
-      hipLaunchKernelGGL(select_score_kernel<64>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, hist, rpb);
+      hipLaunchKernelGGL(select_score_kernel<64>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, ws.hist, rpb);
   }
-  hipLaunchKernelGGL(select_topb_kernel, dim3(p.Hkv), dim3(SEL_THREADS), 0, stream, p, hist);
-  if (p.n_part > 0) {
-    const int rpb = 32;
-    const int chunks = (p.n_part + rpb - 1) / rpb;
-    if (p.d == 128)
-      hipLaunchKernelGGL(select_gather_kernel<128>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, rpb);
-    else
-      hipLaunchKernelGGL(select_gather_kernel<64>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, rpb);
+  const int nb = select_blocks_per_head(p.n_ctx, p.Hkv, p.n_sink, p.n_recent);
+  if (p.b_eff > 0) {
+    hipLaunchKernelGGL(select_cutbin_kernel, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
   }
+  if (p.d == 128)
+    hipLaunchKernelGGL(select_emit_kernel<128>, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
+  else
+    hipLaunchKernelGGL(select_emit_kernel<64>, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
   return hipGetLastError();
 }
 

@@ -12,13 +12,13 @@ import torch
 
 import long_kv_attention_amd as ts
 from oracle import bf16_to_f64, draft_attention, partial_kv_select, verify_attention
-from synth import CONFIGS, attention_inputs, tree_parent
+from synth import CONFIGS, attention_inputs, bf16_round, tree_parent
 from tests.gpu_util import banner, dev_bf16, rel_max_err
 
 pytestmark = pytest.mark.gpu
 
 
-def _check(x, n_ctx, Hq, Hkv, n_sink, budget, n_recent, heads=None):
+def _check(x, n_ctx, Hq, Hkv, n_sink, budget, n_recent, heads=None, strict=False):
     q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
     sel, kp, vp, n_part, sc = ts.partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, want_scores=True)
     torch.cuda.synchronize()
@@ -41,6 +41,8 @@ def _check(x, n_ctx, Hq, Hkv, n_sink, budget, n_recent, heads=None):
         assert np.all(np.diff(gs) > 0)
         rs = ref.sel_idx[0][:b_eff]
         diff = np.setxor1d(gs, rs)
+        if strict:   # exactly equal scores: the row order decides, with no rounding band
+            assert len(diff) == 0, (g, diff[:10])
         if len(diff):
             cut = ref.cutoff[0]
             band = 1e-4 * max(abs(cut), 1.0)
@@ -76,6 +78,27 @@ def test_exact_ties_go_to_earlier_rows():
     x = attention_inputs(12, 8, 2, 128, n_ctx, 4)
     x["k"][:, 1500:1600] = x["k"][:, 100:200]    # 100 exact score ties per head
     _check(x, n_ctx, 8, 2, 4, 150, 64)
+
+
+@pytest.mark.parametrize("kind", ["top", "zero"])
+def test_massive_ties_span_blocks(kind):
+    """Tens of thousands of exactly equal scores at the cut: more cut-bin keys
+    than the in-LDS refinement holds, ties spread over many blocks, and the
+    earliest tied rows must be the ones taken."""
+    n_ctx, Hq, Hkv = 60_000, 8, 2
+    banner(f"select massive ties {kind}")
+    x = attention_inputs(21, Hq, Hkv, 128, n_ctx, 4)
+    G = Hq // Hkv
+    if kind == "top":
+        # rows 1000..44999 share one key whose score tops every random row
+        for g in range(Hkv):
+            qbar = bf16_to_f64(x["q"][g * G:(g + 1) * G]).sum(axis=(0, 1))
+            u = np.where(qbar >= 0, 3.0, -3.0).astype(np.float32)
+            x["k"][g, 1000:45000] = bf16_round(u)[None, :]
+        _check(x, n_ctx, Hq, Hkv, 4, 30_000, 64, strict=True)
+    else:
+        x["k"][:] = 0   # every score is exactly 0
+        _check(x, n_ctx, Hq, Hkv, 4, 5_000, 64, strict=True)
 
 
 def test_full_budget_draft_equals_verification():
