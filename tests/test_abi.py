@@ -54,7 +54,7 @@ def test_workspace_queries_depend_on_shapes_only():
     assert L.ts_verify_attn_workspace_size(100_000, 65, 32, 8, 128, 0) == 0   # unsupported -> 0
     assert L.ts_draft_attn_workspace_size(4164, 4, 32, 8, 128, 0) == L.ts_verify_attn_workspace_size(4164, 4, 32, 8, 128, 0)
     assert L.ts_partial_kv_select_workspace_size(100_000, 24, 32, 8, 128, 4096) >= 8 * 100_000 * 4
-    assert L.ts_penalty_sample_workspace_size(1, 128256) == 0
+    assert L.ts_penalty_sample_workspace_size(28, 128256) >= 28 * 128256 * 4   # per-row cut-bin lists
 
 
 def _verify(L, **kw):
@@ -123,7 +123,7 @@ def test_partial_kv_select_rejects(kw, code):
 
 def _penalty(L, **kw):
     a = dict(logits=FAKE, rows=2, V=1000, window=FAKE, W=16, wstride=16, penalty=1.2, temp=1.0, top_p=0.9,
-             min_p=0.05, out=FAKE, keep=FAKE, probs=FAKE, u=FAKE, token=FAKE, ws=None, ws_bytes=0)
+             min_p=0.05, out=FAKE, keep=FAKE, probs=FAKE, u=FAKE, token=FAKE, ws=FAKE, ws_bytes=1 << 40)
     a.update(kw)
     return L.ts_penalty_sample(a["logits"], a["rows"], a["V"], a["window"], a["W"], a["wstride"], a["penalty"],
                                a["temp"], a["top_p"], a["min_p"], a["out"], a["keep"], a["probs"], a["u"], a["token"],
@@ -135,6 +135,7 @@ def _penalty(L, **kw):
     (dict(W=-1), EINVAL), (dict(window=None), EINVAL), (dict(wstride=8), EINVAL), (dict(penalty=0.0), EINVAL),
     (dict(penalty=-1.2), EINVAL), (dict(temp=0.0), EINVAL), (dict(top_p=1.5), EINVAL), (dict(top_p=-0.1), EINVAL),
     (dict(min_p=float("nan")), EINVAL), (dict(u=None), EINVAL), (dict(out=FAKE_ODD), EINVAL),
+    (dict(ws_bytes=1024), EWORKSPACE), (dict(ws=None), EINVAL), (dict(ws=FAKE_ODD), EINVAL),
 ])
 def test_penalty_sample_rejects(kw, code):
     L = _lib()
