@@ -20,13 +20,13 @@ struct AttnParams {
   int32_t n_ctx, T, Hq, Hkv, d;
   int32_t M;             // rows per KV head = (Hq/Hkv) * T
   int32_t n_split;       // effective number of chunks per KV head
-  int32_t rows_per_split;  // cache rows per split (a multiple of 64)
+  int32_t rows_per_split;  // cache rows per split (a multiple of 128)
   float scale_log2e;     // softmax scale * log2(e)
   uint64_t anc[64];      // anc[i] bit a set <=> tree node a is i or an ancestor of i
 };
 
 // Automatic split count: a pure function of the shapes (so the workspace
-// query needs no device), aimed at ~2 resident workgroups per compute unit.
+// query needs no device), aimed at one resident workgroup per compute unit.
 int attn_auto_split(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d);
 // Effective split count and cache rows per split for a requested count.
 void attn_split_plan(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
@@ -52,7 +52,7 @@ struct SelectParams {
   int64_t sp_head, sp_pos;
   float* scores;              // [Hkv][n_ctx] (user buffer or workspace)
   float* qbar;                // [Hkv][d] workspace
-  int32_t* sel_ws;            // workspace: per-head key histogram of the scoring pass
+  int32_t* sel_ws;            // workspace of the selection passes (histograms, cut-bin lists)
 };
 size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
                               int32_t budget);
