@@ -82,19 +82,34 @@ constexpr float LAZY_LOG2 = 8.0f;
 // and give exp2(-inf) = 0; a row with any visible score moves the max).
 constexpr float NEG_BIG = -1.0e30f;
 
-__device__ inline float lane_max4(float a, float b, float c, float d) {
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+// max(a, b, c) in one v_max3_f32. Scores are finite or -inf (never NaN), so
+// the IEEE-mode quieting that fmaxf would add before every max is not needed.
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Lane-local max of the 8 scores a lane holds for one row.
+__device__ inline float lane_max8(const f32x4& x, const f32x4& y) {
+  return max3(max3(x[0], x[1], x[2]), max3(x[3], y[0], y[1]), max3(y[2], y[3], y[3]));
 }
 
 // Max over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
 // gfx950 row-swap permutes: VALU only, no LDS round trip. With both operands
 // holding x, permlane16_swap leaves rows (0,0,2,2) in one result and (1,1,3,3)
 // in the other; permlane32_swap does the same for the two halves.
+__device__ inline float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ inline float group4_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // bf16 pair (low, high halves of a 32-bit word) -> f16 pair. Exact for
@@ -366,8 +381,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     bool bump_any = false;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      mx[t] = group4_max(fmaxf(lane_max4(s[t][0][0], s[t][0][1], s[t][0][2], s[t][0][3]),
-                               lane_max4(s[t][1][0], s[t][1][1], s[t][1][2], s[t][1][3])));
+      mx[t] = group4_max(lane_max8(s[t][0], s[t][1]));
       bump_any |= mx[t] > m_thr[t];
     }
     // Lazy rescale: the reference max only moves when the tile max exceeds it
