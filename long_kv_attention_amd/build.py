@@ -29,11 +29,26 @@ FLAGS = [
 
 
 def _compile(src, obj):
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(HERE, src), "-o", obj]
+    # The resource-usage remarks report every kernel's scratch use: a kernel
+    # that spills to scratch fails the build (the attention kernels keep their
+    # LDS ring and accumulators in registers; a spill would also cost time).
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(HERE, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
-    return r.returncode, " ".join(cmd), err
+    lines = (r.stderr or "").splitlines()
+    spills, kernel = [], None
+    for l in lines:
+        if "Function Name:" in l:
+            kernel = l.split("Function Name:")[-1].split("[-Rpass")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in l and not l.rstrip().endswith(": 0") and "remark" in l:
+            size = l.split("ScratchSize [bytes/lane]:")[-1].split()[0]
+            if size != "0":
+                spills.append(f"{kernel}: {size} bytes/lane of scratch")
+    noise = ("is not a recognized feature for this target", "remark:", "[-Rpass-analysis")
+    err = "\n".join(l for l in lines if not any(n in l for n in noise))
+    rc = r.returncode
+    if not rc and spills:
+        rc, err = 1, err + "\nkernels using scratch (register spills):\n  " + "\n  ".join(spills)
+    return rc, " ".join(cmd), err
 
 
 def build(verbose=False, jobs=None):

@@ -66,6 +66,10 @@ struct Cfg {
   static constexpr int ROWS_PER_BLOCK = RG * TPW * 16;
   static constexpr int KV_BYTES = STAGES * STAGE_BYTES;
   static constexpr int Q_BYTES = ROWS_PER_BLOCK * ROWB;    // the block's query rows
+  // 8-wave shapes with few row tiles per wave keep their query fragments in
+  // registers after the first tile (fewer LDS reads per tile); the others
+  // read them from LDS each tile (registers are short).
+  static constexpr bool Q_REG = NW >= 8 && TPW <= 3;
   static constexpr int ANC_BYTES = 1024;  // ancestor words of the tree nodes (one full 64-lane copy)
   static constexpr int MSLOT = 64 * CT * 16 + 2 * 16 * 4;   // one wave's O^T of a row tile + m, l
   static constexpr int MERGE_BYTES = PG * RG * MSLOT;
@@ -143,9 +147,11 @@ __device__ inline void dma16(i32x4 desc, unsigned int off, unsigned int lds_off)
 // The same copy with the non-temporal cache policy, for the K/V stream that
 // is read once: measured on the LDS-copy ring over a 100K-row cache, it
 // streams at 6.8-7.0 TB/s instead of 5.8-6.1 TB/s with the default policy.
-__device__ inline void dma16_nt(i32x4 desc, unsigned int off, unsigned int lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc) : "memory", "m0");
+// `soff` is a wave-uniform byte offset added to every lane's.
+__device__ inline void dma16_nt(i32x4 desc, unsigned int off, unsigned int soff, unsigned int lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
 
 template <int N>
@@ -209,13 +215,19 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   const int dma_row = lane / C::LANES_PER_ROW;
   const int dma_pc = lane % C::LANES_PER_ROW;
   const int64_t row_bytes = p.s_pos * 2;
-  unsigned int koff[C::DMA_T_PER_WAVE], voff[C::DMA_T_PER_WAVE];
+  // When a wave's successive copies are NW * ROWS_PER_DMA rows apart and that
+  // is a multiple of the swizzle period, the lane offsets repeat and only a
+  // uniform row offset (the copy's scalar offset) changes: one VGPR per tensor.
+  constexpr bool UNIFORM_STEP = (C::NW * C::ROWS_PER_DMA) % C::NCH == 0;
+  constexpr int NOFF = UNIFORM_STEP ? 1 : C::DMA_T_PER_WAVE;
+  unsigned int koff[NOFF], voff[NOFF];
 #pragma unroll
-  for (int jj = 0; jj < C::DMA_T_PER_WAVE; ++jj) {
+  for (int jj = 0; jj < NOFF; ++jj) {
     const int r = (wave + jj * C::NW) * C::ROWS_PER_DMA + dma_row;
     koff[jj] = (unsigned int)(r * row_bytes) + ((dma_pc ^ (r & (C::NCH - 1))) << 4);
     voff[jj] = (unsigned int)(r * row_bytes) + ((dma_pc ^ ((2 * r) & (C::NCH - 1))) << 4);
   }
+  const unsigned int jj_step = (unsigned int)(C::NW * C::ROWS_PER_DMA * row_bytes);
   auto issue = [&](int tile, bool is_v) {
     const unsigned int slot = ring_off + (unsigned int)((tile % STAGES) * C::STAGE_BYTES + (is_v ? C::TILE_BYTES : 0));
     const int64_t tile_bytes = (int64_t)tile * TN * row_bytes;
@@ -226,7 +238,8 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     for (int jj = 0; jj < C::DMA_T_PER_WAVE; ++jj) {
       const int j = wave + jj * C::NW;
       if (C::DMA_PER_TENSOR % C::NW == 0 || j < C::DMA_PER_TENSOR)
-        dma16_nt(desc, is_v ? voff[jj] : koff[jj], slot + j * 1024);
+        dma16_nt(desc, is_v ? voff[UNIFORM_STEP ? 0 : jj] : koff[UNIFORM_STEP ? 0 : jj],
+                 UNIFORM_STEP ? jj * jj_step : 0u, slot + j * 1024);
     }
   };
 
@@ -302,6 +315,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   if (t_begin + STAGES - 1 < t_end) issue(t_begin + STAGES - 1, false);
 
   constexpr int NK = C::DMA_T_MIN, VS = STAGES - 2;
+  bf16x8 qreg[C::Q_REG ? TPW : 1][C::KSTEPS];
   for (int tile = t_begin; tile < t_end; ++tile) {
     const int later = min(STAGES - 1, t_end - 1 - tile);   // tiles issued after this one
     // K(i): later K tiles, plus V(i) and min(S-2, later) more V tiles
@@ -315,6 +329,17 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     const unsigned char* kl = lds + (tile % STAGES) * C::STAGE_BYTES;
     const unsigned char* vl = kl + C::TILE_BYTES;
 
+    if constexpr (C::Q_REG) {
+      if (tile == t_begin) {   // the queries have landed with the first K tile
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            const int r = (rg * TPW + t) * 16 + l16;
+            qreg[t][ks] = *reinterpret_cast<const bf16x8*>(qlds + r * C::ROWB + (((4 * ks + kg) ^ (r & (C::NCH - 1))) << 4));
+          }
+      }
+    }
     // ---- S^T = K Q^T over this wave's 32 positions ----
     f32x4 s[TPW][2];
 #pragma unroll
@@ -329,8 +354,13 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const int r = (rg * TPW + t) * 16 + l16;
-        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qlds + r * C::ROWB + (((4 * ks + kg) ^ (r & (C::NCH - 1))) << 4));
+        bf16x8 qv;
+        if constexpr (C::Q_REG) {
+          qv = qreg[t][ks];
+        } else {
+          const int r = (rg * TPW + t) * 16 + l16;
+          qv = *reinterpret_cast<const bf16x8*>(qlds + r * C::ROWB + (((4 * ks + kg) ^ (r & (C::NCH - 1))) << 4));
+        }
         s[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qv, s[t][0], 0, 0, 0);
         s[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qv, s[t][1], 0, 0, 0);
       }
