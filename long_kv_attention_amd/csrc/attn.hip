@@ -11,20 +11,24 @@
 //   grid.z  = block of query rows when a group has more rows than one
 //             workgroup holds.
 //   The M = G*T query rows of a KV head (G query heads x T tree nodes) are
-//   cut into 16-row MFMA tiles; wave w owns TPW consecutive row tiles, so the
-//   K/V tile staged in LDS once serves every head of the group and every node.
-//   Per KV tile of TN positions:
-//     S^T = K Q^T     v_mfma_f32_16x16x32_bf16 (A = K rows from LDS,
-//                     B = Q kept in registers); lane holds 4 positions of one
+//   cut into 16-row MFMA tiles; the RG x PG waves of a workgroup split them
+//   into RG row groups of TPW row tiles and each K/V tile into PG groups of 32
+//   positions, so the K/V tile staged in LDS once serves every head of the
+//   group and every node. Per K/V tile of TN = 32 * PG positions:
+//     S^T = K Q^T     v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q
+//                     from LDS or registers); a lane holds 4 positions of one
 //                     query row, so row statistics are lane-local plus two
-//                     cross-lane steps.
-//     online softmax  base-2, scale folded into one FMA before exp2.
+//                     cross-lane permutes.
+//     online softmax  base-2, scale folded into one FMA before exp2, lazy
+//                     rescaling of the running max.
 //     O^T += V^T P^T  v_mfma_f32_16x16x32_f16; P is packed to f16 straight
 //                     from the S^T accumulators (no shuffles); V^T comes from
-//                     LDS with ds_read_b64_tr_b16 (V stored as f16, converted
-//                     once per tile while staging).
-//   K/V tiles are double-buffered in LDS; the next tile's global loads are in
-//   flight while the current one is computed. One barrier per tile.
+//                     LDS with ds_read_b64_tr_b16, converted bf16 -> f16 in
+//                     registers (or once per tile in LDS when three or more
+//                     row groups would each convert it).
+//   All global reads are asynchronous copies into LDS (queries first, then a
+//   STAGES-deep K/V ring with separate K and V refills); two barriers per
+//   tile (K landed / previous P V done, and V landed / K reads done).
 //   Splits write (max, sum, unnormalised output) partials; a combine kernel
 //   merges them with the log-sum-exp rule. A single split normalises in place.
 #include "ts_internal.h"
@@ -70,6 +74,10 @@ struct Cfg {
   // registers after the first tile (fewer LDS reads per tile); the others
   // read them from LDS each tile (registers are short).
   static constexpr bool Q_REG = NW >= 8 && TPW <= 3;
+  // With three or more row groups, each V fragment would be converted bf16 ->
+  // f16 by that many waves: convert the tile once in LDS instead (one more
+  // barrier per tile; measured: T = 64 shapes -6%, no gain at RG = 2).
+  static constexpr bool V_SHARED = RG >= 3;
   static constexpr int ANC_BYTES = 1024;  // ancestor words of the tree nodes (one full 64-lane copy)
   static constexpr int MSLOT = 64 * CT * 16 + 2 * 16 * 4;   // one wave's O^T of a row tile + m, l
   static constexpr int MERGE_BYTES = PG * RG * MSLOT;
@@ -381,6 +389,21 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         if (tile * TN + ch / C::NCH >= rows_total) *reinterpret_cast<u32x4*>(vw + ch * 16) = u32x4{0u, 0u, 0u, 0u};
       __syncthreads();
     }
+    if constexpr (C::V_SHARED) {   // V(tile) bf16 -> f16 in place, each wave a share
+      unsigned char* vw = lds + (tile % STAGES) * C::STAGE_BYTES + C::TILE_BYTES;
+      constexpr int NCHK = C::TILE_BYTES / 16;
+      constexpr int CPL = (NCHK + C::NT - 1) / C::NT;
+      u32x4 w[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        if (NCHK % C::NT == 0 || tid + i * C::NT < NCHK) w[i] = *reinterpret_cast<const u32x4*>(vw + (tid + i * C::NT) * 16);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        if (NCHK % C::NT == 0 || tid + i * C::NT < NCHK)
+          *reinterpret_cast<u32x4*>(vw + (tid + i * C::NT) * 16) =
+              u32x4{bf16x2_to_f16x2(w[i].x), bf16x2_to_f16x2(w[i].y), bf16x2_to_f16x2(w[i].z), bf16x2_to_f16x2(w[i].w)};
+      lds_barrier();
+    }
 
     // ---- tree mask and tail (only tiles reaching past the context) ----
     if ((tile + 1) * TN > n_ctx) {
@@ -444,7 +467,8 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, f, lsum[t], 0, 0, 0);
     }
 
-    // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads, bf16 -> f16 in registers) ----
+    // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads, f16 from the shared
+    //      conversion or bf16 -> f16 in registers) ----
     {
       const int r_lo = 32 * pg + 4 * kg + (l16 >> 2);
       const int swz = (2 * r_lo) & (C::NCH - 1);  // same for r_lo + 16
@@ -457,8 +481,12 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)a_lo);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)a_hi);
         const u32x4 wb = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        const f16x8 vf = __builtin_bit_cast(
-            f16x8, u32x4{bf16x2_to_f16x2(wb.x), bf16x2_to_f16x2(wb.y), bf16x2_to_f16x2(wb.z), bf16x2_to_f16x2(wb.w)});
+        f16x8 vf;
+        if constexpr (C::V_SHARED)
+          vf = __builtin_bit_cast(f16x8, wb);
+        else
+          vf = __builtin_bit_cast(
+              f16x8, u32x4{bf16x2_to_f16x2(wb.x), bf16x2_to_f16x2(wb.y), bf16x2_to_f16x2(wb.z), bf16x2_to_f16x2(wb.w)});
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
           o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfrag[t], o[t][ct], 0, 0, 0);
