@@ -82,6 +82,8 @@ struct Cfg {
   static constexpr int MSLOT = 64 * CT * 16 + 2 * 16 * 4;   // one wave's O^T of a row tile + m, l
   static constexpr int MERGE_BYTES = PG * RG * MSLOT;
   static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES + ANC_BYTES;
+  // row tiles merged per round at the end of a split (all of LDS is free then)
+  static constexpr int MERGE_RT = LDS_BYTES / (NW * MSLOT) < TPW ? LDS_BYTES / (NW * MSLOT) : TPW;
   static_assert(MERGE_BYTES <= KV_BYTES, "split-local merge reuses the K/V ring");
   static_assert(CT % PG == 0, "merge splits the channel tiles evenly over position groups");
   static_assert(DMA_MIN_PER_WAVE >= 1, "every wave takes part in staging");
@@ -500,55 +502,15 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   for (int t = 0; t < TPW; ++t) l_run[t] = lsum[t][0];
 
   // ---- merge the PG position groups of each row group, then store ----
-  // Every wave parks its O^T fragments and (m, l) of row tile t in LDS; wave
-  // (rg, pg) then merges channel tiles pg, pg + PG, ... of its row group over
-  // the PG slots and stores them: all waves share the merge and the stores.
-  // Output: normalised rows (single split) or the split's partial (O^T, m, l).
+  // Every wave parks its O^T fragments and (m, l) of MERGE_RT row tiles in
+  // LDS per round; wave (rg, pg) then merges channel tiles pg, pg + PG, ... of
+  // its row group over the PG slots and stores them: all waves share the merge
+  // and the stores. Output: normalised rows (single split) or the split's
+  // partial (O^T, m, l).
   constexpr int CTW = C::CT / PG;   // channel tiles merged and stored per wave
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    float mu = m_run[t], wsum = l_run[t];
-    f32x4 om[CTW];
-    if constexpr (PG > 1) {
-      // LDS-only barriers: the partial stores of the previous round may stay
-      // in flight (__syncthreads would wait for them).
-      lds_barrier();  // the ring (or the previous round) is free
-      unsigned char* my = lds + (rg * PG + pg) * C::MSLOT;
-#pragma unroll
-      for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(my + (ct * 64 + lane) * 16) = o[t][ct];
-      if (kg == 0) {
-        reinterpret_cast<float*>(my + 64 * C::CT * 16)[l16] = m_run[t];
-        reinterpret_cast<float*>(my + 64 * C::CT * 16)[16 + l16] = l_run[t];
-      }
-      lds_barrier();
-      const unsigned char* grp = lds + rg * PG * C::MSLOT;
-      float mq[PG], wq[PG];
-      mu = NEG_BIG;
-#pragma unroll
-      for (int q = 0; q < PG; ++q) {
-        mq[q] = reinterpret_cast<const float*>(grp + q * C::MSLOT + 64 * C::CT * 16)[l16];
-        mu = fmaxf(mu, mq[q]);
-      }
-      wsum = 0.f;
-#pragma unroll
-      for (int q = 0; q < PG; ++q) {
-        wq[q] = __builtin_amdgcn_exp2f((mq[q] - mu) * c);
-        wsum += wq[q] * reinterpret_cast<const float*>(grp + q * C::MSLOT + 64 * C::CT * 16)[16 + l16];
-      }
-#pragma unroll
-      for (int i = 0; i < CTW; ++i) {
-        const int ct = pg + i * PG;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < PG; ++q) acc += wq[q] * *reinterpret_cast<const f32x4*>(grp + q * C::MSLOT + (ct * 64 + lane) * 16);
-        om[i] = acc;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < CTW; ++i) om[i] = o[t][i];
-    }
+  auto store = [&](int t, float mu, float wsum, const f32x4 (&om)[CTW]) {
     const int row = (rt0 + t) * 16 + l16;
-    if (!tile_on[t] || row >= M) continue;
+    if (!tile_on[t] || row >= M) return;
     if (p.n_split == 1) {
       const float inv = 1.0f / wsum;
       float* dst = p.out + ((int64_t)g * M + row) * D + 4 * kg;
@@ -562,6 +524,66 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       if (pg == 0 && kg == 0) {
         p.part_ml[prow * 2 + 0] = mu;
         p.part_ml[prow * 2 + 1] = wsum;
+      }
+    }
+  };
+  if constexpr (PG == 1) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      f32x4 om[CTW];
+#pragma unroll
+      for (int i = 0; i < CTW; ++i) om[i] = o[t][i];
+      store(t, m_run[t], l_run[t], om);
+    }
+  } else {
+    constexpr int RT = C::MERGE_RT;
+    constexpr int OFF_ML = 64 * C::CT * 16;   // m and l after the O^T fragments in a slot
+#pragma unroll
+    for (int t0 = 0; t0 < TPW; t0 += RT) {
+      // LDS-only barriers: the partial stores of the previous round may stay
+      // in flight (__syncthreads would wait for them).
+      lds_barrier();  // the ring (or the previous round) is free
+#pragma unroll
+      for (int u = 0; u < RT; ++u) {
+        const int t = t0 + u;
+        if (t >= TPW) break;
+        unsigned char* my = lds + ((u * RG + rg) * PG + pg) * C::MSLOT;
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(my + (ct * 64 + lane) * 16) = o[t][ct];
+        if (kg == 0) {
+          reinterpret_cast<float*>(my + OFF_ML)[l16] = m_run[t];
+          reinterpret_cast<float*>(my + OFF_ML)[16 + l16] = l_run[t];
+        }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int u = 0; u < RT; ++u) {
+        const int t = t0 + u;
+        if (t >= TPW) break;
+        const unsigned char* grp = lds + (u * RG + rg) * PG * C::MSLOT;
+        float mq[PG], wq[PG];
+        float mu = NEG_BIG;
+#pragma unroll
+        for (int q = 0; q < PG; ++q) {
+          mq[q] = reinterpret_cast<const float*>(grp + q * C::MSLOT + OFF_ML)[l16];
+          mu = fmaxf(mu, mq[q]);
+        }
+        float wsum = 0.f;
+#pragma unroll
+        for (int q = 0; q < PG; ++q) {
+          wq[q] = __builtin_amdgcn_exp2f((mq[q] - mu) * c);
+          wsum += wq[q] * reinterpret_cast<const float*>(grp + q * C::MSLOT + OFF_ML)[16 + l16];
+        }
+        f32x4 om[CTW];
+#pragma unroll
+        for (int i = 0; i < CTW; ++i) {
+          const int ct = pg + i * PG;
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q = 0; q < PG; ++q) acc += wq[q] * *reinterpret_cast<const f32x4*>(grp + q * C::MSLOT + (ct * 64 + lane) * 16);
+          om[i] = acc;
+        }
+        store(t, mu, wsum, om);
       }
     }
   }
