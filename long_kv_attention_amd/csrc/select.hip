@@ -32,6 +32,7 @@ namespace ts {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int HIST1_BITS = 12;
 constexpr int HIST1 = 1 << HIST1_BITS;  // bins of the first radix digit
@@ -91,53 +92,135 @@ __global__ __launch_bounds__(256) void select_prologue_kernel(const SelectParams
   }
 }
 
-// LPR lanes per row, each holding 8 channels; a wave covers 64/LPR rows.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (gfx9 layout): 48-bit base, stride 0, num_records bytes.
+// Reads at offsets >= num_records are out of range and do not touch memory.
+__device__ inline i32x4 buffer_desc(const void* base, unsigned int num_records) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  return i32x4{(int)(unsigned int)b, (int)((unsigned int)(b >> 32) & 0xffffu), (int)num_records, 0x00020000};
+}
+
+// One wave-wide asynchronous copy global -> LDS (16 B per lane) with the
+// non-temporal policy (K is streamed once): lane l's 16 bytes come from the
+// buffer at byte offset off + soff and land at LDS byte lds_off + 16 * l.
+// Callers order the LDS write with explicit vmcnt waits and barriers.
+__device__ inline void dma16_nt(i32x4 desc, unsigned int off, unsigned int soff, unsigned int lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
+}
+
+constexpr int SC_ROWS = 128;    // K rows per tile of the scoring ring
+constexpr int SC_STAGES = 4;    // ring depth: three tiles in flight while one is scored
+constexpr int SC_WAVES = 8;     // two waves per SIMD hide the LDS and reduction latencies
+
+// Sum over the 16 lanes of a DPP row (every lane gets the sum): rotations by
+// 8, 4, 2, 1 within the row, VALU only.
+__device__ inline float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
+  return x;
+}
+
+// One workgroup per chunk of rows_per_block rows of one KV head: K streams
+// through a 4-deep LDS ring of 128-row tiles (asynchronous copies, three
+// tiles in flight), each row is scored from LDS by LPR lanes holding 8
+// channels (lane-local FMAs, then an LPR-lane reduction), and candidate rows
+// are histogrammed by the top 12 bits of their order-preserving key.
 template <int D>
-__global__ __launch_bounds__(256) void select_score_kernel(const SelectParams p, unsigned int* ghist, int rows_per_block) {
-  constexpr int LPR = D / 8;
-  constexpr int RPW = 64 / LPR;   // rows per wave per step
-  constexpr int UNROLL = 4;
+__global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const SelectParams p, unsigned int* ghist,
+                                                                    int rows_per_block) {
+  constexpr int NT = SC_WAVES * 64;
+  constexpr int LPR = D / 8;                 // lanes per row
+  constexpr int RPW = 64 / LPR;              // rows per wave per step
+  constexpr int ROWB = D * 2;                // bytes per staged row
+  constexpr int TILE_BYTES = SC_ROWS * ROWB;
+  constexpr int ROWS_PER_DMA = 1024 / ROWB;
+  constexpr int DPW = TILE_BYTES / 1024 / SC_WAVES;   // copies per wave per tile
+  constexpr int STEPS = SC_ROWS / SC_WAVES / RPW;     // steps per wave per tile
+  static_assert(DPW >= 1 && STEPS >= 1, "tile covers every wave");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[SC_STAGES * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) float qlds[256];   // q-bar of the head (one 64-lane copy)
   __shared__ unsigned int lhist[HIST1];
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sub = lane % LPR;
   const int rsub = lane / LPR;
-  for (int b = tid; b < HIST1; b += 256) lhist[b] = 0u;
-
-  float qb[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) qb[e] = p.qbar[g * D + sub * 8 + e];
-  __syncthreads();
+  for (int b = tid; b < HIST1; b += NT) lhist[b] = 0u;
 
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(r0 + rows_per_block, p.n_ctx);
-  const uint16_t* kg = p.k + (int64_t)g * p.s_head + sub * 8;
-  float* sc = p.scores + (int64_t)g * p.n_ctx;
-  // each wave walks rows r0 + wave*RPW*UNROLL + ..., UNROLL groups of RPW rows in flight
-  for (int base = r0 + wave * RPW * UNROLL; base < r1; base += 4 * RPW * UNROLL) {
-    u32x4 w[UNROLL];
+  const int ntiles = r1 > r0 ? (r1 - r0 + SC_ROWS - 1) / SC_ROWS : 0;
+  const int64_t row_bytes = p.s_pos * 2;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k + (int64_t)g * p.s_head);
+  const unsigned int ring_off = (unsigned int)(uintptr_t)(const __attribute__((address_space(3))) void*)ring;
+  // copy j of a tile (wave w issues j = w, w + SC_WAVES, ...) covers ROWS_PER_DMA dense rows
+  const unsigned int loff = (unsigned int)((wave * ROWS_PER_DMA + lane / LPR) * row_bytes) + (lane % LPR) * 16;
+  const unsigned int jj_step = (unsigned int)(SC_WAVES * ROWS_PER_DMA * row_bytes);
+  auto issue = [&](int t) {
+    const int64_t rem = (int64_t)(r1 - r0 - t * SC_ROWS) * row_bytes;
+    const unsigned int nrec = rem > 0xffffffffll ? 0xffffffffu : (unsigned int)rem;
+    const i32x4 desc = buffer_desc(kbase + (int64_t)(r0 + t * SC_ROWS) * row_bytes, nrec);
+    const unsigned int slot = ring_off + (unsigned int)((t % SC_STAGES) * TILE_BYTES);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int j = base + u * RPW + rsub;
-      w[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j < r1) w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + (int64_t)j * p.s_pos));
+    for (int jj = 0; jj < DPW; ++jj) dma16_nt(desc, loff, jj * jj_step, slot + (wave + jj * SC_WAVES) * 1024);
+  };
+  // q-bar by the same copy, first, so the first tile's wait covers it (a plain
+  // load would make the compiler wait for every copy in flight before the loop)
+  if (wave == 0)
+    dma16_nt(buffer_desc(p.qbar + g * D, (unsigned int)(D * 4)), (unsigned int)(lane * 16), 0u,
+             (unsigned int)(uintptr_t)(const __attribute__((address_space(3))) void*)qlds);
+#pragma unroll
+  for (int t = 0; t < SC_STAGES - 1; ++t)
+    if (t < ntiles) issue(t);
+
+  float* sc = p.scores + (int64_t)g * p.n_ctx;
+  for (int t = 0; t < ntiles; ++t) {
+    const int later = min(SC_STAGES - 2, ntiles - 1 - t);   // tiles issued after this one
+    if (later >= 2) wait_vm<2 * DPW>();
+    else if (later == 1) wait_vm<DPW>();
+    else wait_vm<0>();
+    __syncthreads();   // tile t landed for every wave; tile t-1's slot is free
+    if (t + SC_STAGES - 1 < ntiles) issue(t + SC_STAGES - 1);
+    const unsigned char* tl = ring + (t % SC_STAGES) * TILE_BYTES;
+    float qb[8];
+    {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(qlds + sub * 8);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(qlds + sub * 8 + 4);
+      qb[0] = a.x; qb[1] = a.y; qb[2] = a.z; qb[3] = a.w;
+      qb[4] = b.x; qb[5] = b.y; qb[6] = b.z; qb[7] = b.w;
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
+    for (int st = 0; st < STEPS; ++st) {
+      const int row = (wave * STEPS + st) * RPW + rsub;   // row within the tile
+      const int j = r0 + t * SC_ROWS + row;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(tl + row * ROWB + sub * 16);
       float acc = 0.f;
-      acc = fmaf(qb[0], bf16_lo(w[u].x), acc);
-      acc = fmaf(qb[1], bf16_hi(w[u].x), acc);
-      acc = fmaf(qb[2], bf16_lo(w[u].y), acc);
-      acc = fmaf(qb[3], bf16_hi(w[u].y), acc);
-      acc = fmaf(qb[4], bf16_lo(w[u].z), acc);
-      acc = fmaf(qb[5], bf16_hi(w[u].z), acc);
-      acc = fmaf(qb[6], bf16_lo(w[u].w), acc);
-      acc = fmaf(qb[7], bf16_hi(w[u].w), acc);
+      acc = fmaf(qb[0], bf16_lo(w.x), acc);
+      acc = fmaf(qb[1], bf16_hi(w.x), acc);
+      acc = fmaf(qb[2], bf16_lo(w.y), acc);
+      acc = fmaf(qb[3], bf16_hi(w.y), acc);
+      acc = fmaf(qb[4], bf16_lo(w.z), acc);
+      acc = fmaf(qb[5], bf16_hi(w.z), acc);
+      acc = fmaf(qb[6], bf16_lo(w.w), acc);
+      acc = fmaf(qb[7], bf16_hi(w.w), acc);
+      if constexpr (LPR == 16) {
+        acc = row16_sum(acc);
+      } else {
 #pragma unroll
-      for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-      const int j = base + u * RPW + rsub;
+        for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+      }
       if (sub == 0 && j < r1) {
         sc[j] = acc;
         if (j >= p.cand_lo && j < p.cand_hi) atomicAdd(&lhist[f2key(acc) >> (32 - HIST1_BITS)], 1u);
@@ -145,7 +228,7 @@ __global__ __launch_bounds__(256) void select_score_kernel(const SelectParams p,
     }
   }
   __syncthreads();
-  for (int b = tid; b < HIST1; b += 256) {
+  for (int b = tid; b < HIST1; b += NT) {
     const unsigned int c = lhist[b];
     if (c) atomicAdd(&ghist[g * HIST1 + b], c);
   }
@@ -568,15 +651,16 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   else
     hipLaunchKernelGGL(select_prologue_kernel<64>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist);
   if (p.n_ctx > 0) {
-    // ~1024 scoring blocks over all heads, at least 256 rows each
-    int chunks = (1024 + p.Hkv - 1) / p.Hkv;
+    // about one scoring workgroup per compute unit over all heads, at least
+    // one 128-row tile each
+    int chunks = (256 + p.Hkv - 1) / p.Hkv;
     int rpb = (p.n_ctx + chunks - 1) / chunks;
-    if (rpb < 256) rpb = 256;
+    if (rpb < SC_ROWS) rpb = SC_ROWS;
     chunks = (p.n_ctx + rpb - 1) / rpb;
     if (p.d == 128)
-      hipLaunchKernelGGL(select_score_kernel<128>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, ws.hist, rpb);
+      hipLaunchKernelGGL(select_score_kernel<128>, dim3(chunks, p.Hkv), dim3(SC_WAVES * 64), 0, stream, p, ws.hist, rpb);
     else
-      hipLaunchKernelGGL(select_score_kernel<64>, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, ws.hist, rpb);
+      hipLaunchKernelGGL(select_score_kernel<64>, dim3(chunks, p.Hkv), dim3(SC_WAVES * 64), 0, stream, p, ws.hist, rpb);
   }
   const int nb = select_blocks_per_head(p.n_ctx, p.Hkv, p.n_sink, p.n_recent);
   if (p.b_eff > 0) {
