@@ -9,27 +9,38 @@
 // most top_p), the min-p set (p_i >= min_p * max p), their intersection, the
 // renormalised probabilities and an inverse-CDF token for a given u.
 //
-// Every row is split into nb chunks of ids, one 256-thread workgroup each, so
-// a few rows still spread over the whole chip. Passes (one launch each, in
-// stream order; the row's z stays in L2 / the last-level cache after the
-// first):
-//   1. z       window ids of the chunk -> LDS bitmap (set semantics makes
-//              duplicates harmless); penalty + temperature -> logits_out; the
-//              chunk's max. Also clears the row's mass histogram.
-//   2. hist    row max from the chunk maxima; e_i = exp(z_i - max) as 2^-40
-//              fixed point; mass and count histogram over the top 12 bits of
-//              the order-preserving key of z (integer atomics, so the sums do
-//              not depend on timing); the chunk's total mass.
-//   3. cutbin  every workgroup finds the bin where the mass from the top
-//              crosses top_p * total and lists its chunk's keys in that bin.
-//   4. keep    every workgroup refines the lists by two 10-bit radix digits
-//              (mass histograms) to the exact cut key, the mass above it and
-//              how many of its ties (ids ascending) stay; keep mask (top-p and
-//              min-p) and the chunk's kept mass.
-//   5. probs   renormalised probabilities; the workgroup whose kept-mass range
-//              holds u * total finds the token by an ordered scan.
-// Passes 2-3 and the refinement are skipped when top_p >= 1, pass 5 when
-// neither probs nor a token is requested.
+// Both filters keep a prefix of the (p desc, id asc) order, so the kept set
+// is the shorter of the two prefixes, and every token ordered before a min-p
+// token is itself a min-p token: the top-p masses inside the min-p set need
+// nothing outside it. On peaked rows the min-p set is small (a few hundred
+// ids of a 128K vocabulary at min_p = 0.05), so the pass decides on it alone
+// whenever it fits, and runs a radix select over the whole row only when it
+// does not (min_p near 0, flat rows).
+//
+// Two launches; every row is split into nb chunks of ids, one 512-thread
+// workgroup each, so a few rows still spread over the whole chip:
+//   1. z    window ids of the chunk -> LDS bitmap (set semantics makes
+//           duplicates harmless); penalty and temperature -> logits_out; the
+//           chunk's max m_b and sum of exp(z - m_b), merged in a fixed order;
+//           the chunk's candidates z - m_b >= ln(min_p) (a superset of its
+//           min-p members, as m_b <= max z), listed as sort keys (z
+//           descending, id ascending), at most CAP_B per chunk.
+//   2. out  every workgroup of a row takes the same decision: row max and mass
+//           Z from the chunk partials; if no list overflowed, the min-p set S
+//           from the lists (at most SCAP); if the mass of S less its lightest
+//           member is within top_p * Z, all of S is kept, else S is sorted in
+//           LDS and cut by exclusive prefix mass. Otherwise a radix select over
+//           the whole row (a 12-bit and two 10-bit digits of the key, mass
+//           histograms) gives the top-p cut key and how many of its ties (ids
+//           ascending) stay. The token, when the kept set is listed, comes
+//           from the one workgroup whose chunk holds the crossing of u times
+//           the kept mass (else from an ordered scan of the row by the first
+//           workgroup); then the chunk's keep mask and renormalised
+//           probabilities.
+// The mass of one token is exp(z - max z) in fp32 taken to 2^-40 fixed point,
+// so every prefix mass is an exact integer sum, whatever the summation order.
+// The penalty and the temperature are applied as products with their fp32
+// reciprocals (within two roundings of the quotients).
 #include "ts_internal.h"
 
 #include <climits>
@@ -38,20 +49,24 @@
 namespace ts {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+typedef unsigned long long u64;
 
-constexpr int PB = 256;                 // threads per workgroup
+constexpr int PB = 512;                 // threads per workgroup
 constexpr int NW = PB / 64;
 constexpr int NBR_MAX = 64;             // workgroups per row
 constexpr int H1_BITS = 12;
-constexpr int H1 = 1 << H1_BITS;
+constexpr int H1 = 1 << H1_BITS;        // bins of the first radix digit
+constexpr int H2 = 1 << 10;             // bins of the second and third digits
 constexpr int MAX_V = 262144;
 constexpr int RPT = 16;                 // 64-id steps per wave in an ordered sub-chunk
 constexpr int SEGW = 64 * RPT;          // ids per wave segment of a sub-chunk
 constexpr int SUBC = PB * RPT;          // ids per ordered sub-chunk (NW segments, ascending)
-constexpr int CAND_CAP = 8192;          // cut-bin keys refined in LDS (more are refined from L2)
+constexpr int CAP_B = 1024;             // candidates listed per chunk
+constexpr int SCAP = 4096;              // largest min-p set decided in LDS
+constexpr int UNR = 16;                 // loads per thread in flight in the strided passes
 constexpr float FIX_SCALE = 1099511627776.0f;  // 2^40
+static_assert(SCAP == H1, "the sorted list and the first-digit mass histogram share LDS");
+static_assert(H2 % PB == 0 && H1 % PB == 0, "bins split evenly over the threads");
 
 __device__ inline unsigned int f2key(float f) {
   const unsigned int u = __float_as_uint(f);
@@ -61,58 +76,56 @@ __device__ inline float key2f(unsigned int k) {
   const unsigned int u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   return __uint_as_float(u);
 }
-__device__ inline unsigned long long to_fix(float e) { return (unsigned long long)(e * FIX_SCALE); }
+__device__ inline u64 to_fix(float e) { return (u64)(e * FIX_SCALE); }
+
+// Sort key: ascending order is z descending, then id ascending.
+__device__ inline u64 sort_key(float z, int id) { return ((u64)(~f2key(z)) << 32) | (unsigned int)id; }
+__device__ inline unsigned int sk_key(u64 s) { return ~(unsigned int)(s >> 32); }
+__device__ inline int sk_id(u64 s) { return (int)(unsigned int)s; }
 
 __host__ __device__ inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
+}  // namespace
+
+int penalty_blocks_per_row(int32_t rows, int32_t V) {
+  int nb = 256 / rows;                      // at most one workgroup per compute unit over all rows
+  const int by_ids = (V + 4095) / 4096;     // at least 4096 ids per workgroup
+  if (nb > by_ids) nb = by_ids;
+  if (nb > NBR_MAX) nb = NBR_MAX;
+  if (nb < 1) nb = 1;
+  return nb;
+}
+
+namespace {
+
 // Workspace (256-byte aligned pieces):
-//   hmass [rows][H1] u64, hcnt [rows][H1] u32   the row's first-digit histogram
-//   bmax  [rows][NBR_MAX] f32                  chunk maxima of z
-//   zs    [rows][NBR_MAX] u64                  chunk masses (fixed point)
-//   ccnt  [rows][NBR_MAX] u32                  cut-bin keys listed by each chunk
-//   km    [rows][NBR_MAX] f32                  chunk kept masses
-//   tie0  [rows][NBR_MAX] u32                  ties at the cut in earlier chunks
-//   cut   [rows][4] u32                        cut key, ties kept, ties in all
-//   cand  [rows][V] u32                        the cut-bin keys, chunk b's at its ids
+//   pm   [rows][NBR_MAX] f32   chunk max of z
+//   ps   [rows][NBR_MAX] f32   chunk sum of exp(z - chunk max)
+//   pc   [rows][NBR_MAX] u32   chunk candidates (> CAP_B: the list overflowed)
+//   cand [rows][nb][CAP_B] u64 candidate sort keys
 struct PenWs {
-  unsigned long long* hmass;
-  unsigned int* hcnt;
-  float* bmax;
-  unsigned long long* zs;
-  unsigned int* ccnt;
-  float* km;
-  unsigned int* tie0;
-  unsigned int* cut;
-  unsigned int* cand;
+  float* pm;
+  float* ps;
+  unsigned int* pc;
+  u64* cand;
 };
 
 __host__ __device__ inline PenWs carve(void* base, int rows) {
   char* w = static_cast<char*>(base);
   PenWs s;
-  s.hmass = reinterpret_cast<unsigned long long*>(w);
-  w += round256((size_t)rows * H1 * 8);
-  s.hcnt = reinterpret_cast<unsigned int*>(w);
-  w += round256((size_t)rows * H1 * 4);
-  s.bmax = reinterpret_cast<float*>(w);
+  s.pm = reinterpret_cast<float*>(w);
   w += round256((size_t)rows * NBR_MAX * 4);
-  s.zs = reinterpret_cast<unsigned long long*>(w);
-  w += round256((size_t)rows * NBR_MAX * 8);
-  s.ccnt = reinterpret_cast<unsigned int*>(w);
+  s.ps = reinterpret_cast<float*>(w);
   w += round256((size_t)rows * NBR_MAX * 4);
-  s.km = reinterpret_cast<float*>(w);
+  s.pc = reinterpret_cast<unsigned int*>(w);
   w += round256((size_t)rows * NBR_MAX * 4);
-  s.tie0 = reinterpret_cast<unsigned int*>(w);
-  w += round256((size_t)rows * NBR_MAX * 4);
-  s.cut = reinterpret_cast<unsigned int*>(w);
-  w += round256((size_t)rows * 4 * 4);
-  s.cand = reinterpret_cast<unsigned int*>(w);
+  s.cand = reinterpret_cast<u64*>(w);
   return s;
 }
 
 size_t pen_ws_bytes(int rows, int V) {
-  return round256((size_t)rows * H1 * 8) + round256((size_t)rows * H1 * 4) + round256((size_t)rows * NBR_MAX * 4) +
-         round256((size_t)rows * NBR_MAX * 8) + 3 * round256((size_t)rows * NBR_MAX * 4) +
-         round256((size_t)rows * 4 * 4) + round256((size_t)rows * V * 4);
+  const int nb = penalty_blocks_per_row(rows, V);
+  return 3 * round256((size_t)rows * NBR_MAX * 4) + round256((size_t)rows * nb * CAP_B * 8);
 }
 
 // Chunk b of nb over ids [0, V): a multiple of 64 ids.
@@ -122,25 +135,92 @@ __device__ inline void chunk_of(int V, int nb, int b, int* i0, int* i1) {
   *i1 = min(*i0 + chunk, V);
 }
 
+__device__ inline u64 lanemask_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
+
+// Workgroup barrier for LDS only: no thread of a workgroup here reads global
+// memory that another thread of it wrote in the same launch, so outstanding
+// global stores need not drain at every barrier (__syncthreads would wait).
+__device__ inline void bar() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---- wave reductions without LDS: DPP rotations inside each 16-lane row,
+// then the gfx950 row-pair and half swaps (v_permlane16/32_swap: with both
+// operands holding x, one result holds rows 0,0,2,2 and the other 1,1,3,3, and
+// likewise for the halves). Integer results are the same in every lane; float
+// sums can differ between lanes in the last bit, so callers use lane 0's. ----
+template <int CTRL>
+__device__ inline unsigned int dpp32(unsigned int x) {
+  return (unsigned int)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+template <typename T>
+__device__ inline void to_words(T x, unsigned int (&w)[sizeof(T) / 4]) { __builtin_memcpy(w, &x, sizeof(T)); }
+template <typename T>
+__device__ inline T from_words(const unsigned int (&w)[sizeof(T) / 4]) {
+  T x;
+  __builtin_memcpy(&x, w, sizeof(T));
+  return x;
+}
+template <int CTRL, typename T>
+__device__ inline T dpp_t(T x) {
+  unsigned int w[sizeof(T) / 4];
+  to_words(x, w);
+#pragma unroll
+  for (unsigned int& v : w) v = dpp32<CTRL>(v);
+  return from_words<T>(w);
+}
+template <bool HALVES, typename T>
+__device__ inline void swap_t(T x, T& a, T& b) {
+  unsigned int w[sizeof(T) / 4], wa[sizeof(T) / 4], wb[sizeof(T) / 4];
+  to_words(x, w);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) {
+    const auto r = HALVES ? __builtin_amdgcn_permlane32_swap(w[i], w[i], false, false)
+                          : __builtin_amdgcn_permlane16_swap(w[i], w[i], false, false);
+    wa[i] = r[0];
+    wb[i] = r[1];
+  }
+  a = from_words<T>(wa);
+  b = from_words<T>(wb);
+}
+template <typename T, typename Op>
+__device__ inline T wave_reduce(T x, Op op) {
+  x = op(x, dpp_t<0x128>(x));   // row_ror:8
+  x = op(x, dpp_t<0x124>(x));   // row_ror:4
+  x = op(x, dpp_t<0x122>(x));   // row_ror:2
+  x = op(x, dpp_t<0x121>(x));   // row_ror:1
+  T a, b;
+  swap_t<false>(x, a, b);
+  x = op(a, b);
+  swap_t<true>(x, a, b);
+  return op(a, b);
+}
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpAdd { template <typename T> __device__ T operator()(T a, T b) const { return a + b; } };
+struct OpMinU { __device__ u64 operator()(u64 a, u64 b) const { return a < b ? a : b; } };
+struct OpMaxI { __device__ int operator()(int a, int b) const { return a > b ? a : b; } };
+
 // ---- block reductions (fixed order: results do not depend on timing) ----
 __device__ inline float block_max(float x, float* red) {
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  x = wave_reduce(x, OpMax());
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
+  bar();
   float r = red[0];
   for (int w = 1; w < NW; ++w) r = fmaxf(r, red[w]);
-  __syncthreads();
+  bar();
   return r;
 }
 
 template <typename T>
 __device__ inline T block_sum(T x, T* red) {
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  x = wave_reduce(x, OpAdd());
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
+  bar();
   T r = red[0];
   for (int w = 1; w < NW; ++w) r += red[w];
-  __syncthreads();
+  bar();
   return r;
 }
 
@@ -154,75 +234,31 @@ __device__ inline T block_scan(T x, T* red, T* total) {
     if (lane >= off) incl += y;
   }
   if (lane == 63) red[wave] = incl;
-  __syncthreads();
+  bar();
   T pre = 0, tot = 0;
   for (int w = 0; w < NW; ++w) {
     if (w < wave) pre += red[w];
     tot += red[w];
   }
-  __syncthreads();
+  bar();
   *total = tot;
   return pre + incl - x;
 }
 
-// Row maximum of z from the chunk maxima (one wave loads them).
-__device__ inline float row_max(const PenWs& ws, int row, int nb, float* red) {
-  if (threadIdx.x < 64) {
-    float m = (int)threadIdx.x < nb ? ws.bmax[row * NBR_MAX + threadIdx.x] : -INFINITY;
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
-    if (threadIdx.x == 0) red[0] = m;
-  }
-  __syncthreads();
-  const float r = red[0];
-  __syncthreads();
-  return r;
-}
-
-// Row mass (fixed point) from the chunk masses.
-__device__ inline unsigned long long row_mass(const PenWs& ws, int row, int nb, unsigned long long* red) {
-  if (threadIdx.x < 64) {
-    unsigned long long m = (int)threadIdx.x < nb ? ws.zs[row * NBR_MAX + threadIdx.x] : 0ull;
-    for (int s = 32; s >= 1; s >>= 1) m += __shfl_xor(m, s);
-    if (threadIdx.x == 0) red[0] = m;
-  }
-  __syncthreads();
-  const unsigned long long r = red[0];
-  __syncthreads();
-  return r;
-}
-
-// LDS copy of the row's histogram, every thread's loads issued together.
-__device__ inline void load_hist(unsigned long long* hmass, unsigned int* hcnt, const PenWs& ws, int row) {
-  constexpr int PM = H1 / 2 / PB, PC = H1 / 4 / PB;
-  u64x2 m[PM];
-  u32x4 c[PC];
-  const u64x2* sm = reinterpret_cast<const u64x2*>(ws.hmass + (size_t)row * H1);
-  const u32x4* scnt = reinterpret_cast<const u32x4*>(ws.hcnt + (size_t)row * H1);
-#pragma unroll
-  for (int i = 0; i < PM; ++i) m[i] = sm[threadIdx.x + i * PB];
-#pragma unroll
-  for (int i = 0; i < PC; ++i) c[i] = scnt[threadIdx.x + i * PB];
-#pragma unroll
-  for (int i = 0; i < PM; ++i) reinterpret_cast<u64x2*>(hmass)[threadIdx.x + i * PB] = m[i];
-#pragma unroll
-  for (int i = 0; i < PC; ++i) reinterpret_cast<u32x4*>(hcnt)[threadIdx.x + i * PB] = c[i];
-}
-
 // Lowest non-empty bin of hmass/hcnt[0, nbins) whose mass from the top
 // (exclusive) is <= P; returns it and its exclusive mass above.
-__device__ inline int crossing_bin(const unsigned long long* hmass, const unsigned int* hcnt, int nbins,
-                                   unsigned long long P, unsigned long long* red, int* s_low,
-                                   unsigned long long* s_above, unsigned long long* above) {
+__device__ inline int crossing_bin(const u64* hmass, const unsigned int* hcnt, int nbins, u64 P, u64* red,
+                                   int* s_low, u64* s_above, u64* above) {
   const int tid = threadIdx.x;
   const int per = nbins / PB;
   const int hi_bin = nbins - 1 - tid * per;
-  unsigned long long m = 0;
+  u64 m = 0;
   for (int i = 0; i < per; ++i) m += hmass[hi_bin - i];
   if (tid == 0) *s_low = nbins;
-  unsigned long long tot;
-  const unsigned long long before = block_scan(m, red, &tot);   // ends with a barrier
+  u64 tot;
+  const u64 before = block_scan(m, red, &tot);   // ends with a barrier
   {
-    unsigned long long acc = before;
+    u64 acc = before;
     int best = nbins;
     for (int i = 0; i < per; ++i) {
       const int b = hi_bin - i;
@@ -231,19 +267,17 @@ __device__ inline int crossing_bin(const unsigned long long* hmass, const unsign
     }
     if (best < nbins) atomicMin(s_low, best);
   }
-  __syncthreads();
+  bar();
   const int b = *s_low;
   if (b <= hi_bin && b > hi_bin - per) {
-    unsigned long long acc = before;
+    u64 acc = before;
     for (int i = 0; i < per && hi_bin - i != b; ++i) acc += hmass[hi_bin - i];
     *s_above = acc;
   }
-  __syncthreads();
+  bar();
   *above = *s_above;
   return b;
 }
-
-constexpr int UNR = 16;   // loads per thread in flight in the strided passes
 
 // Thread-strided pass over ids [i0, i1) with UNR loads issued before any use.
 template <typename F>
@@ -277,149 +311,29 @@ __device__ inline void load_run(const float* z, int s0, int i1, float (&v)[RPT])
   }
 }
 
-__device__ inline unsigned long long lanemask_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
-
-// Ranks of the ties at the cut in a sub-chunk: on return tie0 is the number
-// of ties before this wave's segment (given tie_run before the sub-chunk) and
-// tie_run has advanced past the sub-chunk.
+// Ranks of the ties at the cut in a sub-chunk: returns the number of ties
+// before this wave's segment (given tie_run before the sub-chunk) and
+// advances tie_run past the sub-chunk.
 __device__ inline unsigned int wave_tie_base(const float (&v)[RPT], int s0, int i1, unsigned int cut,
                                              unsigned int* wtie, unsigned int& tie_run) {
   unsigned int c = 0;
 #pragma unroll
   for (int e = 0; e < RPT; ++e) c += (unsigned int)__popcll(__ballot(seg_id(s0, e) < i1 && f2key(v[e]) == cut));
   if ((threadIdx.x & 63) == 0) wtie[threadIdx.x >> 6] = c;
-  __syncthreads();
+  bar();
   unsigned int before = tie_run, tot = 0;
   for (int w = 0; w < NW; ++w) {
     if (w < (int)(threadIdx.x >> 6)) before += wtie[w];
     tot += wtie[w];
   }
-  __syncthreads();
+  bar();
   tie_run += tot;
   return before;
 }
 
-// ---- pass 1: penalty, temperature, chunk max; clear the histogram ----
-__global__ __launch_bounds__(PB) void pen_z_kernel(const PenaltyParams p, int nb) {
-  __shared__ unsigned int bitmap[MAX_V / 32];
-  __shared__ float red[NW];
-  const int row = blockIdx.y, tid = threadIdx.x;
-  const PenWs ws = carve(p.ws, p.rows);
-  int i0, i1;
-  chunk_of(p.V, nb, blockIdx.x, &i0, &i1);
-  if (p.top_p < 1.0f) {   // this chunk's share of the row's histogram
-    const int h0 = blockIdx.x * H1 / nb, h1 = (blockIdx.x + 1) * H1 / nb;
-    for (int b = h0 + tid; b < h1; b += PB) {
-      ws.hmass[row * H1 + b] = 0ull;
-      ws.hcnt[row * H1 + b] = 0u;
-    }
-  }
-  const int nwords = (i1 - i0 + 31) / 32;
-  for (int w = tid; w < nwords; w += PB) bitmap[w] = 0u;
-  __syncthreads();
-  if (p.W > 0) {
-    const int32_t* win = p.window + (int64_t)row * p.window_stride;
-    constexpr int WB = 8;   // window ids per thread in flight
-    for (int w0 = tid; w0 < p.W; w0 += PB * WB) {
-      int id[WB];
-#pragma unroll
-      for (int u = 0; u < WB; ++u) id[u] = w0 + u * PB < p.W ? win[w0 + u * PB] : -1;
-#pragma unroll
-      for (int u = 0; u < WB; ++u)
-        if (id[u] >= i0 && id[u] < i1) atomicOr(&bitmap[(id[u] - i0) >> 5], 1u << ((id[u] - i0) & 31));
-    }
-  }
-  __syncthreads();
-  const float* x = p.logits + (int64_t)row * p.V;
-  float* z = p.logits_out + (int64_t)row * p.V;
-  float mx = -INFINITY;
-  strided_pass(x, i0, i1, [&](int i, float v) {
-    if ((bitmap[(i - i0) >> 5] >> ((i - i0) & 31)) & 1u) v = v > 0.f ? v / p.penalty : v * p.penalty;
-    v = v / p.temperature;
-    z[i] = v;
-    mx = fmaxf(mx, v);
-  });
-  mx = block_max(mx, red);
-  if (tid == 0) ws.bmax[row * NBR_MAX + blockIdx.x] = mx;
-}
-
-// ---- pass 2: mass histogram and chunk mass ----
-__global__ __launch_bounds__(PB) void pen_hist_kernel(const PenaltyParams p, int nb) {
-  __shared__ unsigned long long hmass[H1];
-  __shared__ unsigned int hcnt[H1];
-  __shared__ unsigned long long red64[NW];
-  __shared__ float redf[NW];
-  const int row = blockIdx.y, tid = threadIdx.x;
-  const PenWs ws = carve(p.ws, p.rows);
-  int i0, i1;
-  chunk_of(p.V, nb, blockIdx.x, &i0, &i1);
-  for (int b = tid; b < H1; b += PB) {
-    hmass[b] = 0ull;
-    hcnt[b] = 0u;
-  }
-  const float zmax = row_max(ws, row, nb, redf);   // its barriers also order the clears
-  const float* z = p.logits_out + (int64_t)row * p.V;
-  unsigned long long zsum = 0;
-  strided_pass(z, i0, i1, [&](int, float v) {
-    const unsigned long long f = to_fix(__expf(v - zmax));
-    const unsigned int b = f2key(v) >> (32 - H1_BITS);
-    atomicAdd(&hmass[b], f);
-    atomicAdd(&hcnt[b], 1u);
-    zsum += f;
-  });
-  zsum = block_sum(zsum, red64);   // its barriers also retire the LDS atomics
-  for (int b = tid; b < H1; b += PB) {
-    const unsigned int c = hcnt[b];
-    if (c) {
-      atomicAdd(&ws.hmass[row * H1 + b], hmass[b]);
-      atomicAdd(&ws.hcnt[row * H1 + b], c);
-    }
-  }
-  if (tid == 0) ws.zs[row * NBR_MAX + blockIdx.x] = zsum;
-}
-
-// ---- pass 3: the crossing bin and the chunk's keys in it ----
-__global__ __launch_bounds__(PB) void pen_cutbin_kernel(const PenaltyParams p, int nb) {
-  __shared__ __attribute__((aligned(16))) unsigned long long hmass[H1];
-  __shared__ __attribute__((aligned(16))) unsigned int hcnt[H1];
-  __shared__ unsigned long long red64[NW];
-  __shared__ int s_low;
-  __shared__ unsigned long long s_above;
-  __shared__ unsigned int s_n;
-  const int row = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  const PenWs ws = carve(p.ws, p.rows);
-  int i0, i1;
-  chunk_of(p.V, nb, blockIdx.x, &i0, &i1);
-  const float* z = p.logits_out + (int64_t)row * p.V;
-  float v[RPT];
-  load_run(z, i0, i1, v);   // the first sub-chunk, in flight with the histogram
-  load_hist(hmass, hcnt, ws, row);
-  if (tid == 0) s_n = 0;
-  const unsigned long long Z = row_mass(ws, row, nb, red64);
-  const unsigned long long P = (unsigned long long)((double)p.top_p * (double)Z);
-  unsigned long long above;
-  const unsigned int bin = (unsigned int)crossing_bin(hmass, hcnt, H1, P, red64, &s_low, &s_above, &above);
-  unsigned int* cand = ws.cand + (int64_t)row * p.V + i0;
-  for (int s0 = i0; s0 < i1; s0 += SUBC) {
-    if (s0 != i0) load_run(z, s0, i1, v);
-#pragma unroll
-    for (int e = 0; e < RPT; ++e) {
-      const bool take = seg_id(s0, e) < i1 && (f2key(v[e]) >> (32 - H1_BITS)) == bin;
-      const unsigned long long m = __ballot(take);
-      if (m) {   // one LDS atomic per wave step with takers
-        const int leader = __ffsll((long long)m) - 1;
-        unsigned int base = 0;
-        if (lane == leader) base = atomicAdd(&s_n, (unsigned int)__popcll(m));
-        base = __shfl(base, leader);
-        if (take) cand[base + (unsigned int)__popcll(m & lanemask_lt())] = f2key(v[e]);
-      }
-    }
-  }
-  __syncthreads();
-  if (tid == 0) ws.ccnt[row * NBR_MAX + blockIdx.x] = s_n;
-}
-
-// The cut as every pass after the refinement sees it.
+// The kept set as every workgroup of the row sees it: keys above `cut` and
+// the first ties_kept ids with key == cut (all of them unless rank_ties), or
+// every key when all_top; then the min-p test.
 struct Cut {
   bool all_top, rank_ties;
   unsigned int cut, ties_kept;
@@ -432,251 +346,676 @@ __device__ inline bool keep_step(const Cut& c, float zv, bool valid, unsigned in
   const unsigned int key = f2key(zv);
   bool top = c.all_top || key > c.cut;
   const bool tie = !c.all_top && valid && key == c.cut;
-  const unsigned long long tm = __ballot(tie);
+  const u64 tm = __ballot(tie);
   if (tie) top = !c.rank_ties || tie_i + (unsigned int)__popcll(tm & lanemask_lt()) < c.ties_kept;
   tie_i += (unsigned int)__popcll(tm);
   return valid && top && (zv - c.zmax >= c.ln_min_p);
 }
 
-// ---- pass 4: exact cut, keep mask and the chunk's kept mass ----
-__global__ __launch_bounds__(PB) void pen_keep_kernel(const PenaltyParams p, int nb) {
-  __shared__ __attribute__((aligned(16))) unsigned long long hmass[H1];
-  __shared__ __attribute__((aligned(16))) unsigned int hcnt[H1];
-  __shared__ unsigned int cand_l[CAND_CAP];
-  __shared__ unsigned long long red64[NW];
+// Ascending in-place bitonic sort of s[0, n), n a power of two, by the whole
+// workgroup; ends with a barrier.
+__device__ inline void bitonic_sort(u64* s, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += PB) {
+        const int pr = i ^ j;
+        if (pr > i) {
+          const u64 a = s[i], b = s[pr];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) {
+            s[i] = b;
+            s[pr] = a;
+          }
+        }
+      }
+      bar();
+    }
+  }
+}
+
+// Appends the values of the taking lanes of N wave steps to an LDS-counted
+// list with one LDS atomic per wave (step order, then lane order);
+// put(step, slot) stores one value. The counter counts every taker.
+template <int N, typename F>
+__device__ inline void wave_append(const bool (&take)[N], unsigned int* counter, F&& put) {
+  u64 bm[N];
+  unsigned int tot = 0;
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    bm[r] = __ballot(take[r]);
+    tot += (unsigned int)__popcll(bm[r]);
+  }
+  if (tot == 0u) return;   // wave-uniform
+  unsigned int base = 0;
+  if ((threadIdx.x & 63) == 0) base = atomicAdd(counter, tot);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    if (take[r]) put(r, base + (unsigned int)__popcll(bm[r] & lanemask_lt()));
+    base += (unsigned int)__popcll(bm[r]);
+  }
+}
+
+__device__ inline int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// ---- pass 1: penalty, temperature, chunk partials and min-p candidates ----
+// Chunks of up to ZR * PB ids stay in registers (one read of the logits, the
+// window ids in flight with them; 16-byte accesses of 4 ids when the rows are
+// 16-byte aligned); larger ones (few rows) take a strided loop with an online
+// sum and re-read their own z for the candidates.
+constexpr int ZR = 32;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(PB) void pen_z_kernel(const PenaltyParams p, int nb) {
+  __shared__ unsigned int bitmap[MAX_V / 32];
   __shared__ float redf[NW];
-  __shared__ unsigned int redu[NW];
-  __shared__ unsigned int seg_off[NBR_MAX + 1];
-  __shared__ int s_low;
-  __shared__ unsigned long long s_above;
+  __shared__ unsigned int s_n;
   const int row = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const PenWs ws = carve(p.ws, p.rows);
   int i0, i1;
   chunk_of(p.V, nb, blockIdx.x, &i0, &i1);
-  const float* z = p.logits_out + (int64_t)row * p.V;
-  float v[RPT];
-  load_run(z, i0, i1, v);   // the first sub-chunk, in flight with what follows
+  const float* x = p.logits + (int64_t)row * p.V;
+  float* z = p.logits_out + (int64_t)row * p.V;
+  const bool in_regs = i1 - i0 <= ZR * PB;
+  // 4 ids per access: chunk bounds are then multiples of 4 (i0 of 64, V of 4)
+  const bool vec = in_regs && (p.V & 3) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(p.logits) | reinterpret_cast<uintptr_t>(p.logits_out)) & 15) == 0;
+  // id of register slot u
+  auto slot_id = [&](int u) { return vec ? i0 + 4 * (tid + (u >> 2) * PB) + (u & 3) : i0 + tid + u * PB; };
+  float v[ZR];
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < ZR / 4; ++q) {
+      const int g = i0 + 4 * (tid + q * PB);
+      const f32x4 t = g < i1 ? *reinterpret_cast<const f32x4*>(x + g) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[4 * q + c] = t[c];
+    }
+  } else if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) {
+      const int i = slot_id(u);
+      v[u] = i < i1 ? x[i] : -INFINITY;
+    }
+  }
+  constexpr int WB = 4;   // window ids per thread loaded with the logits
+  const int32_t* win = p.window + (int64_t)row * p.window_stride;
+  int wid[WB];
+#pragma unroll
+  for (int u = 0; u < WB; ++u) wid[u] = tid + u * PB < p.W ? win[tid + u * PB] : -1;
+  const int nwords = (i1 - i0 + 31) / 32;
+  for (int w = tid; w < nwords; w += PB) bitmap[w] = 0u;
+  if (tid == 0) s_n = 0u;
+  bar();
+  auto mark = [&](int id) {
+    if (id >= i0 && id < i1) atomicOr(&bitmap[(id - i0) >> 5], 1u << ((id - i0) & 31));
+  };
+#pragma unroll
+  for (int u = 0; u < WB; ++u) mark(wid[u]);
+  for (int j = tid + WB * PB; j < p.W; j += PB) mark(win[j]);
+  bar();
+  // x / penalty or x * penalty on window ids, then / temperature, by reciprocals
+  const float inv_pen = 1.0f / p.penalty, inv_t = p.inv_temperature;
+  auto penalised = [&](bool hit, float w) {
+    w = hit ? (w > 0.f ? w * inv_pen : w * p.penalty) : w;
+    return w * inv_t;
+  };
+  auto hit_at = [&](int i) { return ((bitmap[(i - i0) >> 5] >> ((i - i0) & 31)) & 1u) != 0u; };
+  float mb, sb;
+  if (in_regs) {
+    // the slots' bitmap words first (all LDS reads in flight), then branch-free
+    // arithmetic; slots past the chunk hold -inf and stay -inf
+    unsigned int pw[ZR];
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) {
+      const int o = slot_id(u) - i0;   // < ZR * PB: inside the bitmap
+      pw[u] = bitmap[o >> 5] >> (o & 31);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) {
+      v[u] = penalised((pw[u] & 1u) != 0u, v[u]);
+      m = fmaxf(m, v[u]);
+    }
+    if (vec) {
+#pragma unroll
+      for (int q = 0; q < ZR / 4; ++q) {
+        const int g = i0 + 4 * (tid + q * PB);
+        if (g < i1) *reinterpret_cast<f32x4*>(z + g) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) {
+        const int i = slot_id(u);
+        if (i < i1) z[i] = v[u];
+      }
+    }
+    mb = block_max(m, redf);
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) s += v[u] > -INFINITY ? __expf(v[u] - mb) : 0.f;   // -inf past i1
+    sb = block_sum(s, redf);
+  } else {
+    // running max of this thread's z and sum of exp(z - running max)
+    float m = -INFINITY, s = 0.f;
+    strided_pass(x, i0, i1, [&](int i, float w) {
+      w = penalised(hit_at(i), w);
+      z[i] = w;
+      if (w > m) {
+        s = s * __expf(m - w) + 1.f;
+        m = w;
+      } else if (w > -INFINITY) {
+        s += __expf(w - m);
+      }
+    });
+    mb = block_max(m, redf);
+    sb = block_sum(m > -INFINITY ? s * __expf(m - mb) : 0.f, redf);
+  }
+  // candidates z - mb >= ln(min_p), listed by one LDS atomic per wave step with takers
+  const float ln_min_p = logf(p.min_p);   // -inf for min_p = 0
+  const bool listed = !(ln_min_p == -INFINITY && i1 - i0 > CAP_B);
+  u64* out = ws.cand + ((int64_t)row * nb + blockIdx.x) * CAP_B;
+  auto list_step = [&](int i, float w) {   // all lanes of the wave call it
+    const bool take = i < i1 && w - mb >= ln_min_p;
+    const u64 bm = __ballot(take);
+    if (bm) {
+      const int leader = __ffsll((long long)bm) - 1;
+      unsigned int base = 0;
+      if (lane == leader) base = atomicAdd(&s_n, (unsigned int)__popcll(bm));
+      base = __shfl(base, leader);
+      const unsigned int slot = base + (unsigned int)__popcll(bm & lanemask_lt());
+      if (take && slot < (unsigned int)CAP_B) out[slot] = sort_key(w, i);
+    }
+  };
+  if (listed) {
+    if (in_regs) {
+      bool take[ZR];
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) take[u] = slot_id(u) < i1 && v[u] - mb >= ln_min_p;
+      wave_append(take, &s_n, [&](int u, unsigned int slot) {
+        if (slot < (unsigned int)CAP_B) out[slot] = sort_key(v[u], slot_id(u));
+      });
+    } else {
+      // every thread re-reads the z it wrote above (same ids)
+      for (int b = i0 + tid; b < i1; b += UNR * PB) {
+        float w[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int i = b + u * PB;
+          w[u] = i < i1 ? z[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) list_step(b + u * PB, w[u]);
+      }
+    }
+  }
+  bar();
+  if (tid == 0) {
+    ws.pm[row * NBR_MAX + blockIdx.x] = mb;
+    ws.ps[row * NBR_MAX + blockIdx.x] = sb;
+    ws.pc[row * NBR_MAX + blockIdx.x] = listed ? s_n : 0xffffffffu;
+  }
+}
+
+// ---- pass 2: the row's cut, keep mask, probabilities and token ----
+constexpr int SPEC_R = 8;   // list entries per thread loaded together with the partials
+
+__global__ __launch_bounds__(PB) void pen_out_kernel(const PenaltyParams p, int nb) {
+  // the min-p set's sort keys, or the first-digit mass histogram of the radix select
+  __shared__ __attribute__((aligned(16))) u64 list[SCAP];
+  // counts of the radix select; the chunk's kept-id bitmap or the members' masses afterwards
+  __shared__ __attribute__((aligned(16))) unsigned int hcnt[H1];
+  __shared__ unsigned int hbefore[H2];
+  __shared__ u64 red64[NW], red64b[NW];
+  __shared__ unsigned int redu[NW];
+  __shared__ unsigned int s_cnt[NBR_MAX];
+  __shared__ float s_zmax;
+  __shared__ double s_Z;
+  __shared__ int s_over, s_low, s_k, s_first, s_last, s_tok, s_lastkept;
+  __shared__ unsigned int s_n;
+  __shared__ u64 s_above, s_w;
+  const int row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const PenWs ws = carve(p.ws, p.rows);
+  const int V = p.V;
+  int i0, i1;
+  chunk_of(V, nb, blockIdx.x, &i0, &i1);
+  const float* z = p.logits_out + (int64_t)row * V;
+
+  // the first `per` entries of every list, in flight with the partials (entries
+  // past a list's count are read but not used)
+  const int per = min(CAP_B, SPEC_R * PB / nb);
+  const u64* cand = ws.cand + (int64_t)row * nb * CAP_B;
+  u64 spec[SPEC_R];
+#pragma unroll
+  for (int r = 0; r < SPEC_R; ++r) {
+    const int idx = tid + r * PB, b = idx / per;
+    spec[r] = b < nb ? cand[(int64_t)b * CAP_B + (idx - b * per)] : 0ull;
+  }
+  // row max, row mass Z (chunk sums rescaled, fixed order), list counts: one wave
+  if (tid < 64) {
+    const float mb = lane < nb ? ws.pm[row * NBR_MAX + lane] : -INFINITY;
+    const float sb = lane < nb ? ws.ps[row * NBR_MAX + lane] : 0.f;
+    const unsigned int cb = lane < nb ? ws.pc[row * NBR_MAX + lane] : 0u;
+    const float zm = wave_reduce(mb, OpMax());
+    const double t = wave_reduce(mb > -INFINITY ? (double)sb * (double)__expf(mb - zm) : 0.0, OpAdd());
+    const bool over = cb > (unsigned int)CAP_B;
+    if (lane < nb) s_cnt[lane] = over ? 0u : cb;
+    const u64 ob = __ballot(over);
+    if (lane == 0) {
+      s_zmax = zm;
+      s_Z = t;
+      s_over = ob != 0ull;
+      s_n = 0u;
+    }
+  }
+  bar();
   Cut c;
-  c.all_top = p.top_p >= 1.0f;
+  c.zmax = s_zmax;
   c.ln_min_p = logf(p.min_p);   // -inf for min_p = 0
+  c.all_top = p.top_p >= 1.0f;
   c.cut = 0u;
   c.ties_kept = 0u;
   c.rank_ties = false;
-  unsigned int tie_before = 0;   // ties at the cut in earlier chunks
-  if (!c.all_top) {
-    load_hist(hmass, hcnt, ws, row);
-    if (tid < 64) {   // list offsets: one wave scans the chunks' list lengths
-      const unsigned int cn = lane < nb ? ws.ccnt[row * NBR_MAX + lane] : 0u;
-      unsigned int incl = cn;
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+  const double Zfix = s_Z * (double)FIX_SCALE;
+  const u64 P = c.all_top ? ~0ull : (u64)((double)p.top_p * Zfix);   // top-p mass bound, fixed point
+  unsigned int tie_before = 0;   // ties at the cut with ids below the chunk
+  u64 W = 0;                     // kept mass, fixed point
+  bool fast = !s_over;
+  int n_S = 0;
+  int n_K = 0;                   // fast path: the kept members are list[0, n_K) after the decision
+
+  if (fast) {
+    // the row's min-p set: listed entries with z - zmax >= ln(min_p)
+    auto push = [&](bool take, u64 e) {   // all lanes of the wave call it
+      const u64 bm = __ballot(take);
+      if (bm) {
+        const int leader = __ffsll((long long)bm) - 1;
+        unsigned int base = 0;
+        if (lane == leader) base = atomicAdd(&s_n, (unsigned int)__popcll(bm));
+        base = __shfl(base, leader);
+        const unsigned int slot = base + (unsigned int)__popcll(bm & lanemask_lt());
+        if (take && slot < (unsigned int)SCAP) list[slot] = e;
       }
-      if (lane < nb) seg_off[lane] = incl - cn;
-      if (lane == 63) seg_off[nb] = incl;
+    };
+    auto member = [&](u64 e) { return key2f(sk_key(e)) - c.zmax >= c.ln_min_p; };
+    {
+      bool take[SPEC_R];
+#pragma unroll
+      for (int r = 0; r < SPEC_R; ++r) {
+        const int idx = tid + r * PB, b = idx / per;
+        take[r] = b < nb && (unsigned int)(idx - b * per) < s_cnt[min(b, nb - 1)] && member(spec[r]);
+      }
+      wave_append(take, &s_n, [&](int r, unsigned int slot) {
+        if (slot < (unsigned int)SCAP) list[slot] = spec[r];
+      });
     }
+    for (int b = 0; b < nb; ++b) {   // lists longer than `per`
+      const int cb = (int)s_cnt[b];
+      for (int j0 = per; j0 < cb; j0 += PB) {
+        const int j = j0 + tid;
+        const u64 e = j < cb ? cand[(int64_t)b * CAP_B + j] : 0ull;
+        push(j < cb && member(e), e);
+      }
+    }
+    bar();
+    n_S = (int)s_n;
+    fast = n_S <= SCAP;
   }
-  c.zmax = row_max(ws, row, nb, redf);   // its barriers also publish the loads above
-  if (!c.all_top) {
-    unsigned long long P = (unsigned long long)((double)p.top_p * (double)row_mass(ws, row, nb, red64));
-    const unsigned int n = seg_off[nb];
-    const unsigned int* cand_g = ws.cand + (int64_t)row * p.V;
-    auto seg_of = [&](unsigned int i) {   // list owning key i: the last b with seg_off[b] <= i
-      int lo = 0, hi = nb - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seg_off[mid] <= i) lo = mid; else hi = mid - 1;
-      }
-      return lo;
-    };
-    auto key_at = [&](unsigned int i) {
-      const int b = seg_of(i);
-      int c0, c1;
-      chunk_of(p.V, nb, b, &c0, &c1);
-      return cand_g[c0 + (i - seg_off[b])];
-    };
-    const bool in_lds = n <= (unsigned int)CAND_CAP;
-    if (in_lds) {
-      constexpr int BATCH = 8;
-      for (unsigned int b0 = tid; b0 < n; b0 += PB * BATCH) {
-        unsigned int kv[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) kv[u] = b0 + u * PB < n ? key_at(b0 + u * PB) : 0u;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u)
-          if (b0 + u * PB < n) cand_l[b0 + u * PB] = kv[u];
-      }
+
+  if (fast) {
+    // mass of S and of its lightest member (one pair of barriers for both)
+    u64 tot = 0, emin = ~0ull;
+    for (int j = tid; j < n_S; j += PB) {
+      const u64 ef = to_fix(__expf(key2f(sk_key(list[j])) - c.zmax));
+      tot += ef;
+      emin = ef < emin ? ef : emin;
     }
-    __syncthreads();
-    unsigned long long above;
-    unsigned int prefix = (unsigned int)crossing_bin(hmass, hcnt, H1, P, red64, &s_low, &s_above, &above);
-    P -= above;
-    int shift = 32 - H1_BITS;
-    unsigned int cut_count = 0;
-    for (int pass = 0; pass < 2; ++pass) {
-      constexpr int nbins = 1 << 10;
-      const int new_shift = shift - 10;
-      __syncthreads();
-      for (int b = tid; b < nbins; b += PB) {
-        hmass[b] = 0ull;
-        hcnt[b] = 0u;
+    tot = wave_reduce(tot, OpAdd());
+    emin = wave_reduce(emin, OpMinU());
+    if (lane == 0) {
+      red64[wave] = tot;
+      red64b[wave] = emin;
+    }
+    bar();
+    tot = 0;
+    emin = ~0ull;
+    for (int w = 0; w < NW; ++w) {
+      tot += red64[w];
+      emin = red64b[w] < emin ? red64b[w] : emin;
+    }
+    bar();
+    if (c.all_top || n_S == 0 || tot - emin <= P) {
+      // the last member of S in order has mass tot - emin before it: all of S is kept
+      c.all_top = true;
+      W = tot;
+      n_K = n_S;
+    } else {
+      const int n_pad = pow2_at_least(n_S);
+      for (int j = n_S + tid; j < n_pad; j += PB) list[j] = ~0ull;
+      if (tid == 0) {
+        s_k = -1;
+        s_first = INT_MAX;
+        s_last = -1;
       }
-      __syncthreads();
-      for (unsigned int i = tid; i < n; i += PB) {
-        const unsigned int key = in_lds ? cand_l[i] : key_at(i);
-        if ((key >> shift) == prefix) {
-          const unsigned int b = (key >> new_shift) & (nbins - 1);
-          atomicAdd(&hmass[b], to_fix(__expf(key2f(key) - c.zmax)));
-          atomicAdd(&hcnt[b], 1u);
+      bar();
+      bitonic_sort(list, n_pad);
+      // exclusive prefix masses; thread t owns the run [t*R, (t+1)*R) of the sorted list
+      const int R = (n_pad + PB - 1) / PB;
+      const int j0 = tid * R;
+      u64 run = 0;
+      for (int r = 0; r < R; ++r) {
+        const int j = j0 + r;
+        if (j < n_S) run += to_fix(__expf(key2f(sk_key(list[j])) - c.zmax));
+      }
+      u64 total;
+      u64 excl = block_scan(run, red64, &total);
+      int k_loc = -1;
+      u64 w_loc = 0;
+      for (int r = 0; r < R; ++r) {
+        const int j = j0 + r;
+        if (j < n_S) {
+          const u64 ef = to_fix(__expf(key2f(sk_key(list[j])) - c.zmax));
+          if (excl <= P) {   // kept members form the prefix list[0, k]
+            k_loc = j;
+            w_loc = excl + ef;
+          }
+          excl += ef;
         }
       }
-      __syncthreads();
-      const int b = crossing_bin(hmass, hcnt, nbins, P, red64, &s_low, &s_above, &above);
-      P -= above;
-      if (pass == 1) cut_count = hcnt[b];
-      prefix = (prefix << 10) | (unsigned int)b;
-      shift = new_shift;
+      if (k_loc >= 0) atomicMax(&s_k, k_loc);
+      bar();
+      const int k = s_k;   // >= 0: the first member has no mass before it
+      if (k_loc == k) s_w = w_loc;
+      const unsigned int ck = sk_key(list[k]);
+      for (int j = tid; j < n_S; j += PB)
+        if (sk_key(list[j]) == ck) {
+          atomicMin(&s_first, j);
+          atomicMax(&s_last, j);
+        }
+      bar();
+      const int f = s_first, l = s_last;
+      W = s_w;
+      n_K = k + 1;
+      c.cut = ck;
+      c.ties_kept = (unsigned int)(k - f + 1);
+      c.rank_ties = k < l;
+      if (c.rank_ties) {   // the ties are sorted by id: count those below the chunk
+        unsigned int t = 0;
+        for (int j = f + tid; j <= l; j += PB) t += sk_id(list[j]) < i0;
+        tie_before = block_sum(t, redu);
+      }
     }
-    c.cut = prefix;
-    const unsigned long long ecut = to_fix(__expf(key2f(c.cut) - c.zmax));
-    // ties at the cut: the t-th (0-based, ids ascending) has mass before it = above + t * ecut
-    const unsigned long long nt = ecut ? P / ecut + 1ull : (unsigned long long)cut_count;
-    c.ties_kept = nt < cut_count ? (unsigned int)nt : cut_count;
-    c.rank_ties = c.ties_kept < cut_count;
-    if (c.rank_ties) {   // ties in earlier chunks: their listed keys equal to the cut
-      unsigned int t = 0;
-      for (unsigned int i = tid; i < seg_off[blockIdx.x]; i += PB) t += (in_lds ? cand_l[i] : key_at(i)) == c.cut;
-      tie_before = block_sum(t, redu);
+  } else {
+    // ---- radix select over the whole row ----
+    u64* hmass = list;
+    for (int b = tid; b < H1; b += PB) {
+      hmass[b] = 0ull;
+      hcnt[b] = 0u;
     }
-    if (tid == 0) {
-      ws.tie0[row * NBR_MAX + blockIdx.x] = tie_before;
-      if (blockIdx.x == 0) {
-        ws.cut[row * 4 + 0] = c.cut;
-        ws.cut[row * 4 + 1] = c.ties_kept;
-        ws.cut[row * 4 + 2] = cut_count;
+    bar();
+    u64 smass = 0;   // mass of the min-p set
+    const bool top = !c.all_top;
+    strided_pass(z, 0, V, [&](int, float v) {
+      const u64 ef = to_fix(__expf(v - c.zmax));
+      if (v - c.zmax >= c.ln_min_p) smass += ef;
+      if (top) {
+        const unsigned int b = f2key(v) >> (32 - H1_BITS);
+        atomicAdd(&hmass[b], ef);
+        atomicAdd(&hcnt[b], 1u);
+      }
+    });
+    smass = block_sum(smass, red64);   // its barriers also retire the LDS atomics
+    if (!top) {
+      W = smass;
+    } else {
+      u64 above;
+      unsigned int prefix = (unsigned int)crossing_bin(hmass, hcnt, H1, P, red64, &s_low, &s_above, &above);
+      u64 Pr = P - above;
+      int shift = 32 - H1_BITS;
+      unsigned int cut_count = 0;
+      for (int pass = 0; pass < 2; ++pass) {
+        const int new_shift = shift - 10;
+        for (int b = tid; b < H2; b += PB) {
+          hmass[b] = 0ull;
+          hcnt[b] = 0u;
+          hbefore[b] = 0u;
+        }
+        bar();
+        strided_pass(z, 0, V, [&](int i, float v) {
+          const unsigned int key = f2key(v);
+          if ((key >> shift) == prefix) {
+            const unsigned int b = (key >> new_shift) & (H2 - 1);
+            atomicAdd(&hmass[b], to_fix(__expf(v - c.zmax)));
+            atomicAdd(&hcnt[b], 1u);
+            if (i < i0) atomicAdd(&hbefore[b], 1u);
+          }
+        });
+        bar();
+        const int b = crossing_bin(hmass, hcnt, H2, Pr, red64, &s_low, &s_above, &above);
+        Pr -= above;
+        if (pass == 1) {
+          cut_count = hcnt[b];
+          tie_before = hbefore[b];
+        }
+        prefix = (prefix << 10) | (unsigned int)b;
+        shift = new_shift;
+      }
+      c.cut = prefix;
+      // the t-th tie at the cut (0-based, ids ascending) has mass above + t * ecut before it
+      const u64 ecut = to_fix(__expf(key2f(c.cut) - c.zmax));
+      const u64 nt = ecut ? Pr / ecut + 1ull : (u64)cut_count;
+      c.ties_kept = nt < cut_count ? (unsigned int)nt : cut_count;
+      c.rank_ties = c.ties_kept < cut_count;
+      // kept: the top-p prefix if its last key passes min-p, else the min-p set
+      W = key2f(c.cut) - c.zmax >= c.ln_min_p ? (P - Pr) + (u64)c.ties_kept * ecut : smass;
+    }
+  }
+
+  // ---- keep mask and probabilities of the chunk ----
+  const float inv = (float)((double)FIX_SCALE / (double)W);
+  constexpr u64 MASK41 = (1ull << 41) - 1ull;
+  uint8_t* keep = p.keep ? p.keep + (int64_t)row * V : nullptr;
+  float* probs = p.probs ? p.probs + (int64_t)row * V : nullptr;
+  if (fast) {
+    // the kept members list[0, n_K) as (id << 41) | mass (mass <= 2^40)
+    for (int j = tid; j < n_K; j += PB) {
+      const u64 e = list[j];
+      list[j] = ((u64)(unsigned int)sk_id(e) << 41) | to_fix(__expf(key2f(sk_key(e)) - c.zmax));
+    }
+    bar();
+  }
+  // ---- token, when the kept set is listed: the smallest id whose inclusive kept mass exceeds u * W ----
+  const u64 target = p.token ? (u64)((double)p.u[row] * (double)W) : 0ull;
+  if (fast && p.token) {
+    // kept mass below the chunk and inside it, and the last kept id; the one
+    // workgroup whose chunk holds the crossing (or the last kept id, when
+    // rounding leaves no mass above the target) searches its members
+    u64 below = 0, inside = 0;
+    int last = -1;
+    for (int j = tid; j < n_K; j += PB) {
+      const int id = (int)(list[j] >> 41);
+      const u64 e = list[j] & MASK41;
+      below += id < i0 ? e : 0ull;
+      inside += id >= i0 && id < i1 ? e : 0ull;
+      last = max(last, id);
+    }
+    below = wave_reduce(below, OpAdd());
+    inside = wave_reduce(inside, OpAdd());
+    last = wave_reduce(last, OpMaxI());
+    if (lane == 0) {
+      red64[wave] = below;
+      red64b[wave] = inside;
+      redu[wave] = (unsigned int)(last + 1);
+    }
+    bar();
+    below = inside = 0;
+    last = -1;
+    for (int w = 0; w < NW; ++w) {
+      below += red64[w];
+      inside += red64b[w];
+      last = max(last, (int)redu[w] - 1);
+    }
+    const bool cross = below <= target && target < below + inside;
+    const bool at_end = target >= W && last >= i0 && last < i1;
+    if (at_end && tid == 0) p.token[row] = last;
+    if (cross) {   // workgroup-uniform
+      if (tid == 0) {
+        s_tok = INT_MAX;
+        s_n = 0u;
+      }
+      bar();
+      // the chunk's members, compacted (the whole list is searched if they do not fit)
+      constexpr int SMALL = H1 / 2;
+      u64* small = reinterpret_cast<u64*>(hcnt);
+      for (int j = tid; j < n_K; j += PB) {
+        const int id = (int)(list[j] >> 41);
+        if (id >= i0 && id < i1) {
+          const unsigned int slot = atomicAdd(&s_n, 1u);
+          if (slot < (unsigned int)SMALL) small[slot] = list[j];
+        }
+      }
+      bar();
+      const bool fits = s_n <= (unsigned int)SMALL;
+      const u64* src = fits ? small : list;
+      const int nsrc = fits ? (int)s_n : n_K;
+      // member t: kept mass before it = below + chunk members with smaller ids
+      for (int j = tid; j < nsrc; j += PB) {
+        const int id = (int)(src[j] >> 41);
+        if (id < i0 || id >= i1) continue;
+        u64 pre = below;
+        for (int q0 = 0; q0 < nsrc; q0 += 8) {
+          u64 e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) e[q] = q0 + q < nsrc ? src[q0 + q] : ~0ull;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int idq = (int)(e[q] >> 41);
+            pre += e[q] != ~0ull && idq >= i0 && idq < id ? e[q] & MASK41 : 0ull;
+          }
+        }
+        if (pre <= target && pre + (src[j] & MASK41) > target) s_tok = id;   // exactly one member
+      }
+      bar();   // also: the count array is free again for the chunk bitmap
+      if (tid == 0 && s_tok != INT_MAX) p.token[row] = s_tok;
+    }
+  }
+  if ((keep || probs) && fast && i1 - i0 <= H1 * 32) {
+    // mark the chunk's kept ids in an LDS bitmap (the count array is free) and
+    // read z only at kept ids
+    unsigned int* kbits = hcnt;
+    const int nwords = (i1 - i0 + 31) / 32;
+    for (int w = tid; w < nwords; w += PB) kbits[w] = 0u;
+    bar();
+    for (int j = tid; j < n_K; j += PB) {
+      const int id = (int)(list[j] >> 41);
+      if (id >= i0 && id < i1) atomicOr(&kbits[(id - i0) >> 5], 1u << ((id - i0) & 31));
+    }
+    bar();
+    // 4 ids per store when the rows allow it (chunk bounds are then multiples of 4)
+    const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(p.keep) & 3) == 0 &&
+                     (reinterpret_cast<uintptr_t>(p.probs) & 15) == 0;
+    if (vec) {
+      for (int g = i0 + 4 * tid; g < i1; g += 4 * PB) {
+        const unsigned int kb = (kbits[(g - i0) >> 5] >> ((g - i0) & 31)) & 0xfu;
+        if (keep)
+          *reinterpret_cast<unsigned int*>(keep + g) =
+              (kb & 1u) | ((kb >> 1) & 1u) << 8 | ((kb >> 2) & 1u) << 16 | ((kb >> 3) & 1u) << 24;
+        if (probs) {
+          f32x4 pr = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (kb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if ((kb >> q) & 1u) pr[q] = __expf(z[g + q] - c.zmax) * inv;
+          }
+          *reinterpret_cast<f32x4*>(probs + g) = pr;
+        }
+      }
+    } else {
+      for (int i = i0 + tid; i < i1; i += PB) {
+        const bool k = (kbits[(i - i0) >> 5] >> ((i - i0) & 31)) & 1u;
+        if (keep) keep[i] = (uint8_t)k;
+        if (probs) probs[i] = k ? __expf(z[i] - c.zmax) * inv : 0.f;
+      }
+    }
+  } else if (keep || probs) {
+    unsigned int tie_run = tie_before;
+    for (int s0 = i0; s0 < i1; s0 += SUBC) {
+      float v[RPT];
+      load_run(z, s0, i1, v);
+      unsigned int tie_i = c.rank_ties ? wave_tie_base(v, s0, i1, c.cut, redu, tie_run) : 0u;
+#pragma unroll
+      for (int e = 0; e < RPT; ++e) {
+        const int i = seg_id(s0, e);
+        const bool valid = i < i1;
+        const bool k = keep_step(c, v[e], valid, tie_i);
+        if (valid && keep) keep[i] = (uint8_t)k;
+        if (valid && probs) probs[i] = k ? __expf(v[e] - c.zmax) * inv : 0.f;
       }
     }
   }
-  // keep mask and kept mass; ties are ranked by id (per-wave counts, then ballots)
-  float wsum = 0.f;
-  unsigned int tie_run = tie_before;
-  for (int s0 = i0; s0 < i1; s0 += SUBC) {
-    if (s0 != i0) load_run(z, s0, i1, v);
-    unsigned int tie_i = c.rank_ties ? wave_tie_base(v, s0, i1, c.cut, redu, tie_run) : 0u;
-#pragma unroll
-    for (int e = 0; e < RPT; ++e) {
-      const int i = seg_id(s0, e);
-      const bool valid = i < i1;
-      const bool k = keep_step(c, v[e], valid, tie_i);
-      if (valid && p.keep) p.keep[(int64_t)row * p.V + i] = (uint8_t)k;
-      wsum += k ? __expf(v[e] - c.zmax) : 0.f;
-    }
-  }
-  wsum = block_sum(wsum, redf);
-  if (tid == 0) ws.km[row * NBR_MAX + blockIdx.x] = wsum;
-}
+  if (!p.token || fast) return;
 
-// ---- pass 5: probabilities and the token ----
-__global__ __launch_bounds__(PB) void pen_probs_kernel(const PenaltyParams p, int nb) {
-  __shared__ float redf[NW];
-  __shared__ unsigned int redu[NW];
-  __shared__ float s_km[NBR_MAX];
-  __shared__ int s_tok, s_last;
-  const int row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const PenWs ws = carve(p.ws, p.rows);
-  int i0, i1;
-  chunk_of(p.V, nb, blockIdx.x, &i0, &i1);
-  const float* z = p.logits_out + (int64_t)row * p.V;
-  float v[RPT];
-  load_run(z, i0, i1, v);   // the first sub-chunk, in flight with what follows
-  Cut c;
-  c.all_top = p.top_p >= 1.0f;
-  c.ln_min_p = logf(p.min_p);
-  c.cut = c.all_top ? 0u : ws.cut[row * 4 + 0];
-  c.ties_kept = c.all_top ? 0u : ws.cut[row * 4 + 1];
-  c.rank_ties = !c.all_top && c.ties_kept < ws.cut[row * 4 + 2];
-  unsigned int tie_run = c.rank_ties ? ws.tie0[row * NBR_MAX + blockIdx.x] : 0u;
-  if (tid < nb) s_km[tid] = ws.km[row * NBR_MAX + tid];
+  // radix-select path: the first workgroup scans the whole row, ids ascending
+  if (blockIdx.x != 0) return;
   if (tid == 0) {
     s_tok = INT_MAX;
-    s_last = -1;
+    s_lastkept = -1;
   }
-  c.zmax = row_max(ws, row, nb, redf);   // its barriers also publish s_km
-  float S = 0.f, wbase = 0.f;   // row kept mass, kept mass of earlier chunks (fixed order)
-  int last_chunk = -1;          // last chunk with kept mass
-  for (int b = 0; b < nb; ++b) {
-    if (b < (int)blockIdx.x) wbase += s_km[b];
-    S += s_km[b];
-    if (s_km[b] > 0.f) last_chunk = b;
-  }
-  const float inv = 1.0f / S;
-  const float target = p.u ? p.u[row] * S : 0.f;
-  const float my = s_km[blockIdx.x];
-  // the chunk whose kept-mass range holds the target searches it; if rounding
-  // put the target at or past the total, the last kept id is the token
-  const bool mine = p.token && ((target >= wbase && target < wbase + my) ||
-                                (target >= S && (int)blockIdx.x == last_chunk));
-  float run = wbase;
-  bool found = false;
-  for (int s0 = i0; s0 < i1; s0 += SUBC) {
-    if (s0 != i0) load_run(z, s0, i1, v);
-    unsigned int tie_i = c.rank_ties ? wave_tie_base(v, s0, i1, c.cut, redu, tie_run) : 0u;
-    float ev[RPT];
-    float esum = 0.f;
+  bar();
+  u64 run = 0;
+  unsigned int tie_run = 0;
+  for (int s0 = 0; s0 < V; s0 += SUBC) {
+    float v[RPT];
+    load_run(z, s0, V, v);
+    unsigned int tie_i = c.rank_ties ? wave_tie_base(v, s0, V, c.cut, redu, tie_run) : 0u;
+    u64 ev[RPT];
+    u64 esum = 0;
     int last_kept = -1;
 #pragma unroll
     for (int e = 0; e < RPT; ++e) {
       const int i = seg_id(s0, e);
-      const bool valid = i < i1;
-      const bool k = keep_step(c, v[e], valid, tie_i);
-      ev[e] = k ? __expf(v[e] - c.zmax) : 0.f;
-      if (valid && p.probs) p.probs[(int64_t)row * p.V + i] = ev[e] * inv;
+      const bool k = keep_step(c, v[e], i < V, tie_i);
+      ev[e] = k ? to_fix(__expf(v[e] - c.zmax)) : 0ull;
       esum += ev[e];
       if (k) last_kept = i;
     }
-    if (mine && !found) {   // block-uniform: inverse CDF over this sub-chunk, ids ascending
-      for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);
-      if (lane == 0) redf[wave] = esum;
-      __syncthreads();
-      float acc = run, tot = 0.f;
-      for (int w = 0; w < NW; ++w) {
-        if (w < wave) acc += redf[w];
-        tot += redf[w];
-      }
-      __syncthreads();
-      int hit = INT_MAX;
-#pragma unroll
-      for (int e = 0; e < RPT; ++e) {
-        float incl = ev[e];   // inclusive prefix over the step's lanes
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(incl, off);
-          if (lane >= off) incl += y;
-        }
-        const unsigned long long h = __ballot(ev[e] > 0.f && acc + incl > target);
-        if (h && hit == INT_MAX) hit = seg_id(s0, e) - lane + __ffsll((long long)h) - 1;
-        acc += __shfl(incl, 63);
-      }
-      if (lane == 0 && hit != INT_MAX) atomicMin(&s_tok, hit);
-      if (last_kept >= 0) atomicMax(&s_last, last_kept);
-      __syncthreads();
-      run += tot;
-      found = s_tok != INT_MAX;
-      __syncthreads();
+    for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);
+    if (lane == 0) red64[wave] = esum;
+    bar();
+    u64 acc = run, tot = 0;
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) acc += red64[w];
+      tot += red64[w];
     }
+    bar();
+    int hit = INT_MAX;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      u64 incl = ev[e];   // inclusive prefix over the step's lanes
+      for (int off = 1; off < 64; off <<= 1) {
+        const u64 y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const u64 h = __ballot(ev[e] > 0ull && acc + incl > target);
+      if (h && hit == INT_MAX) hit = seg_id(s0, e) - lane + __ffsll((long long)h) - 1;
+      acc += __shfl(incl, 63);
+    }
+    if (lane == 0 && hit != INT_MAX) atomicMin(&s_tok, hit);
+    if (last_kept >= 0) atomicMax(&s_lastkept, last_kept);
+    bar();
+    run += tot;
+    const bool found = s_tok != INT_MAX;
+    bar();
+    if (found) break;
   }
-  if (mine && tid == 0) p.token[row] = s_tok != INT_MAX ? s_tok : s_last;
+  if (tid == 0) p.token[row] = s_tok != INT_MAX ? s_tok : s_lastkept;
 }
 
 }  // namespace
-
-int penalty_blocks_per_row(int32_t rows, int32_t V) {
-  int nb = (256 + rows - 1) / rows;         // about one workgroup per compute unit over all rows
-  const int by_ids = (V + 4095) / 4096;     // at least 4096 ids per workgroup
-  if (nb > by_ids) nb = by_ids;
-  if (nb > NBR_MAX) nb = NBR_MAX;
-  if (nb < 1) nb = 1;
-  return nb;
-}
 
 size_t penalty_workspace_bytes(int32_t rows, int32_t V) { return pen_ws_bytes(rows, V); }
 
@@ -684,12 +1023,7 @@ hipError_t launch_penalty(const PenaltyParams& p, hipStream_t stream) {
   const int nb = penalty_blocks_per_row(p.rows, p.V);
   const dim3 grid(nb, p.rows);
   hipLaunchKernelGGL(pen_z_kernel, grid, dim3(PB), 0, stream, p, nb);
-  if (p.top_p < 1.0f) {
-    hipLaunchKernelGGL(pen_hist_kernel, grid, dim3(PB), 0, stream, p, nb);
-    hipLaunchKernelGGL(pen_cutbin_kernel, grid, dim3(PB), 0, stream, p, nb);
-  }
-  hipLaunchKernelGGL(pen_keep_kernel, grid, dim3(PB), 0, stream, p, nb);
-  if (p.probs || p.token) hipLaunchKernelGGL(pen_probs_kernel, grid, dim3(PB), 0, stream, p, nb);
+  if (p.keep || p.probs || p.token) hipLaunchKernelGGL(pen_out_kernel, grid, dim3(PB), 0, stream, p, nb);
   return hipGetLastError();
 }
 

@@ -54,7 +54,9 @@ def test_workspace_queries_depend_on_shapes_only():
     assert L.ts_verify_attn_workspace_size(100_000, 65, 32, 8, 128, 0) == 0   # unsupported -> 0
     assert L.ts_draft_attn_workspace_size(4164, 4, 32, 8, 128, 0) == L.ts_verify_attn_workspace_size(4164, 4, 32, 8, 128, 0)
     assert L.ts_partial_kv_select_workspace_size(100_000, 24, 32, 8, 128, 4096) >= 8 * 100_000 * 4
-    assert L.ts_penalty_sample_workspace_size(28, 128256) >= 28 * 128256 * 4   # per-row cut-bin lists
+    # chunk partials plus 1024 candidate keys (8 bytes) per chunk; 28 rows -> 9 chunks per row
+    assert L.ts_penalty_sample_workspace_size(28, 128256) >= 28 * 9 * 1024 * 8
+    assert L.ts_penalty_sample_workspace_size(1, 262144) >= 64 * 1024 * 8
 
 
 def _verify(L, **kw):
