@@ -9,21 +9,25 @@
 // sink U selected U recent.
 //
 // Kernels (one stream, in order):
-//   1. prologue  grid Hkv:  qbar_g in fp32; clear the head's histogram.
+//   1. prologue  grid Hkv:  qbar_g in fp32; clear the head's histograms.
 //   2. score     grid (chunks, Hkv): one HBM pass over K. 16 lanes x 16 B per
 //                row (d=128), lane-local FMAs then a 16-lane reduction; the
 //                block also histograms the top 12 bits of each candidate's
 //                order-preserving key and adds its non-empty bins to the
 //                head's global histogram.
 //   3. cutbin    grid (nb, Hkv): every block finds the top-12-bit bin holding
-//                the B'-th key, lists its chunk's keys in that bin and counts
-//                its keys in higher bins.
-//   4. emit      grid (nb, Hkv): every block refines the lists to the exact
-//                cut (two more radix digits), counts the rows taken by earlier
-//                blocks, writes its selected rows in ascending order and
-//                copies their K and V rows into the partial cache; block 0
-//                also copies the sink and recent rows.
+//                the B'-th key, lists its chunk's keys in that bin, counts its
+//                keys in higher bins and adds the next 10 bits of its listed
+//                keys to the head's second-digit histogram; the blocks also
+//                share out the -1 padding of sel_idx and the copies of the
+//                sink and recent rows.
+//   4. emit      grid (nb, Hkv): every block takes the second digit from that
+//                histogram and the last one from the lists (exact cut), counts
+//                the rows taken by earlier blocks, writes its selected rows in
+//                ascending order and copies their K and V rows into the
+//                partial cache.
 // Passes 3 and 4 read the L2-resident scores, not K.
+#include "ts_device.h"
 #include "ts_internal.h"
 
 #include <cmath>
@@ -36,6 +40,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int HIST1_BITS = 12;
 constexpr int HIST1 = 1 << HIST1_BITS;  // bins of the first radix digit
+constexpr int HIST2_BITS = 10;
+constexpr int HIST2 = 1 << HIST2_BITS;  // bins of the second and third digits
 // Order-preserving map from float to uint32 (larger float -> larger key).
 __device__ inline unsigned int f2key(float f) {
   const unsigned int u = __float_as_uint(f);
@@ -55,7 +61,8 @@ __device__ inline unsigned int popc64(unsigned long long x) { return (unsigned i
 // Each thread sums 8 channels of every 256/(D/8)-th row, then an LDS
 // reduction over the row slots (fixed order: deterministic).
 template <int D>
-__global__ __launch_bounds__(256) void select_prologue_kernel(const SelectParams p, unsigned int* hist) {
+__global__ __launch_bounds__(256) void select_prologue_kernel(const SelectParams p, unsigned int* hist,
+                                                              unsigned int* hist2) {
   constexpr int LPR = D / 8;          // lanes per row
   constexpr int RS = 256 / LPR;       // row slots
   __shared__ float part[RS][D];
@@ -84,6 +91,7 @@ __global__ __launch_bounds__(256) void select_prologue_kernel(const SelectParams
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[rs][cg * 8 + e] = acc[e];
   for (int b = tid; b < HIST1; b += 256) hist[g * HIST1 + b] = 0u;
+  for (int b = tid; b < HIST2; b += 256) hist2[g * HIST2 + b] = 0u;
   __syncthreads();
   if (tid < D) {
     float t = 0.f;
@@ -236,6 +244,8 @@ __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const Selec
 
 // Workspace after the scores and qbar (all 256-byte aligned):
 //   hist   [Hkv][HIST1]     first-digit histogram (filled by the scoring pass)
+//   hist2  [Hkv][HIST2]     second-digit histogram of the cut bin's keys
+//   cut1   [Hkv][2]         the cut bin of the first digit and the keys above it
 //   ccnt   [Hkv][NB_MAX][2] per block: cut-bin keys collected, keys in higher bins
 //   cand   [Hkv][n_ctx]     the cut-bin keys, block b's at its chunk's rows
 constexpr int NB_MAX = 64;   // blocks per head in the parallel passes
@@ -245,6 +255,8 @@ __host__ __device__ inline size_t round256(size_t x) { return (x + 255) / 256 * 
 
 struct SelWs {
   unsigned int* hist;
+  unsigned int* hist2;
+  unsigned int* cut1;
   unsigned int* ccnt;
   unsigned int* cand;
 };
@@ -254,6 +266,10 @@ __host__ __device__ inline SelWs carve(int32_t* base, int Hkv, int n_ctx) {
   SelWs s;
   s.hist = reinterpret_cast<unsigned int*>(w);
   w += round256((size_t)Hkv * HIST1 * 4);
+  s.hist2 = reinterpret_cast<unsigned int*>(w);
+  w += round256((size_t)Hkv * HIST2 * 4);
+  s.cut1 = reinterpret_cast<unsigned int*>(w);
+  w += round256((size_t)Hkv * 2 * 4);
   s.ccnt = reinterpret_cast<unsigned int*>(w);
   w += round256((size_t)Hkv * NB_MAX * 2 * 4);
   s.cand = reinterpret_cast<unsigned int*>(w);
@@ -262,8 +278,8 @@ __host__ __device__ inline SelWs carve(int32_t* base, int Hkv, int n_ctx) {
 }
 
 size_t sel_ws_bytes(int Hkv, int n_ctx) {
-  return round256((size_t)Hkv * HIST1 * 4) + round256((size_t)Hkv * NB_MAX * 2 * 4) +
-         round256((size_t)Hkv * (n_ctx > 0 ? n_ctx : 1) * 4);
+  return round256((size_t)Hkv * HIST1 * 4) + round256((size_t)Hkv * HIST2 * 4) + round256((size_t)Hkv * 2 * 4) +
+         round256((size_t)Hkv * NB_MAX * 2 * 4) + round256((size_t)Hkv * (n_ctx > 0 ? n_ctx : 1) * 4);
 }
 
 // Block-wide exclusive scan over NT threads; returns the prefix and the total.
@@ -351,19 +367,56 @@ __device__ inline void load_keys(const float* sc, int j0, int c1, unsigned int (
   for (int e = 0; e < RPT; ++e) key[e] = f2key(v[e]);
 }
 
-// Pass 1 of the selection: the first-digit bin holding the B'-th key (from the
-// scoring histogram; every block finds the same one) and the collection of
-// that bin's keys of the block's chunk into cand[g] at the chunk's own rows
-// (unordered: they are only counted later). The slots come from an LDS
-// counter, so no global atomic is contended.
+constexpr int CAND_CAP = 8192;   // cut-bin keys refined in LDS (more are refined from L2)
+
+// Copy rows of K and V of head g into the partial cache: item i of `n` is
+// 16-byte chunk i % RCH of pair i / RCH, pairs (src, dst) given by `pair`.
+// Items item0, item0 + stride, ... are this thread's; CP of them are in
+// flight together (loads first, then stores).
+template <int D, typename F>
+__device__ inline void copy_rows(const SelectParams& p, int g, int n, int item0, int stride, F&& pair) {
+  constexpr int NCH = D / 8, RCH = 2 * NCH, CP = 16;
+  for (int base = item0; base < n * RCH; base += stride * CP) {
+    u32x4 val[CP];
+    uint16_t* dst[CP];
+#pragma unroll
+    for (int u = 0; u < CP; ++u) {
+      const int id = base + u * stride;
+      dst[u] = nullptr;
+      if (id < n * RCH) {
+        int src_row, dst_row;
+        pair(id / RCH, &src_row, &dst_row);
+        const int c = id % RCH;
+        const bool is_v = c >= NCH;
+        const int ch = is_v ? c - NCH : c;
+        const uint16_t* src = (is_v ? p.v : p.k) + (int64_t)g * p.s_head + (int64_t)src_row * p.s_pos + ch * 8;
+        dst[u] = (is_v ? p.v_part : p.k_part) + (int64_t)g * p.sp_head + (int64_t)dst_row * p.sp_pos + ch * 8;
+        val[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CP; ++u)
+      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
+  }
+}
+
+// Pass 1 of the selection. Every block of a head: the first-digit bin holding
+// the B'-th key (from the scoring histogram; every block finds the same one),
+// the list of its chunk's keys in that bin in cand[g] at the chunk's own rows
+// (unordered; slots from an LDS counter, so no global atomic is contended),
+// its count of keys in higher bins, and the next 10 bits of its listed keys
+// added to the head's second-digit histogram. The blocks of a head also share
+// out the -1 padding of sel_idx and the copies of the sink and recent rows,
+// which do not depend on the cut.
+template <int D>
 __global__ __launch_bounds__(PT) void select_cutbin_kernel(const SelectParams p, int nb) {
   __shared__ __attribute__((aligned(16))) unsigned int hist[HIST1];
+  __shared__ unsigned int h2[HIST2];
   __shared__ unsigned int tmp[PT / 64];
   __shared__ int s_bin;
   __shared__ unsigned int s_above, s_n, s_hi;
   const int g = blockIdx.y;
   const unsigned int k = (unsigned int)p.b_eff;
-  if (k == 0) return;
   const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
   const int tid = threadIdx.x, lane = tid & 63;
   int c0, c1;
@@ -372,12 +425,53 @@ __global__ __launch_bounds__(PT) void select_cutbin_kernel(const SelectParams p,
   unsigned int* cand = ws.cand + (int64_t)g * p.n_ctx + c0;
   // the first sub-chunk's keys are loaded together with the histogram
   unsigned int key[RPT];
-  load_keys(sc, c0 + RPT * tid, c1, key);
-  load_hist<PT>(hist, ws.hist + g * HIST1);
+  if (k > 0) {
+    load_keys(sc, c0 + RPT * tid, c1, key);
+    load_hist<PT>(hist, ws.hist + g * HIST1);
+  }
+  for (int b = tid; b < HIST2; b += PT) h2[b] = 0u;
   if (tid == 0) s_n = s_hi = 0;
-  __syncthreads();
+  // padding and sink / recent copies, strided over the head's blocks: every
+  // thread's first 16-byte item is loaded now and stored at the end, so its
+  // latency hides behind the pass; further items (long sink / recent ranges)
+  // are copied at the end
+  int32_t* out = p.sel_idx + (int64_t)g * p.budget;
+  for (int i = (int)k + blockIdx.x * PT + tid; i < p.budget; i += nb * PT) out[i] = -1;
+  const int n_sink_eff = min(p.n_sink, p.n_ctx);
+  const int rec_lo = max(p.n_sink, p.n_ctx - p.n_recent);
+  const int n_copy = n_sink_eff + (p.n_ctx - rec_lo > 0 ? p.n_ctx - rec_lo : 0);
+  auto pair = [&](int r, int* src, int* dst) {
+    *src = r < n_sink_eff ? r : rec_lo + (r - n_sink_eff);
+    *dst = r < n_sink_eff ? r : n_sink_eff + (int)k + (r - n_sink_eff);
+  };
+  const int item0 = blockIdx.x * PT + tid, stride = nb * PT;
+  u32x4 first_v = {0u, 0u, 0u, 0u};
+  uint16_t* first_dst = nullptr;
+  {
+    constexpr int NCH = D / 8, RCH = 2 * NCH;
+    if (item0 < n_copy * RCH) {
+      int src_row, dst_row;
+      pair(item0 / RCH, &src_row, &dst_row);
+      const int c = item0 % RCH;
+      const bool is_v = c >= NCH;
+      const int ch = is_v ? c - NCH : c;
+      first_v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          (is_v ? p.v : p.k) + (int64_t)g * p.s_head + (int64_t)src_row * p.s_pos + ch * 8));
+      first_dst = (is_v ? p.v_part : p.k_part) + (int64_t)g * p.sp_head + (int64_t)dst_row * p.sp_pos + ch * 8;
+    }
+  }
+  auto finish_copies = [&]() {
+    if (first_dst) *reinterpret_cast<u32x4*>(first_dst) = first_v;
+    copy_rows<D>(p, g, n_copy, item0 + stride, stride, pair);
+  };
+  if (k == 0) {
+    finish_copies();
+    return;
+  }
+  bar();
   find_bin<PT>(hist, HIST1, k, tmp, &s_bin, &s_above);
   const unsigned int bin = (unsigned int)s_bin;
+  constexpr int SH2 = 32 - HIST1_BITS - HIST2_BITS;
   unsigned int n_hi = 0;   // this thread's keys in higher first-digit bins
   for (int s0 = c0; s0 < c1; s0 += SUB) {
     const int j0 = s0 + RPT * tid;
@@ -402,93 +496,69 @@ __global__ __launch_bounds__(PT) void select_cutbin_kernel(const SelectParams p,
     if (nc) {
 #pragma unroll
       for (int e = 0; e < RPT; ++e)
-        if (j0 + e < c1 && (key[e] >> (32 - HIST1_BITS)) == bin) cand[base++] = key[e];
+        if (j0 + e < c1 && (key[e] >> (32 - HIST1_BITS)) == bin) {
+          cand[base++] = key[e];
+          atomicAdd(&h2[(key[e] >> SH2) & (HIST2 - 1)], 1u);
+        }
     }
   }
-  for (int m = 32; m >= 1; m >>= 1) n_hi += __shfl_xor(n_hi, m);
+  n_hi = wave_reduce(n_hi, OpAdd());
   if (lane == 0) atomicAdd(&s_hi, n_hi);
-  __syncthreads();
+  bar();
+  for (int b = tid; b < HIST2; b += PT) {
+    const unsigned int c = h2[b];
+    if (c) atomicAdd(&ws.hist2[g * HIST2 + b], c);
+  }
   if (tid == 0) {
     ws.ccnt[(g * NB_MAX + blockIdx.x) * 2 + 0] = s_n;
     ws.ccnt[(g * NB_MAX + blockIdx.x) * 2 + 1] = s_hi;
-  }
-}
-
-constexpr int CAND_CAP = 8192;   // cut-bin keys refined in LDS (more are refined from L2)
-
-// Copy rows of K and V of head g into the partial cache: item i of `n` is
-// 16-byte chunk i % RCH of pair i / RCH, pairs (src, dst) given by `pair`.
-// CP copies per thread are in flight together (loads first, then stores).
-template <int D, typename F>
-__device__ inline void copy_rows(const SelectParams& p, int g, int n, F&& pair) {
-  constexpr int NCH = D / 8, RCH = 2 * NCH, CP = 16;
-  for (int base = threadIdx.x; base < n * RCH; base += PT * CP) {
-    u32x4 val[CP];
-    uint16_t* dst[CP];
-#pragma unroll
-    for (int u = 0; u < CP; ++u) {
-      const int id = base + u * PT;
-      dst[u] = nullptr;
-      if (id < n * RCH) {
-        int src_row, dst_row;
-        pair(id / RCH, &src_row, &dst_row);
-        const int c = id % RCH;
-        const bool is_v = c >= NCH;
-        const int ch = is_v ? c - NCH : c;
-        const uint16_t* s = (is_v ? p.v : p.k) + (int64_t)g * p.s_head + (int64_t)src_row * p.s_pos + ch * 8;
-        dst[u] = (is_v ? p.v_part : p.k_part) + (int64_t)g * p.sp_head + (int64_t)dst_row * p.sp_pos + ch * 8;
-        val[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s));
-      }
+    if (blockIdx.x == 0) {
+      ws.cut1[g * 2 + 0] = bin;
+      ws.cut1[g * 2 + 1] = s_above;
     }
-#pragma unroll
-    for (int u = 0; u < CP; ++u)
-      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
   }
+  finish_copies();
 }
 
 // Pass 2: exact cut, ordered emission and gather; grid (nb, Hkv).
-// Every block of a head derives the same cut: the first-digit bin of the
-// B'-th key from the histogram, then two more radix digits (10 + 10 bits)
-// over the lists of that bin's keys (blocks' lists back to back, in LDS when
-// they fit) give the exact cut key and how many keys equal to it are taken
-// (the earliest rows). The rows above the cut and at the cut in earlier
-// blocks follow from those blocks' higher-bin counts and lists. Inside its
-// chunk, sub-chunks of SUB rows are ranked by one block scan (rows above and
-// at the cut, packed 16 + 16 bits), so selected rows come out ascending with
-// consecutive output slots; the block copies their K and V rows into the
-// partial cache. Block 0 also copies the sink and recent rows and pads
-// sel_idx with -1.
+// Every block of a head derives the same cut: the first-digit bin and the
+// count above it from pass 1, the second digit from the head's second-digit
+// histogram, and the last 10 bits from the lists of the first-digit bin's
+// keys (blocks' lists back to back, in LDS when they fit) give the exact cut
+// key and how many keys equal to it are taken (the earliest rows). The rows
+// above the cut and at the cut in earlier blocks follow from those blocks'
+// higher-bin counts and lists. Inside its chunk, sub-chunks of SUB rows are
+// ranked by one block scan (rows above and at the cut, packed 16 + 16 bits),
+// so selected rows come out ascending with consecutive output slots; the
+// block copies their K and V rows into the partial cache.
 template <int D>
 __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, int nb) {
-  __shared__ __attribute__((aligned(16))) unsigned int hist[HIST1];
+  __shared__ __attribute__((aligned(16))) unsigned int hist[HIST2];
   __shared__ unsigned int cand_l[CAND_CAP];
   __shared__ int srcs[SUB];
   __shared__ unsigned int tmp[PT / 64];
   __shared__ unsigned int seg_off[NB_MAX + 1], seg_c0[NB_MAX], seg_hi[NB_MAX];
   __shared__ int s_bin;
-  __shared__ unsigned int s_above, s_gt, s_tie;
+  __shared__ unsigned int s_above, s_gt, s_tie, s_bin1, s_above1;
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int k = p.b_eff;
   const int n_sink_eff = min(p.n_sink, p.n_ctx);
   int32_t* out = p.sel_idx + (int64_t)g * p.budget;
-  if (blockIdx.x == 0) {
-    for (int i = k + tid; i < p.budget; i += PT) out[i] = -1;
-    const int rec_lo = max(p.n_sink, p.n_ctx - p.n_recent);
-    const int n_rec = p.n_ctx - rec_lo > 0 ? p.n_ctx - rec_lo : 0;
-    copy_rows<D>(p, g, n_sink_eff + n_rec, [&](int r, int* src, int* dst) {
-      *src = r < n_sink_eff ? r : rec_lo + (r - n_sink_eff);
-      *dst = r < n_sink_eff ? r : n_sink_eff + k + (r - n_sink_eff);
-    });
-  }
-  if (k == 0) return;
   const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
   int c0, c1;
   chunk_of(p, nb, blockIdx.x, &c0, &c1);
   const float* sc = p.scores + (int64_t)g * p.n_ctx;
   unsigned int key[RPT];
   load_keys(sc, c0 + RPT * tid, c1, key);   // in flight with the loads below
-  load_hist<PT>(hist, ws.hist + g * HIST1);
+  {
+    constexpr int PER = HIST2 / 4 / PT;
+    u32x4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const u32x4*>(ws.hist2 + g * HIST2)[tid + i * PT];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) reinterpret_cast<u32x4*>(hist)[tid + i * PT] = v[i];
+  }
   if (tid < 64) {   // list offsets: one wave scans the per-block list lengths
     unsigned int c = 0;
     if (lane < nb) {
@@ -505,9 +575,13 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
     }
     if (lane < nb) seg_off[lane] = incl - c;
     if (lane == 63) seg_off[nb] = incl;
-    if (lane == 0) s_gt = s_tie = 0;
+    if (lane == 0) {
+      s_gt = s_tie = 0;
+      s_bin1 = ws.cut1[g * 2 + 0];
+      s_above1 = ws.cut1[g * 2 + 1];
+    }
   }
-  __syncthreads();
+  bar();
   const unsigned int n = seg_off[nb];
   const unsigned int* cand_g = ws.cand + (int64_t)g * p.n_ctx;
   auto seg_of = [&](unsigned int i) {   // list owning key i: the last b with seg_off[b] <= i
@@ -537,28 +611,23 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
         if (i0 + u * PT < n) cand_l[i0 + u * PT] = v[u];
     }
   }
-  __syncthreads();
-  find_bin<PT>(hist, HIST1, (unsigned int)k, tmp, &s_bin, &s_above);
-  unsigned int prefix = (unsigned int)s_bin;
-  unsigned int rank = (unsigned int)k - s_above;   // rank of the cut key inside the bin, from the top
-  int shift = 32 - HIST1_BITS;
-  for (int pass = 0; pass < 2; ++pass) {
-    constexpr int nbits = 10, nbins = 1 << nbits;
-    __syncthreads();
-    for (int b = tid; b < nbins; b += PT) hist[b] = 0u;
-    __syncthreads();
-    const int new_shift = shift - nbits;
-    for (unsigned int i = tid; i < n; i += PT) {
-      const unsigned int kk = in_lds ? cand_l[i] : key_at(i);
-      if ((kk >> shift) == prefix) atomicAdd(&hist[(kk >> new_shift) & (nbins - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin<PT>(hist, nbins, rank, tmp, &s_bin, &s_above);
-    prefix = (prefix << nbits) | (unsigned int)s_bin;
-    rank -= s_above;
-    shift = new_shift;
+  // second digit from the head's histogram of the cut bin's keys
+  unsigned int rank = (unsigned int)k - s_above1;   // rank of the cut key inside the first-digit bin
+  find_bin<PT>(hist, HIST2, rank, tmp, &s_bin, &s_above);
+  unsigned int prefix = (s_bin1 << HIST2_BITS) | (unsigned int)s_bin;
+  rank -= s_above;
+  bar();   // every thread has read the histogram (and the lists are in LDS)
+  // last digit from the listed keys with that prefix
+  constexpr int SH = 32 - HIST1_BITS - HIST2_BITS;
+  for (int b = tid; b < HIST2; b += PT) hist[b] = 0u;
+  bar();
+  for (unsigned int i = tid; i < n; i += PT) {
+    const unsigned int kk = in_lds ? cand_l[i] : key_at(i);
+    if ((kk >> SH) == prefix) atomicAdd(&hist[kk & (HIST2 - 1)], 1u);
   }
-  const unsigned int cut = prefix, need = rank;
+  bar();
+  find_bin<PT>(hist, HIST2, rank, tmp, &s_bin, &s_above);
+  const unsigned int cut = (prefix << SH) | (unsigned int)s_bin, need = rank - s_above;
   // rows above / at the cut in earlier blocks: their higher-bin counts plus
   // their listed keys above / equal to the cut
   {
@@ -570,16 +639,14 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
       tie += kk == cut;
     }
     if (tid < (int)blockIdx.x) gt += seg_hi[tid];
-    for (int m = 32; m >= 1; m >>= 1) {
-      gt += __shfl_xor(gt, m);
-      tie += __shfl_xor(tie, m);
-    }
+    gt = wave_reduce(gt, OpAdd());
+    tie = wave_reduce(tie, OpAdd());
     if (lane == 0) {
       atomicAdd(&s_gt, gt);
       atomicAdd(&s_tie, tie);
     }
   }
-  __syncthreads();
+  bar();
   unsigned int gt_run = s_gt, tie_run = s_tie;
   for (int s0 = c0; s0 < c1; s0 += SUB) {
     const int j0 = s0 + RPT * tid;
@@ -613,12 +680,12 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
     gt_run += tot & 0xffffu;
     tie_run += tot >> 16;
     const unsigned int end = min(gt_run + min(tie_run, need), (unsigned int)k);
-    __syncthreads();
-    copy_rows<D>(p, g, (int)(end - base), [&](int i, int* src, int* dst) {
+    bar();
+    copy_rows<D>(p, g, (int)(end - base), tid, PT, [&](int i, int* src, int* dst) {
       *src = srcs[i];
       *dst = n_sink_eff + (int)base + i;
     });
-    __syncthreads();
+    bar();
   }
 }
 
@@ -647,9 +714,9 @@ size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv,
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
   if (p.d == 128)
-    hipLaunchKernelGGL(select_prologue_kernel<128>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist);
+    hipLaunchKernelGGL(select_prologue_kernel<128>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist, ws.hist2);
   else
-    hipLaunchKernelGGL(select_prologue_kernel<64>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist);
+    hipLaunchKernelGGL(select_prologue_kernel<64>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist, ws.hist2);
   if (p.n_ctx > 0) {
     // about one scoring workgroup per compute unit over all heads, at least
     // one 128-row tile each
@@ -662,14 +729,18 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
     else
       hipLaunchKernelGGL(select_score_kernel<64>, dim3(chunks, p.Hkv), dim3(SC_WAVES * 64), 0, stream, p, ws.hist, rpb);
   }
+  // the cut-bin pass always runs: it also pads sel_idx and copies the sink and recent rows
   const int nb = select_blocks_per_head(p.n_ctx, p.Hkv, p.n_sink, p.n_recent);
-  if (p.b_eff > 0) {
-    hipLaunchKernelGGL(select_cutbin_kernel, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
-  }
   if (p.d == 128)
-    hipLaunchKernelGGL(select_emit_kernel<128>, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
+    hipLaunchKernelGGL(select_cutbin_kernel<128>, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
   else
-    hipLaunchKernelGGL(select_emit_kernel<64>, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
+    hipLaunchKernelGGL(select_cutbin_kernel<64>, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
+  if (p.b_eff > 0) {
+    if (p.d == 128)
+      hipLaunchKernelGGL(select_emit_kernel<128>, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
+    else
+      hipLaunchKernelGGL(select_emit_kernel<64>, dim3(nb, p.Hkv), dim3(PT), 0, stream, p, nb);
+  }
   return hipGetLastError();
 }
 
