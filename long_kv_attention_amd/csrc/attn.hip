@@ -589,26 +589,22 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   }
 }
 
-// Log-sum-exp merge of the split partials. One row per block for d=128 (two
-// for d=64): 8 split groups x D/4 float4 lanes. Each thread merges its splits
-// in one pass (U splits' loads issued together, online max), then one LDS
-// round merges the 8 split groups in a fixed order (bitwise repeatable).
+// Log-sum-exp merge of the split partials: one wave per output row, no LDS.
+// Lane (sg, c4) holds float4 channel group c4 of the splits sg, sg + SG, ...
+// (SG = 64 / (d/4) split groups), merges them in one online pass with U
+// splits' loads in flight, then the split groups merge across lanes with the
+// gfx950 row / half swaps, in a fixed order (bitwise repeatable).
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int CG = D / 4;                 // float4 channel groups per row
-  constexpr int SG = 8;                     // split groups
-  constexpr int RPB = 256 / (CG * SG);      // rows per block
-  constexpr int U = 4;                      // splits in flight per thread
-  __shared__ float red_m[RPB][SG];
-  __shared__ float red_l[RPB][SG];
-  __shared__ f32x4 red_acc[RPB][SG][CG];
-  const int tid = threadIdx.x;
-  const int r_in = tid / (CG * SG);
-  const int sg = (tid / CG) % SG;
-  const int c4 = tid % CG;
+  constexpr int SG = 64 / CG;               // split groups per wave
+  constexpr int U = 8;                      // splits in flight per lane
+  static_assert(SG == 2 || SG == 4, "one row per wave");
+  const int lane = threadIdx.x & 63;
   const int nrows = p.Hkv * p.M;
-  const int row = blockIdx.x * RPB + r_in;   // g * M + r
-  const bool ok = row < nrows;
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);   // g * M + r
+  if (row >= nrows) return;   // wave-uniform
+  const int sg = lane / CG, c4 = lane % CG;
   const float c = p.scale_log2e;
   const int64_t sstride = nrows;
 
@@ -616,54 +612,54 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   // marks "no split here" and gets weight exp2(-inf) = 0.
   float m_loc = -INFINITY, l_loc = 0.f;
   f32x4 a_loc = {0.f, 0.f, 0.f, 0.f};
-  if (ok)
-    for (int s0 = sg; s0 < p.n_split; s0 += SG * U) {
-      float mv[U], lv[U];
-      f32x4 av[U];
+  for (int s0 = sg; s0 < p.n_split; s0 += SG * U) {
+    float mv[U], lv[U];
+    f32x4 av[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = s0 + u * SG;
-        const bool in = s < p.n_split;
-        const int64_t pr = (int64_t)(in ? s : s0) * sstride + row;
-        const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + pr * 2);
-        mv[u] = in ? ml.x : -INFINITY;
-        lv[u] = in ? ml.y : 0.f;
-        av[u] = *reinterpret_cast<const f32x4*>(p.part_acc + pr * D + 4 * c4);
-      }
-      float mn = m_loc;
-#pragma unroll
-      for (int u = 0; u < U; ++u) mn = fmaxf(mn, mv[u]);
-      const float sc = __builtin_amdgcn_exp2f((m_loc - mn) * c);   // 0 on the first round
-      l_loc *= sc;
-      a_loc *= sc;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = __builtin_amdgcn_exp2f((mv[u] - mn) * c);
-        l_loc += w * lv[u];
-        a_loc += w * av[u];
-      }
-      m_loc = mn;
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * SG;
+      const bool in = s < p.n_split;
+      const int64_t pr = (int64_t)(in ? s : s0) * sstride + row;
+      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + pr * 2);
+      mv[u] = in ? ml.x : -INFINITY;
+      lv[u] = in ? ml.y : 0.f;
+      av[u] = *reinterpret_cast<const f32x4*>(p.part_acc + pr * D + 4 * c4);
     }
-  red_acc[r_in][sg][c4] = a_loc;
-  if (c4 == 0) {
-    red_m[r_in][sg] = m_loc;
-    red_l[r_in][sg] = l_loc;
-  }
-  __syncthreads();
-  if (sg == 0 && ok) {
-    float mu = red_m[r_in][0];
+    float mn = m_loc;
 #pragma unroll
-    for (int q = 1; q < SG; ++q) mu = fmaxf(mu, red_m[r_in][q]);
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, mv[u]);
+    const float sc = __builtin_amdgcn_exp2f((m_loc - mn) * c);   // 0 on the first round
+    l_loc *= sc;
+    a_loc *= sc;
 #pragma unroll
-    for (int q = 0; q < SG; ++q) {
-      const float w = __builtin_amdgcn_exp2f((red_m[r_in][q] - mu) * c);
-      a += w * red_acc[r_in][q][c4];
-      l += w * red_l[r_in][q];
+    for (int u = 0; u < U; ++u) {
+      const float w = __builtin_amdgcn_exp2f((mv[u] - mn) * c);
+      l_loc += w * lv[u];
+      a_loc += w * av[u];
     }
-    *reinterpret_cast<f32x4*>(p.out + (int64_t)row * D + 4 * c4) = a * (1.0f / l);
+    m_loc = mn;
   }
+  // merge the split groups: lanes l and l ^ 32 (and l ^ 16 for d = 64)
+  auto merge = [&](auto swap) {
+    const auto mm = swap(__float_as_uint(m_loc));
+    const float m0 = __uint_as_float(mm[0]), m1 = __uint_as_float(mm[1]);
+    const float mu = fmaxf(m0, m1);
+    // the pair (lower group, upper group) in the same order in both lanes
+    const float w0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m0 - mu) * c);
+    const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mu) * c);
+    const auto ll = swap(__float_as_uint(l_loc));
+    l_loc = w0 * __uint_as_float(ll[0]) + w1 * __uint_as_float(ll[1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto aa = swap(__float_as_uint(a_loc[i]));
+      a_loc[i] = w0 * __uint_as_float(aa[0]) + w1 * __uint_as_float(aa[1]);
+    }
+    m_loc = mu;
+  };
+  if constexpr (SG == 4)
+    merge([](unsigned int x) { return __builtin_amdgcn_permlane16_swap(x, x, false, false); });
+  merge([](unsigned int x) { return __builtin_amdgcn_permlane32_swap(x, x, false, false); });
+  if (sg == 0) *reinterpret_cast<f32x4*>(p.out + (int64_t)row * D + 4 * c4) = a_loc * (1.0f / l_loc);
 }
 
 struct KernelChoice {
@@ -767,13 +763,11 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {
   const int nz = row_blocks_for(p.M);
   hipError_t e = p.d == 128 ? launch_split_d<128>(p, kc, nz, stream) : launch_split_d<64>(p, kc, nz, stream);
   if (e != hipSuccess || p.n_split == 1) return e;
-  if (p.d == 128) {
-    const int rpb = 1;
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3((p.Hkv * p.M + rpb - 1) / rpb), dim3(256), 0, stream, p);
-  } else {
-    const int rpb = 2;
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3((p.Hkv * p.M + rpb - 1) / rpb), dim3(256), 0, stream, p);
-  }
+  const dim3 cgrid((p.Hkv * p.M + 3) / 4);   // one row per wave, four waves per block
+  if (p.d == 128)
+    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
