@@ -79,7 +79,10 @@ struct Cfg {
   // barrier per tile; measured: T = 64 shapes -6%, no gain at RG = 2).
   static constexpr bool V_SHARED = RG >= 3;
   static constexpr int ANC_BYTES = 1024;  // ancestor words of the tree nodes (one full 64-lane copy)
-  static constexpr int MSLOT = 64 * CT * 16 + 2 * 16 * 4;   // one wave's O^T of a row tile + m, l
+  // At the end of a split each wave keeps the CT / PG channel tiles it merges
+  // and parks the others (and its m, l) for the waves that merge them.
+  static constexpr int CT_OUT = PG > 1 ? CT - CT / PG : CT;
+  static constexpr int MSLOT = 64 * CT_OUT * 16 + 2 * 16 * 4;   // one wave's parked O^T of a row tile + m, l
   static constexpr int MERGE_BYTES = PG * RG * MSLOT;
   static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES + ANC_BYTES;
   // row tiles merged per round at the end of a split (all of LDS is free then)
@@ -502,11 +505,11 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   for (int t = 0; t < TPW; ++t) l_run[t] = lsum[t][0];
 
   // ---- merge the PG position groups of each row group, then store ----
-  // Every wave parks its O^T fragments and (m, l) of MERGE_RT row tiles in
-  // LDS per round; wave (rg, pg) then merges channel tiles pg, pg + PG, ... of
-  // its row group over the PG slots and stores them: all waves share the merge
-  // and the stores. Output: normalised rows (single split) or the split's
-  // partial (O^T, m, l).
+  // Wave (rg, pg) merges and stores channel tiles pg, pg + PG, ... of its row
+  // group: it keeps those in registers and parks the other channel tiles and
+  // its (m, l) in LDS, MERGE_RT row tiles per round (all of LDS is free after
+  // the loop). Output: normalised rows (single split) or the split's partial
+  // (O^T, m, l).
   constexpr int CTW = C::CT / PG;   // channel tiles merged and stored per wave
   auto store = [&](int t, float mu, float wsum, const f32x4 (&om)[CTW]) {
     const int row = (rt0 + t) * 16 + l16;
@@ -537,7 +540,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     }
   } else {
     constexpr int RT = C::MERGE_RT;
-    constexpr int OFF_ML = 64 * C::CT * 16;   // m and l after the O^T fragments in a slot
+    constexpr int OFF_ML = 64 * C::CT_OUT * 16;   // m and l after the parked O^T fragments in a slot
 #pragma unroll
     for (int t0 = 0; t0 < TPW; t0 += RT) {
       // LDS-only barriers: the partial stores of the previous round may stay
@@ -548,8 +551,13 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         const int t = t0 + u;
         if (t >= TPW) break;
         unsigned char* my = lds + ((u * RG + rg) * PG + pg) * C::MSLOT;
+        // channel tiles of the other waves' share, in ascending order
 #pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) *reinterpret_cast<f32x4*>(my + (ct * 64 + lane) * 16) = o[t][ct];
+        for (int ct = 0; ct < C::CT; ++ct)
+          if (ct % PG != pg) {
+            const int pos = (ct / PG) * (PG - 1) + ct % PG - (ct % PG > pg ? 1 : 0);
+            *reinterpret_cast<f32x4*>(my + (pos * 64 + lane) * 16) = o[t][ct];
+          }
         if (kg == 0) {
           reinterpret_cast<float*>(my + OFF_ML)[l16] = m_run[t];
           reinterpret_cast<float*>(my + OFF_ML)[16 + l16] = l_run[t];
@@ -565,24 +573,33 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         float mu = NEG_BIG;
 #pragma unroll
         for (int q = 0; q < PG; ++q) {
-          mq[q] = reinterpret_cast<const float*>(grp + q * C::MSLOT + OFF_ML)[l16];
+          mq[q] = q == pg ? m_run[t] : reinterpret_cast<const float*>(grp + q * C::MSLOT + OFF_ML)[l16];
           mu = fmaxf(mu, mq[q]);
         }
         float wsum = 0.f;
 #pragma unroll
         for (int q = 0; q < PG; ++q) {
           wq[q] = __builtin_amdgcn_exp2f((mq[q] - mu) * c);
-          wsum += wq[q] * reinterpret_cast<const float*>(grp + q * C::MSLOT + OFF_ML)[16 + l16];
+          wsum += wq[q] * (q == pg ? l_run[t] : reinterpret_cast<const float*>(grp + q * C::MSLOT + OFF_ML)[16 + l16]);
         }
         f32x4 om[CTW];
 #pragma unroll
-        for (int i = 0; i < CTW; ++i) {
-          const int ct = pg + i * PG;
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < C::CT; ++ct)
+          if (ct % PG == pg) {
+            // in wave q's slot this channel tile sits after (ct / PG) * (PG - 1)
+            // tiles of earlier groups and the tiles pg' < pg, pg' != q, of its own group
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < PG; ++q) acc += wq[q] * *reinterpret_cast<const f32x4*>(grp + q * C::MSLOT + (ct * 64 + lane) * 16);
-          om[i] = acc;
-        }
+            for (int q = 0; q < PG; ++q) {
+              if (q == pg) {
+                acc += wq[q] * o[t][ct];
+              } else {
+                const int pos = (ct / PG) * (PG - 1) + pg - (q < pg ? 1 : 0);
+                acc += wq[q] * *reinterpret_cast<const f32x4*>(grp + q * C::MSLOT + (pos * 64 + lane) * 16);
+              }
+            }
+            om[ct / PG] = acc;
+          }
         store(t, mu, wsum, om);
       }
     }
