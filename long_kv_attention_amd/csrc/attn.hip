@@ -686,8 +686,12 @@ struct KernelChoice {
 constexpr int KV_TILE = 128;  // split granularity in positions (a multiple of every kernel's tile)
 
 // Row tiles per KV head -> (row groups, position groups, row tiles per wave).
-// Up to 8 row tiles the workgroup has 8 waves (two per SIMD, 128-position
-// tiles); every choice keeps the accumulators in registers without spilling.
+// From 4 row tiles on the workgroup has 8 waves (two per SIMD); every choice
+// keeps the accumulators in registers without spilling. Past 16 row tiles
+// the rows go to several workgroups (grid.z) of 12 or 16 row tiles, whichever
+// pads fewer. Measured at 100K: T = 48 (12 row tiles) 132 us with (4, 2, 3)
+// against 164 us with four waves (4, 1, 3); T = 64 (16) 154 against 185 us
+// with (4, 1, 4); 14B T = 64 (20) 214 against 240 us with (4, 1, 5).
 KernelChoice choose(int nrt) {
   if (nrt <= 1) return {1, 4, 1};
   if (nrt == 2) return {1, 4, 2};
@@ -696,9 +700,10 @@ KernelChoice choose(int nrt) {
   if (nrt <= 6) return {2, 4, 3};
   if (nrt <= 8) return {4, 2, 2};
   if (nrt == 9) return {3, 2, 3};
-  if (nrt <= 12) return {4, 1, 3};
-  if (nrt <= 16) return {4, 1, 4};
-  return {4, 1, 5};
+  if (nrt <= 12) return {4, 2, 3};
+  if (nrt <= 16) return {4, 2, 4};
+  const int pad3 = (nrt + 11) / 12 * 12, pad4 = (nrt + 15) / 16 * 16;
+  return pad3 < pad4 ? KernelChoice{4, 2, 3} : KernelChoice{4, 2, 4};
 }
 
 // K/V ring depth: three tiles (two in flight while one is computed), or two
@@ -723,9 +728,8 @@ hipError_t launch_split_d(const AttnParams& p, const KernelChoice& kc, int nz, h
   TS_CASE(2, 4, 3)
   TS_CASE(4, 2, 2)
   TS_CASE(3, 2, 3)
-  TS_CASE(4, 1, 3)
-  TS_CASE(4, 1, 4)
-  TS_CASE(4, 1, 5)
+  TS_CASE(4, 2, 3)
+  TS_CASE(4, 2, 4)
 #undef TS_CASE
   return hipErrorInvalidValue;
 }
