@@ -63,6 +63,7 @@ constexpr int SUBC = PB * RPT;          // ids per ordered sub-chunk (NW segment
 constexpr int CAP_B = 1024;             // candidates listed per chunk
 constexpr int SCAP = 4096;              // largest min-p set decided in LDS
 constexpr int UNR = 16;                 // loads per thread in flight in the strided passes
+constexpr int ZR = 32;                  // ids per thread held in registers in pass 1
 constexpr float FIX_SCALE = 1099511627776.0f;  // 2^40
 static_assert(SCAP == H1, "the sorted list and the first-digit mass histogram share LDS");
 static_assert(H2 % PB == 0 && H1 % PB == 0, "bins split evenly over the threads");
@@ -87,7 +88,9 @@ __host__ __device__ inline size_t round256(size_t x) { return (x + 255) / 256 * 
 }  // namespace
 
 int penalty_blocks_per_row(int32_t rows, int32_t V) {
-  int nb = 256 / rows;                      // at most one workgroup per compute unit over all rows
+  int nb = 256 / rows;                      // about one workgroup per compute unit over all rows,
+  const int by_regs = (V + ZR * PB - 1) / (ZR * PB);   // but chunks small enough for the register path
+  if (nb < by_regs) nb = by_regs;
   const int by_ids = (V + 4095) / 4096;     // at least 4096 ids per workgroup
   if (nb > by_ids) nb = by_ids;
   if (nb > NBR_MAX) nb = NBR_MAX;
@@ -341,7 +344,6 @@ __device__ inline int pow2_at_least(int n) {
 // window ids in flight with them; 16-byte accesses of 4 ids when the rows are
 // 16-byte aligned); larger ones (few rows) take a strided loop with an online
 // sum and re-read their own z for the candidates.
-constexpr int ZR = 32;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(PB) void pen_z_kernel(const PenaltyParams p, int nb) {
