@@ -98,3 +98,43 @@ def test_single_token_vocab_and_empty_window():
     x = penalty_inputs(25, 1, 1, 0)
     z, keep, probs, tok = _run(x, 1.2, 1.0, 0.9, 0.05)
     assert keep.tolist() == [[True]] and probs[0, 0] == 1.0 and tok[0] == 0
+
+
+def test_top_p_cut_inside_min_p_set():
+    """The min-p set carries almost all the mass, so top-p cuts inside it: the
+    listed set is sorted and cut by prefix mass (several rows, ragged vocab)."""
+    x = penalty_inputs(26, 4, 128251, 1024)
+    rng = np.random.default_rng(26)
+    x["logits"][:] = rng.normal(-6.0, 1.0, x["logits"].shape).astype(F32)
+    for r in range(4):
+        hot = rng.choice(128251, 300, replace=False)
+        x["logits"][r, hot] = rng.normal(4.0, 1.0, 300).astype(F32)
+    x["logits"][1, 5:9] = x["logits"][1, 4]   # ties inside the set
+    for top_p in (0.5, 0.9, 0.0):
+        _compare(x, 1.2, 1.0, top_p, 0.001)
+
+
+def test_one_chunk_list_overflows():
+    """Thousands of logits equal to the row maximum in one chunk overflow that
+    chunk's candidate list: the whole-row radix select decides, ties ranked by id."""
+    x = penalty_inputs(27, 3, 128256, 1024)
+    top = x["logits"].max(axis=1)
+    for r in range(3):
+        x["logits"][r, 20000:23000] = top[r]
+    x["window"][:] = -1
+    _compare(x, 1.2, 1.0, 0.3, 0.05)
+    _compare(x, 1.2, 1.0, 0.9, 0.05)
+
+
+def test_min_p_set_larger_than_lds():
+    """About 4500 min-p candidates spread so that no chunk list overflows but the
+    row's set exceeds what one workgroup decides in LDS: radix-select path."""
+    rows, V = 2, 128256
+    x = penalty_inputs(28, rows, V, 1024)
+    rng = np.random.default_rng(28)
+    x["logits"][:] = np.float32(-20.0)
+    for r in range(rows):
+        hot = rng.choice(V, 4500, replace=False)
+        x["logits"][r, hot] = rng.uniform(0.0, 1.0, 4500).astype(F32)
+    x["window"][:] = -1
+    _compare(x, 1.2, 1.0, 0.9, 0.05)
