@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--n-ctx", type=int, default=None)
     ap.add_argument("--n-split", type=int, default=0)
     ap.add_argument("--verify-only", action="store_true", help="time only the verification launches")
+    ap.add_argument("--fused-scores", action="store_true",
+                    help="verification also writes the selection scores; the selection reads them (no K pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -129,6 +131,7 @@ def main():
             out=torch.empty((Hq, T, d), dtype=torch.float32, device=dev),
             outd=torch.empty((Hq, Tq, d), dtype=torch.float32, device=dev),
             sel=torch.empty((Hkv, budget), dtype=torch.int32, device=dev),
+            sc=torch.empty((Hkv, n_ctx), dtype=torch.float32, device=dev) if args.fused_scores else None,
         ))
     logits = randn((rows_logits, V), torch.float32) * cfg.get("sigma", 2.0)
     window = torch.randint(0, V, (rows_logits, W), generator=gen, device=dev, dtype=torch.int32)
@@ -137,6 +140,7 @@ def main():
     ws_v = torch.empty(max(1, lib.ts_verify_attn_workspace_size(n_ctx, T, Hq, Hkv, d, args.n_split)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(1, lib.ts_draft_attn_workspace_size(n_part, Tq, Hq, Hkv, d, 0)), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(max(1, lib.ts_partial_kv_select_workspace_size(n_ctx, T, Hq, Hkv, d, budget)), dtype=torch.uint8, device=dev)
+    ws_ss = torch.empty(max(1, lib.ts_partial_kv_select_scored_workspace_size(n_ctx, Hkv, d, budget)), dtype=torch.uint8, device=dev)
     z_out = torch.empty_like(logits)
     torch.cuda.synchronize()
 
@@ -155,7 +159,11 @@ def main():
         if e:
             e[0].record(stream)
         for Ld in L:
-            ts.verify_attn(Ld["q"], Ld["k"], Ld["v"], n_ctx, parent, n_split=args.n_split, out=Ld["out"], ws=ws_v)
+            if args.fused_scores:
+                ts.verify_attn_scored(Ld["q"], Ld["k"], Ld["v"], n_ctx, parent, n_split=args.n_split, out=Ld["out"],
+                                      scores=Ld["sc"], ws=ws_v)
+            else:
+                ts.verify_attn(Ld["q"], Ld["k"], Ld["v"], n_ctx, parent, n_split=args.n_split, out=Ld["out"], ws=ws_v)
         if e:
             e[1].record(stream)
         if not args.verify_only:
@@ -165,8 +173,12 @@ def main():
             e[2].record(stream)
         if not args.verify_only:
             for Ld in L:
-                ts.partial_kv_select(Ld["q"], Ld["k"], Ld["v"], n_ctx, n_sink, budget, n_recent, k_part=Ld["kp2"],
-                                     v_part=Ld["vp2"], sel_idx=Ld["sel"], ws=ws_s)
+                if args.fused_scores:
+                    ts.partial_kv_select_scored(Ld["sc"], Ld["k"], Ld["v"], n_ctx, n_sink, budget, n_recent,
+                                                k_part=Ld["kp2"], v_part=Ld["vp2"], sel_idx=Ld["sel"], ws=ws_ss)
+                else:
+                    ts.partial_kv_select(Ld["q"], Ld["k"], Ld["v"], n_ctx, n_sink, budget, n_recent, k_part=Ld["kp2"],
+                                         v_part=Ld["vp2"], sel_idx=Ld["sel"], ws=ws_s)
         if e:
             e[3].record(stream)
         if not args.verify_only:
@@ -221,7 +233,7 @@ def main():
         "config": {"workload": f"{args.config}-class {'GQA' if Hq != Hkv else 'MHA'} tree verification, "
                                f"{Hq} q / {Hkv} kv heads, d={d}, {n_ctx} context rows, T={T} tree nodes, {layers} layers",
                    "global_batch": 1, "seq_len": n_ctx, "tree_nodes": T, "layers": layers,
-                   "parallelism": "single-gpu"},
+                   "fused_scores": bool(args.fused_scores), "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "kernels_us": {"verify_per_layer": round(verify_us, 3), "draft_per_layer": round(draft_us, 3),

@@ -96,6 +96,35 @@ size_t ts_verify_attn_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq, int32
                                      int32_t d, int32_t n_split);
 
 /*
+ * ts_verify_attn_scored -- ts_verify_attn that also writes the grouped key
+ * scores of the committed rows, summed from the query-key products the
+ * attention already forms (no second pass over the keys).
+ *
+ * TokenSwift summary §3.3 "Dynamic KV Cache Management": a cached pair's
+ * importance is a query-key dot product and, under GQA, the products of the
+ * query heads of a group are added; when the partial cache is refreshed with
+ * the queries of the verification step, those are exactly the products of
+ * this pass.
+ *
+ *   scores  [Hkv][n_ctx] float32 output (row j of head g at g*n_ctx + j):
+ *           scores[g][j] = sum_{h in group g} sum_{i<T} q[h][i] . k[g][j]
+ *           for j < n_ctx: raw products (no softmax scale, no tree mask),
+ *           the same sigma as ts_partial_kv_select with the same q.
+ *   Every other argument and output as for ts_verify_attn (same workspace
+ *   query); `out` is bitwise what ts_verify_attn writes for the same call.
+ *   The (Hq/Hkv)*T query rows of a KV head must fit one workgroup: at most
+ *   256, else TS_ENOTSUP (use ts_partial_kv_select for the scores then).
+ *
+ * Precision: bf16 x bf16 products with float32 accumulation, summed over the
+ * rows in float32 (in another order than ts_partial_kv_select's).
+ */
+int ts_verify_attn_scored(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t T,
+                          const int32_t* parent, int32_t Hq, int32_t Hkv, int32_t d,
+                          float scale, float* out, float* scores, int32_t n_split,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * ts_draft_attn -- draft attention over the PARTIAL cache.
  *
  * TokenSwift summary §3.1 and §3.3: drafting runs the target model with a
@@ -151,6 +180,30 @@ int ts_partial_kv_select(const uint16_t* q, int32_t T, const uint16_t* k, const 
 
 size_t ts_partial_kv_select_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv,
                                            int32_t d, int32_t budget);
+
+/*
+ * ts_partial_kv_select_scored -- the select and gather steps of
+ * ts_partial_kv_select on scores the caller provides (for instance those
+ * ts_verify_attn_scored wrote in the same step), so no query or key pass runs.
+ *
+ * TokenSwift summary §3.3 "Dynamic KV Cache Management" (as for
+ * ts_partial_kv_select).
+ *
+ *   scores  [Hkv][n_ctx] float32, read only (row j of head g at g*n_ctx + j);
+ *           only the candidate rows are read.
+ *   C, B', the selection order, sel_idx, the gather into k_part / v_part and
+ *   n_part_out (host) exactly as for ts_partial_kv_select, with sigma = scores.
+ *   ws      ts_partial_kv_select_scored_workspace_size(...) bytes.
+ */
+int ts_partial_kv_select_scored(const float* scores, const uint16_t* k, const uint16_t* v,
+                                int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t Hkv,
+                                int32_t d, int32_t n_sink, int32_t budget, int32_t n_recent,
+                                int32_t* sel_idx, uint16_t* k_part, uint16_t* v_part,
+                                int64_t sp_head, int64_t sp_pos, int32_t* n_part_out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+size_t ts_partial_kv_select_scored_workspace_size(int32_t n_ctx, int32_t Hkv, int32_t d,
+                                                  int32_t budget);
 
 /*
  * ts_penalty_sample -- contextual penalty, temperature, min-p and top-p.

@@ -13,8 +13,10 @@ from .binding import (
     lib,
     lib_path,
     partial_kv_select,
+    partial_kv_select_scored,
     penalty_sample,
     verify_attn,
+    verify_attn_scored,
 )
 
 __all__ = [
@@ -22,7 +24,9 @@ __all__ = [
     "lib",
     "lib_path",
     "verify_attn",
+    "verify_attn_scored",
     "draft_attn",
     "partial_kv_select",
+    "partial_kv_select_scored",
     "penalty_sample",
 ]

@@ -24,6 +24,8 @@ _SIGNATURES = {
     "ts_verify_attn": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32p, c_i32, c_i32, c_i32,
                                c_f32, c_vp, c_i32, c_vp, c_sz, c_vp]),
     "ts_verify_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "ts_verify_attn_scored": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32p, c_i32, c_i32, c_i32,
+                                      c_f32, c_vp, c_vp, c_i32, c_vp, c_sz, c_vp]),
     "ts_draft_attn": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp,
                               c_i32, c_vp, c_sz, c_vp]),
     "ts_draft_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
@@ -31,6 +33,9 @@ _SIGNATURES = {
                                      c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32p, c_vp, c_vp, c_sz,
                                      c_vp]),
     "ts_partial_kv_select_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "ts_partial_kv_select_scored": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                            c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32p, c_vp, c_sz, c_vp]),
+    "ts_partial_kv_select_scored_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
     "ts_penalty_sample": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_i32, c_i64, c_f32, c_f32, c_f32, c_f32, c_vp, c_vp,
                                   c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ts_penalty_sample_workspace_size": (c_sz, [c_i32, c_i32]),
@@ -115,6 +120,37 @@ def verify_attn(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, ws=None,
     return out
 
 
+def _score_buffer(scores, Hkv, n_ctx, device):
+    if scores is None:
+        return torch.empty((Hkv, max(n_ctx, 1)), dtype=torch.float32, device=device)
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != Hkv or scores.shape[1] < n_ctx:
+        raise ValueError(f"scores must be float32 [{Hkv}][{n_ctx}]")
+    if n_ctx > 0 and scores.stride() != (n_ctx, 1):
+        raise ValueError("scores must be contiguous with row stride n_ctx")
+    return scores
+
+
+def verify_attn_scored(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, scores=None, ws=None, stream=None):
+    """Verification attention plus the grouped key scores (ts_verify_attn_scored).
+
+    Returns (out [Hq][T][d] fp32, scores [Hkv][n_ctx] fp32).
+    """
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    s_head, s_pos = _cache_strides(k, v)
+    par = (ctypes.c_int32 * T)(*[int(x) for x in parent])
+    if out is None:
+        out = torch.empty((Hq, T, d), dtype=torch.float32, device=q.device)
+    scores = _score_buffer(scores, Hkv, n_ctx, q.device)
+    L = lib()
+    need = L.ts_verify_attn_workspace_size(n_ctx, T, Hq, Hkv, d, n_split)
+    wst = _workspace(need, q.device, ws)
+    rc = L.ts_verify_attn_scored(_ptr(q), _ptr(k), _ptr(v), s_head, s_pos, n_ctx, T, par, Hq, Hkv, d, float(scale),
+                                 _ptr(out), _ptr(scores), n_split, _ptr(wst), need, _stream(stream))
+    _check("ts_verify_attn_scored", rc)
+    return out, scores
+
+
 def draft_attn(q, k_part, v_part, n_part, scale=0.0, n_split=0, out=None, ws=None, stream=None):
     """Draft attention over the partial cache (ts_draft_attn)."""
     Hq, Tq, d = q.shape
@@ -163,6 +199,36 @@ def partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, k_part=None, v_p
                                 _stream(stream))
     _check("ts_partial_kv_select", rc)
     return sel_idx[:, :budget], k_part, v_part, n_part.value, (scores if want_scores else None)
+
+
+def partial_kv_select_scored(scores, k, v, n_ctx, n_sink, budget, n_recent, k_part=None, v_part=None,
+                             sel_idx=None, extra_rows=0, ws=None, stream=None):
+    """Select and gather the partial cache from given scores (ts_partial_kv_select_scored).
+
+    scores [Hkv][n_ctx] fp32 (e.g. from verify_attn_scored). Returns
+    (sel_idx [Hkv][budget] int32, k_part, v_part, n_part).
+    """
+    Hkv, d = k.shape[0], k.shape[2]
+    s_head, s_pos = _cache_strides(k, v)
+    dev = k.device
+    scores = _score_buffer(scores, Hkv, n_ctx, dev)
+    if k_part is None:
+        k_part = torch.empty((Hkv, max(n_sink + budget + n_recent + extra_rows, 1), d), dtype=torch.bfloat16,
+                             device=dev)
+    if v_part is None:
+        v_part = torch.empty_like(k_part)
+    sp_head, sp_pos = _cache_strides(k_part, v_part)
+    if sel_idx is None:
+        sel_idx = torch.empty((Hkv, max(budget, 1)), dtype=torch.int32, device=dev)
+    L = lib()
+    need = L.ts_partial_kv_select_scored_workspace_size(n_ctx, Hkv, d, budget)
+    wst = _workspace(need, dev, ws)
+    n_part = ctypes.c_int32(-1)
+    rc = L.ts_partial_kv_select_scored(_ptr(scores), _ptr(k), _ptr(v), s_head, s_pos, n_ctx, Hkv, d, n_sink, budget,
+                                       n_recent, _ptr(sel_idx), _ptr(k_part), _ptr(v_part), sp_head, sp_pos,
+                                       ctypes.byref(n_part), _ptr(wst), need, _stream(stream))
+    _check("ts_partial_kv_select_scored", rc)
+    return sel_idx[:, :budget], k_part, v_part, n_part.value
 
 
 def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None, want_keep=True, want_probs=True,

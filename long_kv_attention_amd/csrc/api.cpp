@@ -73,8 +73,8 @@ int check_attention(const char* who, const uint16_t* q, const uint16_t* k, const
 
 int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                   int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t T, const uint64_t* anc,
-                  int32_t Hq, int32_t Hkv, int32_t d, float scale, float* out, int32_t n_split,
-                  void* ws, size_t ws_bytes, void* stream) {
+                  int32_t Hq, int32_t Hkv, int32_t d, float scale, float* out, float* scores,
+                  int32_t n_split, void* ws, size_t ws_bytes, void* stream) {
   const int32_t rows_total = n_ctx + T;
   const size_t need = ts::attn_workspace_bytes(rows_total, T, Hq, Hkv, d, n_split);
   if (ws_bytes < need) return fail(TS_EWORKSPACE, "%s: workspace of %zu bytes, need %zu", who, ws_bytes, need);
@@ -86,6 +86,7 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
   p.k = k;
   p.v = v;
   p.out = out;
+  p.scores = scores;
   p.s_head = s_head;
   p.s_pos = s_pos;
   p.n_ctx = n_ctx;
@@ -112,7 +113,7 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
 
 extern "C" {
 
-int ts_abi_version(void) { return 100; }
+int ts_abi_version(void) { return 101; }
 
 const char* ts_last_error(void) { return g_err; }
 
@@ -138,7 +139,27 @@ int ts_verify_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int6
   uint64_t anc[64];
   char why[160];
   if (!build_masks(parent, T, anc, why, sizeof(why))) return fail(TS_EINVAL, "%s: %s", who, why);
-  return run_attention(who, q, k, v, s_head, s_pos, n_ctx, T, anc, Hq, Hkv, d, scale, out, n_split, ws,
+  return run_attention(who, q, k, v, s_head, s_pos, n_ctx, T, anc, Hq, Hkv, d, scale, out, nullptr, n_split, ws,
+                       ws_bytes, stream);
+}
+
+int ts_verify_attn_scored(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t s_head, int64_t s_pos,
+                          int32_t n_ctx, int32_t T, const int32_t* parent, int32_t Hq, int32_t Hkv, int32_t d,
+                          float scale, float* out, float* scores, int32_t n_split, void* ws, size_t ws_bytes,
+                          void* stream) {
+  const char* who = "ts_verify_attn_scored";
+  int rc = check_attention(who, q, k, v, out, s_head, s_pos, n_ctx, T, Hq, Hkv, d, scale, n_split);
+  if (rc) return rc;
+  if (!parent) return fail(TS_EINVAL, "%s: parent is null", who);
+  if (!scores) return fail(TS_EINVAL, "%s: scores is null", who);
+  if (!aligned(scores, 4)) return fail(TS_EINVAL, "%s: scores must be 4-byte aligned", who);
+  if (ts::attn_row_blocks(T, Hq, Hkv) != 1)
+    return fail(TS_ENOTSUP, "%s: the %d query rows of a KV head ((Hq/Hkv)*T) exceed the 256 that one workgroup sums",
+                who, (Hq / Hkv) * T);
+  uint64_t anc[64];
+  char why[160];
+  if (!build_masks(parent, T, anc, why, sizeof(why))) return fail(TS_EINVAL, "%s: %s", who, why);
+  return run_attention(who, q, k, v, s_head, s_pos, n_ctx, T, anc, Hq, Hkv, d, scale, out, scores, n_split, ws,
                        ws_bytes, stream);
 }
 
@@ -151,8 +172,8 @@ int ts_draft_attn(const uint16_t* q, const uint16_t* k_part, const uint16_t* v_p
   // The drafting tokens form a chain: token t sees tokens 0..t.
   uint64_t anc[64];
   for (int i = 0; i < 64; ++i) anc[i] = (i < Tq) ? ((i == 63) ? ~0ull : ((1ull << (i + 1)) - 1)) : 0ull;
-  return run_attention(who, q, k_part, v_part, s_head, s_pos, n_part, Tq, anc, Hq, Hkv, d, scale, out, n_split,
-                       ws, ws_bytes, stream);
+  return run_attention(who, q, k_part, v_part, s_head, s_pos, n_part, Tq, anc, Hq, Hkv, d, scale, out, nullptr,
+                       n_split, ws, ws_bytes, stream);
 }
 
 size_t ts_partial_kv_select_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
@@ -162,18 +183,30 @@ size_t ts_partial_kv_select_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq,
   return ts::select_workspace_bytes(n_ctx, T, Hq, Hkv, d, budget);
 }
 
-int ts_partial_kv_select(const uint16_t* q, int32_t T, const uint16_t* k, const uint16_t* v, int64_t s_head,
-                         int64_t s_pos, int32_t n_ctx, int32_t Hq, int32_t Hkv, int32_t d, int32_t n_sink,
-                         int32_t budget, int32_t n_recent, int32_t* sel_idx, uint16_t* k_part, uint16_t* v_part,
-                         int64_t sp_head, int64_t sp_pos, int32_t* n_part_out, float* scores, void* ws,
-                         size_t ws_bytes, void* stream) {
-  const char* who = "ts_partial_kv_select";
-  if (!q || !k || !v || !sel_idx || !k_part || !v_part || !n_part_out)
+}  // extern "C"
+
+namespace {
+
+// Shared by both selection entry points: q == nullptr means the scores are
+// given (scores_in) and no query pass runs.
+int run_select(const char* who, const uint16_t* q, int32_t T, int32_t Hq, const float* scores_in,
+               const uint16_t* k, const uint16_t* v, int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t Hkv,
+               int32_t d, int32_t n_sink, int32_t budget, int32_t n_recent, int32_t* sel_idx, uint16_t* k_part,
+               uint16_t* v_part, int64_t sp_head, int64_t sp_pos, int32_t* n_part_out, float* scores_out, void* ws,
+               size_t ws_bytes, void* stream) {
+  const bool given = q == nullptr;
+  if (given ? !scores_in : false) return fail(TS_EINVAL, "%s: scores is null", who);
+  if (!k || !v || !sel_idx || !k_part || !v_part || !n_part_out)
     return fail(TS_EINVAL, "%s: null pointer argument", who);
   if (d != 64 && d != 128) return fail(TS_ENOTSUP, "%s: head dim %d not supported (64 or 128)", who, d);
-  if (T < 1) return fail(TS_EINVAL, "%s: need at least one query (got %d)", who, T);
-  if (T > TS_MAX_TREE) return fail(TS_ENOTSUP, "%s: %d queries exceed the %d limit", who, T, TS_MAX_TREE);
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return fail(TS_EINVAL, "%s: Hq=%d must be a positive multiple of Hkv=%d", who, Hq, Hkv);
+  if (!given) {
+    if (T < 1) return fail(TS_EINVAL, "%s: need at least one query (got %d)", who, T);
+    if (T > TS_MAX_TREE) return fail(TS_ENOTSUP, "%s: %d queries exceed the %d limit", who, T, TS_MAX_TREE);
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+      return fail(TS_EINVAL, "%s: Hq=%d must be a positive multiple of Hkv=%d", who, Hq, Hkv);
+  } else if (Hkv < 1) {
+    return fail(TS_EINVAL, "%s: Hkv=%d must be positive", who, Hkv);
+  }
   if (Hkv > 65535) return fail(TS_ENOTSUP, "%s: Hkv=%d too large", who, Hkv);
   if (n_ctx < 0 || n_sink < 0 || budget < 0 || n_recent < 0)
     return fail(TS_EINVAL, "%s: n_ctx, n_sink, budget and n_recent must be >= 0", who);
@@ -182,8 +215,8 @@ int ts_partial_kv_select(const uint16_t* q, int32_t T, const uint16_t* k, const 
   if (sp_pos < d || sp_pos % 8 || sp_head < 0 || sp_head % 8)
     return fail(TS_EINVAL, "%s: bad partial-cache strides (sp_head=%lld, sp_pos=%lld)", who, (long long)sp_head,
                 (long long)sp_pos);
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_part, 16) || !aligned(v_part, 16) ||
-      !aligned(sel_idx, 4) || (scores && !aligned(scores, 4)))
+  if ((q && !aligned(q, 16)) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_part, 16) || !aligned(v_part, 16) ||
+      !aligned(sel_idx, 4) || (scores_out && !aligned(scores_out, 4)) || (scores_in && !aligned(scores_in, 4)))
     return fail(TS_EINVAL, "%s: tensors must be 16-byte aligned (indices and scores 4-byte)", who);
 
   const int32_t cand_lo = n_sink;
@@ -197,7 +230,8 @@ int ts_partial_kv_select(const uint16_t* q, int32_t T, const uint16_t* k, const 
   if (Hkv > 1 && sp_head < (int64_t)n_part * sp_pos)
     return fail(TS_EINVAL, "%s: partial heads overlap (sp_head=%lld < n_part*sp_pos)", who, (long long)sp_head);
 
-  const size_t need = ts::select_workspace_bytes(n_ctx, T, Hq, Hkv, d, budget);
+  const size_t need = given ? ts::select_passes_workspace_bytes(n_ctx, Hkv)
+                            : ts::select_workspace_bytes(n_ctx, T, Hq, Hkv, d, budget);
   if (ws_bytes < need) return fail(TS_EWORKSPACE, "%s: workspace of %zu bytes, need %zu", who, ws_bytes, need);
   if (need > 0 && (!ws || !aligned(ws, 256))) return fail(TS_EINVAL, "%s: workspace must be non-null and 256-byte aligned", who);
 
@@ -225,18 +259,54 @@ int ts_partial_kv_select(const uint16_t* q, int32_t T, const uint16_t* k, const 
   p.v_part = v_part;
   p.sp_head = sp_head;
   p.sp_pos = sp_pos;
-  // workspace: scores (if not user-provided) | qbar | selected rows
   char* w = static_cast<char*>(ws);
-  const size_t score_bytes = ((size_t)Hkv * n_ctx * sizeof(float) + 255) / 256 * 256;
-  p.scores = scores ? scores : reinterpret_cast<float*>(w);
-  w += score_bytes;
-  p.qbar = reinterpret_cast<float*>(w);
-  w += ((size_t)Hkv * d * sizeof(float) + 255) / 256 * 256;
+  if (given) {
+    // read-only in this mode: only the query pass writes scores
+    p.scores = const_cast<float*>(scores_in);
+    p.scores_given = 1;
+  } else {
+    // workspace: scores (if not user-provided) | qbar | selection passes
+    const size_t score_bytes = ((size_t)Hkv * n_ctx * sizeof(float) + 255) / 256 * 256;
+    p.scores = scores_out ? scores_out : reinterpret_cast<float*>(w);
+    w += score_bytes;
+    p.qbar = reinterpret_cast<float*>(w);
+    w += ((size_t)Hkv * d * sizeof(float) + 255) / 256 * 256;
+  }
   p.sel_ws = reinterpret_cast<int32_t*>(w);
   *n_part_out = n_part;
   const hipError_t e = ts::launch_select(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ts_partial_kv_select(const uint16_t* q, int32_t T, const uint16_t* k, const uint16_t* v, int64_t s_head,
+                         int64_t s_pos, int32_t n_ctx, int32_t Hq, int32_t Hkv, int32_t d, int32_t n_sink,
+                         int32_t budget, int32_t n_recent, int32_t* sel_idx, uint16_t* k_part, uint16_t* v_part,
+                         int64_t sp_head, int64_t sp_pos, int32_t* n_part_out, float* scores, void* ws,
+                         size_t ws_bytes, void* stream) {
+  const char* who = "ts_partial_kv_select";
+  if (!q) return fail(TS_EINVAL, "%s: q is null", who);
+  return run_select(who, q, T, Hq, nullptr, k, v, s_head, s_pos, n_ctx, Hkv, d, n_sink, budget, n_recent, sel_idx,
+                    k_part, v_part, sp_head, sp_pos, n_part_out, scores, ws, ws_bytes, stream);
+}
+
+size_t ts_partial_kv_select_scored_workspace_size(int32_t n_ctx, int32_t Hkv, int32_t d, int32_t budget) {
+  if (n_ctx < 0 || Hkv < 1 || (d != 64 && d != 128) || budget < 0) return 0;
+  return ts::select_passes_workspace_bytes(n_ctx, Hkv);
+}
+
+int ts_partial_kv_select_scored(const float* scores, const uint16_t* k, const uint16_t* v, int64_t s_head,
+                                int64_t s_pos, int32_t n_ctx, int32_t Hkv, int32_t d, int32_t n_sink, int32_t budget,
+                                int32_t n_recent, int32_t* sel_idx, uint16_t* k_part, uint16_t* v_part,
+                                int64_t sp_head, int64_t sp_pos, int32_t* n_part_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return run_select("ts_partial_kv_select_scored", nullptr, 0, 0, scores, k, v, s_head, s_pos, n_ctx, Hkv, d, n_sink,
+                    budget, n_recent, sel_idx, k_part, v_part, sp_head, sp_pos, n_part_out, nullptr, ws, ws_bytes,
+                    stream);
 }
 
 size_t ts_penalty_sample_workspace_size(int32_t rows, int32_t V) {

@@ -31,6 +31,14 @@
 //   tile (K landed / previous P V done, and V landed / K reads done).
 //   Splits write (max, sum, unnormalised output) partials; a combine kernel
 //   merges them with the log-sum-exp rule. A single split normalises in place.
+//
+// Fused grouped scores (optional, TokenSwift summary §3.3 "Dynamic KV Cache
+// Management"): the importance score of a committed row under GQA is the sum
+// of its query-key products over the group's query heads and tree nodes. The
+// raw S^T tile already holds every one of those products, so a workgroup that
+// holds all query rows of its KV head sums each tile over its rows (lanes,
+// then row tiles, then row groups through LDS) and writes sigma for the
+// tile's committed rows: no second pass over K.
 #include "ts_internal.h"
 
 #include <cmath>
@@ -49,7 +57,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-template <int D, int RG, int PG, int TPW, int STAGES>
+template <int D, int RG, int PG, int TPW, int STAGES, bool SCORE = false>
 struct Cfg {
   static constexpr int NCH = D / 8;                       // 16-byte chunks per row
   static constexpr int ROWB = D * 2;                      // bytes per staged row
@@ -79,14 +87,18 @@ struct Cfg {
   // barrier per tile; measured: T = 64 shapes -6%, no gain at RG = 2).
   static constexpr bool V_SHARED = RG >= 3;
   static constexpr int ANC_BYTES = 1024;  // ancestor words of the tree nodes (one full 64-lane copy)
+  // fused scores: the row sums of row groups 1.. for row group 0 (32 positions per wave)
+  static constexpr int SC_BYTES = SCORE && RG > 1 ? (RG - 1) * PG * 32 * 4 : 0;
   // At the end of a split each wave keeps the CT / PG channel tiles it merges
   // and parks the others (and its m, l) for the waves that merge them.
   static constexpr int CT_OUT = PG > 1 ? CT - CT / PG : CT;
   static constexpr int MSLOT = 64 * CT_OUT * 16 + 2 * 16 * 4;   // one wave's parked O^T of a row tile + m, l
   static constexpr int MERGE_BYTES = PG * RG * MSLOT;
-  static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES + ANC_BYTES;
+  static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES + ANC_BYTES + SC_BYTES;
   // row tiles merged per round at the end of a split (all of LDS is free then)
-  static constexpr int MERGE_RT = LDS_BYTES / (NW * MSLOT) < TPW ? LDS_BYTES / (NW * MSLOT) : TPW;
+  // (the score slots stay out of it: row group 0 may still read them)
+  static constexpr int MERGE_LDS = LDS_BYTES - SC_BYTES;
+  static constexpr int MERGE_RT = MERGE_LDS / (NW * MSLOT) < TPW ? MERGE_LDS / (NW * MSLOT) : TPW;
   static_assert(MERGE_BYTES <= KV_BYTES, "split-local merge reuses the K/V ring");
   static_assert(CT % PG == 0, "merge splits the channel tiles evenly over position groups");
   static_assert(DMA_MIN_PER_WAVE >= 1, "every wave takes part in staging");
@@ -184,11 +196,33 @@ __device__ inline unsigned int lds_offset(const void* p) {
   return (unsigned int)(uintptr_t)(const LDS_AS void*)p;
 }
 
+template <int CTRL>
+__device__ inline float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sums each of x[0..7] over the 16 lanes of a DPP row and leaves sum j =
+// 4*b3 + 2*b2 + b1 in the lanes whose index in the row has bits (b3, b2, b1)
+// (lanes 2m and 2m+1 hold the same value). Reduce-scatter by exchange with
+// partners at xor 8, 7 (row_half_mirror), 2 and 1: each step adds the half
+// the lane keeps to the partner's copy of it, so 4 + 2 + 1 + 1 adds in place
+// of 8 x 4 for full row sums.
+__device__ inline float row16_scatter8(const float (&x)[8], int l16) {
+  const bool h3 = l16 & 8, h2 = l16 & 4, h1 = l16 & 2;
+  float a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = (h3 ? x[4 + i] : x[i]) + dppf<0x128>(h3 ? x[i] : x[4 + i]);   // row_ror:8
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b[i] = (h2 ? a[2 + i] : a[i]) + dppf<0x141>(h2 ? a[i] : a[2 + i]);   // row_half_mirror
+  const float c = (h1 ? b[1] : b[0]) + dppf<0x4e>(h1 ? b[0] : b[1]);   // quad_perm [2,3,0,1]
+  return c + dppf<0xb1>(c);                                           // quad_perm [1,0,3,2]
+}
+
 static_assert(std::is_standard_layout<AttnParams>::value, "kernarg offsets via offsetof");
 
-template <int D, int RG, int PG, int TPW, int STAGES>
+template <int D, int RG, int PG, int TPW, int STAGES, bool SCORE>
 __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnParams p) {
-  using C = Cfg<D, RG, PG, TPW, STAGES>;
+  using C = Cfg<D, RG, PG, TPW, STAGES, SCORE>;
   constexpr int TN = C::TN;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
 
@@ -296,8 +330,12 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   // the (f16-rounded) probabilities, so the sum needs no VALU adds or shuffles.
   f32x4 o[TPW][C::CT];
   f32x4 lsum[TPW];
-  float m_run[TPW], m_thr[TPW];
+  // m_thr is NEG_BIG until the first rescale and m_run + lazy_raw after it
+  // (m_run is then above NEG_BIG); the score variant recomputes it from m_run
+  // to free registers.
   const float lazy_raw = LAZY_LOG2 / c;   // slack in raw score units
+  float m_run[TPW], m_thr[TPW];
+  auto thr = [&](int t) { return SCORE ? (m_run[t] == NEG_BIG ? NEG_BIG : m_run[t] + lazy_raw) : m_thr[t]; };
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     m_run[t] = NEG_BIG;
@@ -309,6 +347,32 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   f16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (_Float16)1.0f;
+
+  // ---- fused scores ----
+  // After the reduce-scatter, lane (kg, l16) holds position
+  // 16*b3 + 4*kg + 2*b2 + b1 of its wave's 32 (b = bits of l16). Row groups
+  // past the first park their sums in LDS after a tile's second barrier; row
+  // group 0 adds them after the next barrier (the next tile's first, or the
+  // one after the loop) and stores; the slots are rewritten only after the
+  // following second barrier.
+  float* const sc_lds = reinterpret_cast<float*>(alds + C::ANC_BYTES);
+  float sig_keep = 0.f;
+  auto score_slot = [&]() {
+    const int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    return ((l & 8) << 1) + ((l >> 4) << 2) + ((l >> 1) & 3);
+  };
+  auto store_score = [&](int tl, float v) {
+    const int pos = tl * TN + 32 * pg + score_slot();
+    if ((l16 & 1) == 0 && pos < n_ctx) p.scores[(int64_t)g * n_ctx + pos] = v;
+  };
+  auto add_parked = [&](int tl) {
+    if (tl * TN >= n_ctx) return;
+    const int sq = score_slot();
+    float v = sig_keep;
+#pragma unroll
+    for (int r = 1; r < RG; ++r) v += sc_lds[((r - 1) * PG + pg) * 32 + sq];
+    store_score(tl, v);
+  };
 
   // Ring schedule. K of tile i+STAGES is issued as soon as every wave has
   // finished S = K Q^T of tile i; V of tile i+STAGES-1 once every wave has
@@ -338,6 +402,8 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     else wait_vm<(4 + (VS < 3 ? VS : 3)) * NK>();
     __builtin_amdgcn_s_barrier();  // K(tile) landed for every wave; P V of tile-1 done everywhere
     if (tile + STAGES - 1 < t_end) issue(tile + STAGES - 1, true);
+    if constexpr (SCORE && RG > 1)
+      if (rg == 0 && tile > t_begin) add_parked(tile - 1);
 
     const unsigned char* kl = lds + (tile % STAGES) * C::STAGE_BYTES;
     const unsigned char* vl = kl + C::TILE_BYTES;
@@ -386,6 +452,23 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     else wait_vm<6 * NK>();
     __builtin_amdgcn_s_barrier();
     if (tile + STAGES < t_end) issue(tile + STAGES, false);
+    if constexpr (SCORE) {
+      // this wave's share of sum_rows S for its 32 positions, after the
+      // barrier so no wave waits for its S products before it
+      if (tile * TN < n_ctx) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[j] = s[0][j >> 2][j & 3];
+#pragma unroll
+          for (int t = 1; t < TPW; ++t) x[j] += s[t][j >> 2][j & 3];
+        }
+        const float sig = row16_scatter8(x, l16);
+        if constexpr (RG == 1) store_score(tile, sig);
+        else if (rg > 0 && (l16 & 1) == 0) sc_lds[((rg - 1) * PG + pg) * 32 + score_slot()] = sig;
+        else sig_keep = sig;
+      }
+    }
     if ((tile + 1) * TN > rows_total) {
       // V rows past the cache were not loaded (the descriptor bounds the read)
       // and hold stale bits; P is exactly 0 there, but 0 * NaN would poison O.
@@ -440,7 +523,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       mx[t] = group4_max(lane_max8(s[t][0], s[t][1]));
-      bump_any |= mx[t] > m_thr[t];
+      bump_any |= mx[t] > thr(t);
     }
     // Lazy rescale: the reference max only moves when the tile max exceeds it
     // by more than 2^8 in probability, so p = exp2(s*c - m*c) stays <= 256
@@ -448,7 +531,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     if (__ballot(bump_any)) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const bool bump = mx[t] > m_thr[t];
+        const bool bump = mx[t] > thr(t);
         const float m_new = bump ? mx[t] : m_run[t];
         const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
         m_run[t] = m_new;
@@ -499,6 +582,11 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     }
   }
 
+  if constexpr (SCORE && RG > 1) {
+    lds_barrier();   // the last tile's parked sums
+    if (rg == 0 && t_end > t_begin) add_parked(t_end - 1);
+  }
+
   // ---- per-row probability sums (every entry of lsum holds the full sum) ----
   float l_run[TPW];
 #pragma unroll
@@ -511,20 +599,27 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   // the loop). Output: normalised rows (single split) or the split's partial
   // (O^T, m, l).
   constexpr int CTW = C::CT / PG;   // channel tiles merged and stored per wave
+  // The score variant derives the store addresses from a lane id the compiler
+  // cannot move above the loop: hoisted there, they would be kept in (short)
+  // registers through the whole loop.
+  int lane_st = lane;
+  if constexpr (SCORE) asm volatile("" : "+v"(lane_st));
+  const int l16_st = lane_st & 15, kg_st = lane_st >> 4;
   auto store = [&](int t, float mu, float wsum, const f32x4 (&om)[CTW]) {
-    const int row = (rt0 + t) * 16 + l16;
+    const int row = (rt0 + t) * 16 + (SCORE ? l16_st : l16);
+    const int kgs = SCORE ? kg_st : kg;
     if (!tile_on[t] || row >= M) return;
     if (p.n_split == 1) {
       const float inv = 1.0f / wsum;
-      float* dst = p.out + ((int64_t)g * M + row) * D + 4 * kg;
+      float* dst = p.out + ((int64_t)g * M + row) * D + 4 * kgs;
 #pragma unroll
       for (int i = 0; i < CTW; ++i) *reinterpret_cast<f32x4*>(dst + (pg + i * PG) * 16) = om[i] * inv;
     } else {
       const int64_t prow = ((int64_t)split * p.Hkv + g) * M + row;
-      float* dst = p.part_acc + prow * D + 4 * kg;
+      float* dst = p.part_acc + prow * D + 4 * kgs;
 #pragma unroll
       for (int i = 0; i < CTW; ++i) *reinterpret_cast<f32x4*>(dst + (pg + i * PG) * 16) = om[i];
-      if (pg == 0 && kg == 0) {
+      if (pg == 0 && kgs == 0) {
         p.part_ml[prow * 2 + 0] = mu;
         p.part_ml[prow * 2 + 1] = wsum;
       }
@@ -711,9 +806,12 @@ KernelChoice choose(int nrt) {
 template <int D, int RG, int PG, int TPW>
 hipError_t launch_split(const AttnParams& p, int nz, hipStream_t stream) {
   constexpr int STAGES = Cfg<D, RG, PG, TPW, 3>::LDS_BYTES <= 160 * 1024 ? 3 : 2;
-  static_assert(Cfg<D, RG, PG, TPW, STAGES>::LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(Cfg<D, RG, PG, TPW, STAGES, true>::LDS_BYTES <= 160 * 1024, "LDS budget");
   dim3 grid(p.n_split, p.Hkv, nz);
-  hipLaunchKernelGGL((attn_split_kernel<D, RG, PG, TPW, STAGES>), grid, dim3(RG * PG * 64), 0, stream, p);
+  if (p.scores)
+    hipLaunchKernelGGL((attn_split_kernel<D, RG, PG, TPW, STAGES, true>), grid, dim3(RG * PG * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<D, RG, PG, TPW, STAGES, false>), grid, dim3(RG * PG * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -742,6 +840,8 @@ int row_blocks_for(int M) {
 }
 
 }  // namespace
+
+int attn_row_blocks(int32_t T, int32_t Hq, int32_t Hkv) { return row_blocks_for((Hq / Hkv) * T); }
 
 int attn_auto_split(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d) {
   (void)d;
@@ -782,6 +882,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {
   const int nrt = (p.M + 15) / 16;
   const KernelChoice kc = choose(nrt);
   const int nz = row_blocks_for(p.M);
+  if (p.scores && nz != 1) return hipErrorInvalidValue;   // the host checks this first
   hipError_t e = p.d == 128 ? launch_split_d<128>(p, kc, nz, stream) : launch_split_d<64>(p, kc, nz, stream);
   if (e != hipSuccess || p.n_split == 1) return e;
   const dim3 cgrid((p.Hkv * p.M + 3) / 4);   // one row per wave, four waves per block

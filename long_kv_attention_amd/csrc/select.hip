@@ -27,6 +27,10 @@
 //                ascending order and copies their K and V rows into the
 //                partial cache.
 // Passes 3 and 4 read the L2-resident scores, not K.
+//
+// With the scores given (computed by the verification pass over the same
+// queries), passes 1 and 2 become a clear of the histograms and one read of
+// the scores that fills the first-digit histogram.
 #include "ts_device.h"
 #include "ts_internal.h"
 
@@ -240,6 +244,42 @@ __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const Selec
   }
   __syncthreads();
   for (int b = tid; b < HIST1; b += NT) {
+    const unsigned int c = lhist[b];
+    if (c) atomicAdd(&ghist[g * HIST1 + b], c);
+  }
+}
+
+// Clears the head's histograms (scores given: nothing else to prepare).
+__global__ __launch_bounds__(256) void select_clear_kernel(unsigned int* hist, unsigned int* hist2) {
+  const int g = blockIdx.x;
+  for (int b = threadIdx.x; b < HIST1; b += 256) hist[g * HIST1 + b] = 0u;
+  for (int b = threadIdx.x; b < HIST2; b += 256) hist2[g * HIST2 + b] = 0u;
+}
+
+// First-digit histogram of the given scores of the candidate rows: one block
+// per chunk of rows_per_block candidates of one KV head, LDS histogram, then
+// the non-empty bins added to the head's global histogram.
+__global__ __launch_bounds__(256) void select_hist_kernel(const SelectParams p, unsigned int* ghist,
+                                                         int rows_per_block) {
+  __shared__ unsigned int lhist[HIST1];
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < HIST1; b += 256) lhist[b] = 0u;
+  __syncthreads();
+  const int r0 = p.cand_lo + blockIdx.x * rows_per_block;
+  const int r1 = min(r0 + rows_per_block, p.cand_hi);
+  const float* sc = p.scores + (int64_t)g * p.n_ctx;
+  constexpr int U = 8;   // loads in flight per thread
+  for (int j0 = r0 + tid; j0 < r1; j0 += 256 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = j0 + u * 256 < r1 ? sc[j0 + u * 256] : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j0 + u * 256 < r1) atomicAdd(&lhist[f2key(v[u]) >> (32 - HIST1_BITS)], 1u);
+  }
+  __syncthreads();
+  for (int b = tid; b < HIST1; b += 256) {
     const unsigned int c = lhist[b];
     if (c) atomicAdd(&ghist[g * HIST1 + b], c);
   }
@@ -714,13 +754,25 @@ size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv,
          sel_ws_bytes(Hkv, n_ctx);
 }
 
+size_t select_passes_workspace_bytes(int32_t n_ctx, int32_t Hkv) { return sel_ws_bytes(Hkv, n_ctx); }
+
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
-  if (p.d == 128)
+  if (p.scores_given) {
+    hipLaunchKernelGGL(select_clear_kernel, dim3(p.Hkv), dim3(256), 0, stream, ws.hist, ws.hist2);
+    const int n_cand = p.cand_hi - p.cand_lo;
+    if (n_cand > 0) {
+      int chunks = (256 + p.Hkv - 1) / p.Hkv;
+      int rpb = (n_cand + chunks - 1) / chunks;
+      if (rpb < 2048) rpb = 2048;
+      chunks = (n_cand + rpb - 1) / rpb;
+      hipLaunchKernelGGL(select_hist_kernel, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, ws.hist, rpb);
+    }
+  } else if (p.d == 128)
     hipLaunchKernelGGL(select_prologue_kernel<128>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist, ws.hist2);
   else
     hipLaunchKernelGGL(select_prologue_kernel<64>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist, ws.hist2);
-  if (p.n_ctx > 0) {
+  if (!p.scores_given && p.n_ctx > 0) {
     // about one scoring workgroup per compute unit over all heads, at least
     // one tile each
     int chunks = (256 + p.Hkv - 1) / p.Hkv;

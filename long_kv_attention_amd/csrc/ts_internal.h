@@ -22,6 +22,7 @@ struct AttnParams {
   int32_t n_split;       // effective number of chunks per KV head
   int32_t rows_per_split;  // cache rows per split (a multiple of 128)
   float scale_log2e;     // softmax scale * log2(e)
+  float* scores;         // [Hkv][n_ctx] grouped scores of the committed rows, or null
   uint64_t anc[64];      // anc[i] bit a set <=> tree node a is i or an ancestor of i
 };
 
@@ -34,6 +35,9 @@ void attn_split_plan(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int
 size_t attn_workspace_bytes(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
                             int32_t n_split_req);
 hipError_t launch_attention(const AttnParams& p, hipStream_t stream);
+// Workgroups along the query rows of one KV head (1: every row of the group in
+// one workgroup, which the fused score output needs).
+int attn_row_blocks(int32_t T, int32_t Hq, int32_t Hkv);
 
 // Partial-KV selection.
 struct SelectParams {
@@ -50,12 +54,15 @@ struct SelectParams {
   uint16_t* k_part;
   uint16_t* v_part;
   int64_t sp_head, sp_pos;
-  float* scores;              // [Hkv][n_ctx] (user buffer or workspace)
+  float* scores;              // [Hkv][n_ctx] (user buffer or workspace; read-only when scores_given)
+  int32_t scores_given;       // 1: scores come from the caller (no query pass)
   float* qbar;                // [Hkv][d] workspace
   int32_t* sel_ws;            // workspace of the selection passes (histograms, cut-bin lists)
 };
 size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
                               int32_t budget);
+// Workspace of the selection passes alone (scores given by the caller).
+size_t select_passes_workspace_bytes(int32_t n_ctx, int32_t Hkv);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 
 // Penalty / sampling pass.

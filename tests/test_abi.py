@@ -41,7 +41,7 @@ def test_library_exports_every_header_symbol():
     L = _lib()
     missing = [s for s in header_symbols() if not hasattr(L, s)]
     assert not missing, missing
-    assert L.ts_abi_version() == 100
+    assert L.ts_abi_version() == 101
 
 
 def test_workspace_queries_depend_on_shapes_only():
@@ -93,6 +93,31 @@ def test_verify_attn_rejects(kw, code, text):
     assert text in L.ts_last_error().decode()
 
 
+def _verify_scored(L, scores=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, s_head=128 * 200, s_pos=128, n_ctx=100, T=3, parent=[-1, 0, 1], Hq=8, Hkv=2,
+             d=128, scale=0.0, out=FAKE, n_split=1, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    par = (ctypes.c_int32 * max(1, len(a["parent"])))(*a["parent"])
+    return L.ts_verify_attn_scored(a["q"], a["k"], a["v"], a["s_head"], a["s_pos"], a["n_ctx"], a["T"], par, a["Hq"],
+                                   a["Hkv"], a["d"], a["scale"], a["out"], scores, a["n_split"], a["ws"],
+                                   a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(scores=None), EINVAL, "scores is null"),
+    (dict(scores=FAKE_ODD), EINVAL, "scores must be 4-byte aligned"),
+    # 40 query heads over 8 KV heads with 64 tree nodes: 320 rows per KV head
+    (dict(Hq=40, Hkv=8, T=64, parent=[-1] + list(range(63)), s_head=128 * 200), ENOTSUP, "320 query rows"),
+    (dict(d=96), ENOTSUP, "head dim"),
+    (dict(parent=[0, 0, 1]), EINVAL, "parent[0]"),
+    (dict(n_ctx=100_000, n_split=0, s_head=128 * 200_000), EWORKSPACE, "workspace"),
+])
+def test_verify_attn_scored_rejects(kw, code, text):
+    L = _lib()
+    assert _verify_scored(L, **kw) == code
+    assert text in L.ts_last_error().decode()
+
+
 def test_draft_attn_rejects():
     L = _lib()
     assert L.ts_draft_attn(FAKE, FAKE, FAKE, 128 * 100, 128, 50, 65, 8, 2, 128, 0.0, FAKE, 0, None, 0, None) == ENOTSUP
@@ -121,6 +146,38 @@ def test_partial_kv_select_rejects(kw, code):
     rc, n_part = _select(L, **kw)
     assert rc == code
     assert n_part == -7  # nothing written on error
+
+
+def _select_scored(L, **kw):
+    a = dict(scores=FAKE, k=FAKE, v=FAKE, s_head=128 * 1000, s_pos=128, n_ctx=1000, Hkv=2, d=128, n_sink=4,
+             budget=100, n_recent=8, sel=FAKE, kp=FAKE, vp=FAKE, sp_head=128 * 112, sp_pos=128, ws=None, ws_bytes=0)
+    a.update(kw)
+    n_part = ctypes.c_int32(-7)
+    rc = L.ts_partial_kv_select_scored(a["scores"], a["k"], a["v"], a["s_head"], a["s_pos"], a["n_ctx"], a["Hkv"],
+                                       a["d"], a["n_sink"], a["budget"], a["n_recent"], a["sel"], a["kp"], a["vp"],
+                                       a["sp_head"], a["sp_pos"], ctypes.byref(n_part), a["ws"], a["ws_bytes"], None)
+    return rc, n_part.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scores=None), EINVAL), (dict(scores=FAKE_ODD), EINVAL), (dict(sel=None), EINVAL), (dict(budget=-1), EINVAL),
+    (dict(Hkv=0), EINVAL), (dict(d=80), ENOTSUP), (dict(sp_head=128 * 50), EINVAL), (dict(kp=FAKE_ODD), EINVAL),
+    (dict(), EWORKSPACE),
+])
+def test_partial_kv_select_scored_rejects(kw, code):
+    L = _lib()
+    rc, n_part = _select_scored(L, **kw)
+    assert rc == code
+    assert n_part == -7
+
+
+def test_scored_selection_needs_less_workspace():
+    L = _lib()
+    full = L.ts_partial_kv_select_workspace_size(100_000, 24, 32, 8, 128, 4096)
+    passes = L.ts_partial_kv_select_scored_workspace_size(100_000, 8, 128, 4096)
+    # no score copy and no query sum: the full query at least adds the scores
+    assert 0 < passes and passes + 8 * 100_000 * 4 <= full
+    assert L.ts_partial_kv_select_scored_workspace_size(100_000, 0, 128, 4096) == 0
 
 
 def _penalty(L, **kw):
