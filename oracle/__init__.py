@@ -15,7 +15,7 @@ follows. Page names used in the citations:
 * "TokenSwift reproducibility checklist" -- the acmrep2026 page on the same
   paper (its Table 11 lists the inference hyper-parameters).
 
-All four parts reach an exactly defined result (the method is lossless), so
+Every part reaches an exactly defined result (the method is lossless), so
 each oracle is that definition written out in float64, vectorised only with
 library primitives (matrix products, sorts, cumulative sums). Where the pages
 are silent the reading taken is stated next to the code.
@@ -29,6 +29,7 @@ from .common import bf16_to_f64, ancestor_sets
 from .attention import verify_attention, draft_attention
 from .select import partial_kv_select, SelectResult
 from .penalty import penalty_sample, PenaltyResult
+from .accept import accept_path, kv_commit
 
 __all__ = [
     "bf16_to_f64",
@@ -39,4 +40,6 @@ __all__ = [
     "SelectResult",
     "penalty_sample",
     "PenaltyResult",
+    "accept_path",
+    "kv_commit",
 ]

@@ -13,6 +13,9 @@ shapes, so seeded Gaussian inputs of the pages' model shapes stand in for them.
   (KV head, channel).
 * Logits are N(0, sigma^2) float32 with sigma = 2 by default; window ids are
   uniform over the vocabulary.
+* Acceptance inputs: uniform target tokens over a small vocabulary; each
+  draft token copies its parent's target token with probability p_match
+  (default 1/2), so paths of every length occur.
 * Parity inputs use NumPy's PCG64 (``default_rng(seed)``).
 """
 
@@ -22,6 +25,9 @@ from .inputs import (
     penalty_inputs,
     CONFIGS,
     tree_parent,
+    random_parent,
+    accept_inputs,
 )
 
-__all__ = ["bf16_round", "attention_inputs", "penalty_inputs", "CONFIGS", "tree_parent"]
+__all__ = ["bf16_round", "attention_inputs", "penalty_inputs", "CONFIGS", "tree_parent", "random_parent",
+           "accept_inputs"]

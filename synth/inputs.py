@@ -110,3 +110,27 @@ def penalty_inputs(seed, rows, V, W, sigma=2.0, shared_window=False, dup_window=
         window[:, W // 2:W // 2 + 2] = window[:, :2]
     u = rng.random(rows).astype(np.float32)
     return dict(logits=logits, window=window[0] if shared_window else window, u=u)
+
+
+def random_parent(seed, T):
+    """A random tree of T nodes in parents-first order: parent[i] ~ U[0, i)."""
+    rng = np.random.default_rng(seed)
+    return [-1] + [int(rng.integers(0, i)) for i in range(1, T)]
+
+
+def accept_inputs(seed, parent, vocab=50, p_match=0.5):
+    """Node tokens and target tokens (int32) of one verified tree.
+
+    target[i] is uniform over [0, vocab). Each non-root node copies its
+    parent's target token with probability p_match (a planted match) and
+    otherwise draws a uniform token, so accepted paths of every length occur.
+    """
+    rng = np.random.default_rng(seed)
+    T = len(parent)
+    target = rng.integers(0, vocab, size=T).astype(np.int32)
+    node = rng.integers(0, vocab, size=T).astype(np.int32)
+    plant = rng.random(T) < p_match
+    for i in range(1, T):
+        if plant[i]:
+            node[i] = target[parent[i]]
+    return dict(node_token=node, target=target)
