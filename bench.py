@@ -8,6 +8,7 @@ working set):
     draft attention (partial cache)            x layers
     partial-KV selection (score/select/gather) x layers
     penalty / temperature / top-p / min-p over the step's logits rows
+    tree acceptance and the KV commit of the accepted path (all layers, one launch)
 The headline value is the verification attention time per layer-step,
 measured with HIP events around the layers' verification launches on the
 stream the library launches on. Inputs are seeded synthetic tensors of the
@@ -116,16 +117,27 @@ def main():
     def randn(shape, dtype=torch.bfloat16):
         return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).to(dtype)
 
+    # caches of all layers in one tensor each (the commit moves rows of every layer in one launch)
+    K = torch.empty((layers, Hkv, n_ctx + T, d), dtype=torch.bfloat16, device=dev)
+    Vc = torch.empty_like(K)
+    part_cap = n_part + max(Tq, T)
+    KP = torch.empty((layers, Hkv, part_cap, d), dtype=torch.bfloat16, device=dev)
+    VP = torch.empty_like(KP)
     L = []
-    for _ in range(layers):
+    for l in range(layers):
         k = randn((Hkv, n_ctx + T, d))
         if "k_scale" in cfg:
             lo, hi = cfg["k_scale"]
             k = (k.float() * (lo + (hi - lo) * torch.rand((Hkv, 1, d), generator=gen, device=dev))).to(torch.bfloat16)
+        K[l] = k
+        Vc[l] = randn((Hkv, n_ctx + T, d))
+        KP[l] = randn((Hkv, part_cap, d))
+        VP[l] = randn((Hkv, part_cap, d))
+        del k
         L.append(dict(
-            q=randn((Hq, T, d)), k=k, v=randn((Hkv, n_ctx + T, d)),
+            q=randn((Hq, T, d)), k=K[l], v=Vc[l],
             qd=randn((Hq, Tq, d)),
-            kp=randn((Hkv, n_part + Tq, d)), vp=randn((Hkv, n_part + Tq, d)),
+            kp=KP[l], vp=VP[l],
             kp2=torch.empty((Hkv, n_part + Tq, d), dtype=torch.bfloat16, device=dev),
             vp2=torch.empty((Hkv, n_part + Tq, d), dtype=torch.bfloat16, device=dev),
             out=torch.empty((Hq, T, d), dtype=torch.float32, device=dev),
@@ -153,7 +165,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    # Draft tokens of the tree: planted once so that the top head path (three
+    # drafted tokens) matches the target's tokens, which the step recomputes
+    # identically (same logits and u): 4 rows committed per step.
+    ts.penalty_sample(logits, window, 1.2, 1.0, 0.9, 0.05, u=u, out=z_out)
+    tok0 = ts.penalty_sample(logits, window, 1.2, 1.0, 0.9, 0.05, u=u, want_keep=False, want_probs=False)[3]
+    target_host = tok0[:T].cpu().numpy()
+    node_host = [-1] * T
+    node_i = 0
+    while True:
+        kids = [c for c in range(T) if parent[c] == node_i]
+        if not kids:
+            break
+        node_host[kids[0]] = int(target_host[node_i])
+        node_i = kids[0]
+    node_tok = torch.tensor(node_host, dtype=torch.int32, device=dev)
+    accept_res = torch.empty(T + 2, dtype=torch.int32, device=dev)
+    token_out = torch.empty(rows_logits, dtype=torch.int32, device=dev)
 
     def step(e=None):
         if e:
@@ -182,9 +211,14 @@ def main():
         if e:
             e[3].record(stream)
         if not args.verify_only:
-            ts.penalty_sample(logits, window, 1.2, 1.0, 0.9, 0.05, u=u, out=z_out)
+            ts.penalty_sample(logits, window, 1.2, 1.0, 0.9, 0.05, u=u, out=z_out, token_out=token_out)
         if e:
             e[4].record(stream)
+        if not args.verify_only:
+            ts.tree_accept(parent, node_tok, token_out[:T], result=accept_res)
+            ts.kv_commit(accept_res, T, K, Vc, n_ctx, KP, VP, n_part)
+        if e:
+            e[5].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -202,7 +236,8 @@ def main():
     draft_us = avg(1, 2) / layers
     select_us = avg(2, 3) / layers
     penalty_us = avg(3, 4)
-    step_ms = avg(0, 4) / 1e3
+    commit_us = avg(4, 5)
+    step_ms = avg(0, 5) / 1e3
     vb = verify_bytes(Hq, Hkv, d, n_ctx, T)
     achieved = vb / (verify_us * 1e-6) / 1e9
 
@@ -238,6 +273,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "kernels_us": {"verify_per_layer": round(verify_us, 3), "draft_per_layer": round(draft_us, 3),
                        "select_per_layer": round(select_us, 3), "penalty_per_step": round(penalty_us, 3),
+                       "accept_commit_per_step": round(commit_us, 3),
                        "verify_bytes_per_launch": vb},
         "wall_s": round(wall, 3),
     }

@@ -4,7 +4,8 @@
  * The library runs the per-step, data-parallel work of TokenSwift-style
  * lossless ultra-long generation on one GPU: tree-masked verification
  * attention over the full KV cache, draft attention over the partial cache,
- * the dynamic partial-KV update, and the contextual-penalty logit pass.
+ * the dynamic partial-KV update, the contextual-penalty logit pass, and the
+ * acceptance of the verified tree with its KV commit.
  *
  * Citations name pages and sections, not files:
  *   "TokenSwift summary"  = the paperlayer.ai source-linked summary of
@@ -241,6 +242,64 @@ int ts_penalty_sample(const float* logits, int32_t rows, int32_t V,
                       void* ws, size_t ws_bytes, void* stream);
 
 size_t ts_penalty_sample_workspace_size(int32_t rows, int32_t V);
+
+/*
+ * ts_tree_accept -- the accepted path of a verified token tree.
+ *
+ * TokenSwift summary §3.1 (with Figure 2): after the target model verifies
+ * the drafted tree, the longest valid draft is accepted; Appendix A "Lossless
+ * Nature of Speculative Decoding": acceptance and rejection together keep
+ * the target model's sampling distribution.
+ *
+ * A child c of node p continues a valid draft iff node_token[c] equals
+ * target[p], the target model's token at node p (its draw from the processed
+ * distribution at p, e.g. ts_penalty_sample's token for that node's row, or
+ * the argmax when decoding greedily). Every emitted token is then the
+ * target's own draw, so the output is distributed as the target's. The path
+ * ends at the deepest node all of whose edges from the root are valid (ties:
+ * the smaller node index); node 0 (the root) is always accepted.
+ *
+ *   parent      (host) [T] int32, a tree listed parents-first as for
+ *               ts_verify_attn.   1 <= T <= 64.
+ *   node_token  [T] int32: the token of each node (node 0's is not read).
+ *   target      [T] int32: the target model's token at each node.
+ *   result      [T + 2] int32 output: result[0] = n = m + 1 nodes accepted,
+ *               result[1] = target[a_m] (the next token, emitted after the
+ *               accepted ones), result[2 .. 2+n) = a_0 = 0 < a_1 < ... < a_m,
+ *               result[2+n .. 2+T) = -1.
+ * One wave; no workspace. The host learns n only by reading result[0].
+ */
+int ts_tree_accept(const int32_t* parent, int32_t T, const int32_t* node_token,
+                   const int32_t* target, int32_t* result, void* stream);
+
+/*
+ * ts_kv_commit -- commit an accepted path into the full and partial caches.
+ *
+ * TokenSwift summary §3.1 (with Figure 2): after acceptance the accepted
+ * tokens' keys and values join the KV cache; §3.3: drafting continues on the
+ * partial cache, so they are appended to it as well.
+ *
+ * For every layer l and KV head g, with a_0..a_m the path in result (as
+ * written by ts_tree_accept for the same T):
+ *   row n_ctx + k of the full cache <- row n_ctx + a_k   (k = 0..m)
+ *   row n_part + k of the partial cache <- the same row  (if k_part given)
+ * Rows n_ctx + m + 1 .. n_ctx + T - 1 keep their contents; nothing else is
+ * touched. The moves are done as a gather (all accepted rows are read before
+ * any is written), so overlapping source and destination rows are fine.
+ *
+ *   k, v        full caches of `layers` layers: element (l, g, j, c) at
+ *               l*s_layer + g*s_head + j*s_pos + c (layers and heads must not
+ *               overlap), holding the tree rows n_ctx .. n_ctx+T-1.
+ *   k_part, v_part  partial caches with strides sp_layer, sp_head, sp_pos, or
+ *               both NULL; they hold part_rows rows per head, of which the
+ *               first n_part are in use: n_part + T <= part_rows.
+ *   d 64 or 128; 1 <= layers, Hkv <= 65535. One launch for all layers.
+ */
+int ts_kv_commit(const int32_t* result, int32_t T, uint16_t* k, uint16_t* v,
+                 int64_t s_layer, int64_t s_head, int64_t s_pos, int32_t layers,
+                 int32_t Hkv, int32_t d, int32_t n_ctx,
+                 uint16_t* k_part, uint16_t* v_part, int64_t sp_layer, int64_t sp_head,
+                 int64_t sp_pos, int32_t n_part, int32_t part_rows, void* stream);
 
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* ts_last_error(void);

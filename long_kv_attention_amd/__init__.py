@@ -10,11 +10,13 @@ the library is missing, every call raises.
 from .binding import (
     TSError,
     draft_attn,
+    kv_commit,
     lib,
     lib_path,
     partial_kv_select,
     partial_kv_select_scored,
     penalty_sample,
+    tree_accept,
     verify_attn,
     verify_attn_scored,
 )
@@ -29,4 +31,6 @@ __all__ = [
     "partial_kv_select",
     "partial_kv_select_scored",
     "penalty_sample",
+    "tree_accept",
+    "kv_commit",
 ]

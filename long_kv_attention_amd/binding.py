@@ -39,6 +39,9 @@ _SIGNATURES = {
     "ts_penalty_sample": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_i32, c_i64, c_f32, c_f32, c_f32, c_f32, c_vp, c_vp,
                                   c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ts_penalty_sample_workspace_size": (c_sz, [c_i32, c_i32]),
+    "ts_tree_accept": (c_i32, [c_i32p, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "ts_kv_commit": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
+                             c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
     "ts_last_error": (ctypes.c_char_p, []),
     "ts_abi_version": (c_i32, []),
 }
@@ -232,7 +235,7 @@ def partial_kv_select_scored(scores, k, v, n_ctx, n_sink, budget, n_recent, k_pa
 
 
 def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None, want_keep=True, want_probs=True,
-                   want_token=None, out=None, ws=None, stream=None):
+                   want_token=None, out=None, token_out=None, ws=None, stream=None):
     """Contextual penalty + temperature + top-p + min-p (ts_penalty_sample).
 
     logits [rows][V] fp32; window [rows][W] or [W] int32 (shared). Returns
@@ -254,7 +257,12 @@ def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None, w
     z = torch.empty_like(logits) if out is None else out
     keep = torch.empty((rows, V), dtype=torch.uint8, device=dev) if want_keep else None
     probs = torch.empty((rows, V), dtype=torch.float32, device=dev) if want_probs else None
-    token = torch.empty(rows, dtype=torch.int32, device=dev) if want_token else None
+    if token_out is not None:
+        if token_out.dtype != torch.int32 or token_out.numel() < rows or not token_out.is_contiguous():
+            raise ValueError(f"token_out must be a contiguous int32 buffer of at least {rows} entries")
+        token = token_out
+    else:
+        token = torch.empty(rows, dtype=torch.int32, device=dev) if want_token else None
     L = lib()
     need = L.ts_penalty_sample_workspace_size(rows, V)
     wst = _workspace(need, dev, ws)
@@ -263,3 +271,54 @@ def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None, w
                              _ptr(wst), need, _stream(stream))
     _check("ts_penalty_sample", rc)
     return z, keep, probs, token
+
+
+def tree_accept(parent, node_token, target, result=None, stream=None):
+    """Accepted path of a verified tree (ts_tree_accept).
+
+    node_token, target: int32 [T] on the device. Returns result int32 [T + 2]:
+    (n accepted, next token, path a_0..a_{n-1}, -1 padding).
+    """
+    T = len(parent)
+    for name, t in (("node_token", node_token), ("target", target)):
+        if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != T or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 vector of {T} tokens")
+    par = (ctypes.c_int32 * T)(*[int(x) for x in parent])
+    if result is None:
+        result = torch.empty(T + 2, dtype=torch.int32, device=node_token.device)
+    rc = lib().ts_tree_accept(par, T, _ptr(node_token), _ptr(target), _ptr(result), _stream(stream))
+    _check("ts_tree_accept", rc)
+    return result
+
+
+def _layer_strides(k, v):
+    if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("caches must be bfloat16")
+    if k.dim() == 3:
+        k, v = k.unsqueeze(0), v.unsqueeze(0)
+    if k.dim() != 4 or k.stride() != v.stride() or k.stride(3) != 1:
+        raise ValueError("caches must be [layers][Hkv][rows][d] (or [Hkv][rows][d]) with contiguous channels "
+                         "and equal strides")
+    return k.shape[0], k.stride(0), k.stride(1), k.stride(2)
+
+
+def kv_commit(result, T, k, v, n_ctx, k_part=None, v_part=None, n_part=0, stream=None):
+    """Commit an accepted path into the caches (ts_kv_commit), in place.
+
+    k, v: [layers][Hkv][rows][d] or [Hkv][rows][d] bf16; k_part, v_part the
+    partial caches of the same form (or None), n_part rows in use.
+    """
+    layers, s_layer, s_head, s_pos = _layer_strides(k, v)
+    Hkv, d = k.shape[-3], k.shape[-1]
+    if k_part is not None:
+        pl, sp_layer, sp_head, sp_pos = _layer_strides(k_part, v_part)
+        if pl != layers:
+            raise ValueError("partial caches need the same number of layers")
+        part_rows = k_part.shape[-2]
+    else:
+        sp_layer = sp_head = sp_pos = 0
+        part_rows = 0
+    rc = lib().ts_kv_commit(_ptr(result), T, _ptr(k), _ptr(v), s_layer, s_head, s_pos, layers, Hkv, d, n_ctx,
+                            _ptr(k_part), _ptr(v_part), sp_layer, sp_head, sp_pos, n_part, part_rows,
+                            _stream(stream))
+    _check("ts_kv_commit", rc)

@@ -1,0 +1,116 @@
+// Tree acceptance and the post-acceptance KV commit for CDNA4 (gfx950).
+//
+// What is computed (TokenSwift summary §3.1 with Figure 2: the target model
+// verifies the drafted tree in one pass and the longest valid draft is
+// accepted, then the caches are updated; Appendix A: acceptance and rejection
+// together keep the target's sampling distribution):
+//   * a child c of node p continues a valid draft iff node_token[c] equals
+//     target[p], the target model's token at p (its sample, or argmax);
+//   * the accepted path ends at the deepest node whose edges from the root
+//     are all valid (ties: the smaller node index); its nodes a_0 = 0 < ... <
+//     a_m are committed and target[a_m] is the next token;
+//   * commit: cache row n_ctx + k receives row n_ctx + a_k (k = 0..m) in every
+//     layer and KV head, and the same rows are appended to the partial cache.
+//
+// Kernels:
+//   accept  one wave, lane i = node i: edge test, one ballot, validity as
+//           "no invalid edge among my ancestors" (ancestor masks from the
+//           host), then a wave max of (depth, -index).
+//   commit  grid (Hkv, layers, {K, V}): a workgroup loads its slice's m + 1
+//           accepted rows into registers, waits for all of them, then stores
+//           them (destination rows can be later source rows, so every load
+//           precedes every store).
+#include "ts_device.h"
+#include "ts_internal.h"
+
+#include <cstddef>
+#include <type_traits>
+
+namespace ts {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+static_assert(std::is_standard_layout<AcceptParams>::value, "kernarg offsets via offsetof");
+
+__global__ __launch_bounds__(64) void accept_kernel(const AcceptParams p) {
+  const int i = threadIdx.x;
+  const bool in = i < p.T;
+  // p is the kernel's only argument, so it starts the kernarg segment; the
+  // per-node tables are read there with lane-varying indices
+  const unsigned char* ka = (const unsigned char*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int32_t* par = reinterpret_cast<const int32_t*>(ka + offsetof(AcceptParams, parent));
+  const u64* anc = reinterpret_cast<const u64*>(ka + offsetof(AcceptParams, anc));
+  const int pi = in && i > 0 ? par[i] : 0;   // the host checked 0 <= parent[i] < i
+  const bool ok = in && (i == 0 || p.node_token[i] == p.target[pi]);
+  const u64 okm = __ballot(ok);
+  const u64 mine = in ? anc[i] : 0ull;
+  const bool valid = in && (mine & ~okm) == 0ull;
+  const int depth = __popcll(mine) - 1;
+  const int key = wave_reduce(valid ? (depth << 8) | (255 - i) : -1, OpMaxI());   // node 0 is always valid
+  const int best = 255 - (key & 255);
+  const u64 path = anc[best];
+  const int n = __popcll(path);
+  if (i == 0) {
+    p.result[0] = n;
+    p.result[1] = p.target[best];
+  }
+  if (in) {
+    if ((path >> i) & 1ull) p.result[2 + __popcll(path & ((1ull << i) - 1ull))] = i;
+    if (i >= n) p.result[2 + i] = -1;
+  }
+}
+
+constexpr int CT = 256;   // threads per commit workgroup
+constexpr int CPT = 4;    // 16-byte chunks per thread: 64 rows x 16 chunks (d = 128)
+
+__global__ __launch_bounds__(CT) void commit_kernel(const CommitParams p) {
+  const int g = blockIdx.x;
+  const int layer = blockIdx.y;
+  const bool is_v = blockIdx.z == 1;
+  const int tid = threadIdx.x;
+  const int nch = p.d / 8;
+  int n = p.result[0];
+  n = n < 1 ? 1 : (n > p.T ? p.T : n);   // a foreign buffer cannot push the copies out of range
+  const int64_t off = (int64_t)layer * p.s_layer + (int64_t)g * p.s_head;
+  uint16_t* base = (is_v ? p.v : p.k) + off;
+  u32x4 buf[CPT];
+#pragma unroll
+  for (int it = 0; it < CPT; ++it) {
+    const int idx = tid + it * CT;
+    if (idx < n * nch) {
+      const int r = idx / nch, c = idx % nch;
+      int a = p.result[2 + r];
+      a = a < 0 ? 0 : (a >= p.T ? p.T - 1 : a);
+      buf[it] = *reinterpret_cast<const u32x4*>(base + (int64_t)(p.n_ctx + a) * p.s_pos + c * 8);
+    }
+  }
+  __syncthreads();   // every source row is read before any row is overwritten
+  uint16_t* pbase = p.k_part ? (is_v ? p.v_part : p.k_part) + (int64_t)layer * p.sp_layer + (int64_t)g * p.sp_head
+                             : nullptr;
+#pragma unroll
+  for (int it = 0; it < CPT; ++it) {
+    const int idx = tid + it * CT;
+    if (idx < n * nch) {
+      const int r = idx / nch, c = idx % nch;
+      *reinterpret_cast<u32x4*>(base + (int64_t)(p.n_ctx + r) * p.s_pos + c * 8) = buf[it];
+      if (pbase) *reinterpret_cast<u32x4*>(pbase + (int64_t)(p.n_part + r) * p.sp_pos + c * 8) = buf[it];
+    }
+  }
+}
+
+static_assert(CT * CPT >= 64 * 16, "one pass covers 64 rows of 16 chunks");
+
+}  // namespace
+
+hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const CommitParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(commit_kernel, dim3(p.Hkv, p.layers, 2), dim3(CT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace ts

@@ -113,7 +113,7 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
 
 extern "C" {
 
-int ts_abi_version(void) { return 101; }
+int ts_abi_version(void) { return 102; }
 
 const char* ts_last_error(void) { return g_err; }
 
@@ -359,6 +359,80 @@ int ts_penalty_sample(const float* logits, int32_t rows, int32_t V, const int32_
   p.token = token;
   p.ws = ws;
   const hipError_t e = ts::launch_penalty(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+int ts_tree_accept(const int32_t* parent, int32_t T, const int32_t* node_token, const int32_t* target,
+                   int32_t* result, void* stream) {
+  const char* who = "ts_tree_accept";
+  if (!parent || !node_token || !target || !result) return fail(TS_EINVAL, "%s: null pointer argument", who);
+  if (T < 1) return fail(TS_EINVAL, "%s: need at least one node (got %d)", who, T);
+  if (T > TS_MAX_TREE) return fail(TS_ENOTSUP, "%s: %d nodes exceed the %d-node limit", who, T, TS_MAX_TREE);
+  if (!aligned(node_token, 4) || !aligned(target, 4) || !aligned(result, 4))
+    return fail(TS_EINVAL, "%s: token and result arrays must be 4-byte aligned", who);
+  ts::AcceptParams p;
+  std::memset(&p, 0, sizeof(p));
+  char why[160];
+  if (!build_masks(parent, T, p.anc, why, sizeof(why))) return fail(TS_EINVAL, "%s: %s", who, why);
+  for (int i = 0; i < T; ++i) p.parent[i] = parent[i];
+  p.node_token = node_token;
+  p.target = target;
+  p.result = result;
+  p.T = T;
+  const hipError_t e = ts::launch_accept(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+int ts_kv_commit(const int32_t* result, int32_t T, uint16_t* k, uint16_t* v, int64_t s_layer, int64_t s_head,
+                 int64_t s_pos, int32_t layers, int32_t Hkv, int32_t d, int32_t n_ctx, uint16_t* k_part,
+                 uint16_t* v_part, int64_t sp_layer, int64_t sp_head, int64_t sp_pos, int32_t n_part,
+                 int32_t part_rows, void* stream) {
+  const char* who = "ts_kv_commit";
+  if (!result || !k || !v) return fail(TS_EINVAL, "%s: null pointer argument", who);
+  if (T < 1) return fail(TS_EINVAL, "%s: need at least one node (got %d)", who, T);
+  if (T > TS_MAX_TREE) return fail(TS_ENOTSUP, "%s: %d nodes exceed the %d-node limit", who, T, TS_MAX_TREE);
+  if (d != 64 && d != 128) return fail(TS_ENOTSUP, "%s: head dim %d not supported (64 or 128)", who, d);
+  if (layers < 1 || layers > 65535 || Hkv < 1 || Hkv > 65535)
+    return fail(TS_EINVAL, "%s: layers=%d and Hkv=%d must lie in [1, 65535]", who, layers, Hkv);
+  if (n_ctx < 0) return fail(TS_EINVAL, "%s: n_ctx=%d is negative", who, n_ctx);
+  if ((int64_t)n_ctx + T > (int64_t)INT32_MAX) return fail(TS_EINVAL, "%s: cache rows overflow int32", who);
+  if (s_pos < d || s_pos % 8 || s_head < 0 || s_head % 8 || s_layer < 0 || s_layer % 8 || (Hkv > 1 && s_head == 0) ||
+      (layers > 1 && s_layer == 0))
+    return fail(TS_EINVAL, "%s: bad cache strides (s_layer=%lld, s_head=%lld, s_pos=%lld)", who, (long long)s_layer,
+                (long long)s_head, (long long)s_pos);
+  if (!aligned(result, 4) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(TS_EINVAL, "%s: k and v must be 16-byte aligned, result 4-byte", who);
+  if ((k_part == nullptr) != (v_part == nullptr)) return fail(TS_EINVAL, "%s: give both k_part and v_part or neither", who);
+  if (k_part) {
+    if (sp_pos < d || sp_pos % 8 || sp_head < 0 || sp_head % 8 || sp_layer < 0 || sp_layer % 8 ||
+        (Hkv > 1 && sp_head == 0) || (layers > 1 && sp_layer == 0))
+      return fail(TS_EINVAL, "%s: bad partial-cache strides", who);
+    if (!aligned(k_part, 16) || !aligned(v_part, 16)) return fail(TS_EINVAL, "%s: partial caches must be 16-byte aligned", who);
+    if (n_part < 0 || part_rows < 0 || (int64_t)n_part + T > (int64_t)part_rows)
+      return fail(TS_EINVAL, "%s: n_part=%d + T=%d rows exceed the partial cache's %d rows", who, n_part, T, part_rows);
+  }
+  ts::CommitParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.result = result;
+  p.k = k;
+  p.v = v;
+  p.s_layer = s_layer;
+  p.s_head = s_head;
+  p.s_pos = s_pos;
+  p.layers = layers;
+  p.Hkv = Hkv;
+  p.d = d;
+  p.n_ctx = n_ctx;
+  p.T = T;
+  p.k_part = k_part;
+  p.v_part = v_part;
+  p.sp_layer = sp_layer;
+  p.sp_head = sp_head;
+  p.sp_pos = sp_pos;
+  p.n_part = n_part;
+  const hipError_t e = ts::launch_commit(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
 }

@@ -82,4 +82,28 @@ struct PenaltyParams {
 size_t penalty_workspace_bytes(int32_t rows, int32_t V);
 hipError_t launch_penalty(const PenaltyParams& p, hipStream_t stream);
 
+// Tree acceptance and KV commit.
+struct AcceptParams {
+  const int32_t* node_token;   // [T]
+  const int32_t* target;       // [T]
+  int32_t* result;             // [T + 2]: n accepted, next token, path, -1 padding
+  int32_t T;
+  int32_t parent[64];
+  uint64_t anc[64];            // ancestor-or-self masks
+};
+hipError_t launch_accept(const AcceptParams& p, hipStream_t stream);
+
+struct CommitParams {
+  const int32_t* result;       // as written by the acceptance kernel
+  uint16_t* k;                 // element (layer, g, j, c) at layer*s_layer + g*s_head + j*s_pos + c
+  uint16_t* v;
+  int64_t s_layer, s_head, s_pos;
+  int32_t layers, Hkv, d, n_ctx, T;
+  uint16_t* k_part;            // or null
+  uint16_t* v_part;
+  int64_t sp_layer, sp_head, sp_pos;
+  int32_t n_part;
+};
+hipError_t launch_commit(const CommitParams& p, hipStream_t stream);
+
 }  // namespace ts

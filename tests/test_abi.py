@@ -41,7 +41,7 @@ def test_library_exports_every_header_symbol():
     L = _lib()
     missing = [s for s in header_symbols() if not hasattr(L, s)]
     assert not missing, missing
-    assert L.ts_abi_version() == 101
+    assert L.ts_abi_version() == 102
 
 
 def test_workspace_queries_depend_on_shapes_only():
@@ -206,3 +206,35 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         binding.lib()
+
+
+def test_tree_accept_rejects():
+    L = _lib()
+    par = (ctypes.c_int32 * 3)(-1, 0, 1)
+    assert L.ts_tree_accept(par, 3, FAKE, FAKE, None, None) == EINVAL
+    assert L.ts_tree_accept(par, 0, FAKE, FAKE, FAKE, None) == EINVAL
+    assert L.ts_tree_accept(par, 65, FAKE, FAKE, FAKE, None) == ENOTSUP
+    assert L.ts_tree_accept(par, 3, FAKE_ODD, FAKE, FAKE, None) == EINVAL
+    bad = (ctypes.c_int32 * 3)(-1, 0, 2)
+    assert L.ts_tree_accept(bad, 3, FAKE, FAKE, FAKE, None) == EINVAL
+    assert "parent[2]" in L.ts_last_error().decode()
+
+
+def _commit(L, **kw):
+    a = dict(result=FAKE, T=24, k=FAKE, v=FAKE, s_layer=8 * 128 * 200, s_head=128 * 200, s_pos=128, layers=4, Hkv=8,
+             d=128, n_ctx=100, kp=FAKE, vp=FAKE, sp_layer=8 * 128 * 64, sp_head=128 * 64, sp_pos=128, n_part=40,
+             part_rows=64)
+    a.update(kw)
+    return L.ts_kv_commit(a["result"], a["T"], a["k"], a["v"], a["s_layer"], a["s_head"], a["s_pos"], a["layers"],
+                          a["Hkv"], a["d"], a["n_ctx"], a["kp"], a["vp"], a["sp_layer"], a["sp_head"], a["sp_pos"],
+                          a["n_part"], a["part_rows"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(result=None), EINVAL), (dict(T=0), EINVAL), (dict(T=65), ENOTSUP), (dict(d=96), ENOTSUP),
+    (dict(layers=0), EINVAL), (dict(s_pos=64), EINVAL), (dict(s_layer=0), EINVAL), (dict(k=FAKE_ODD), EINVAL),
+    (dict(vp=None), EINVAL), (dict(n_part=41), EINVAL), (dict(sp_head=0), EINVAL), (dict(n_ctx=-1), EINVAL),
+])
+def test_kv_commit_rejects(kw, code):
+    L = _lib()
+    assert _commit(L, **kw) == code
