@@ -97,8 +97,8 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
   p.M = (Hq / Hkv) * T;
   ts::attn_split_plan(rows_total, T, Hq, Hkv, d, n_split, &p.n_split, &p.rows_per_split);
   if (p.n_split > 1) {
-    const size_t acc_bytes = (size_t)p.n_split * Hkv * p.M * d * sizeof(float);
-    p.part_acc = static_cast<float*>(ws);
+    const size_t acc_bytes = (size_t)p.n_split * Hkv * p.M * d * sizeof(uint16_t);
+    p.part_acc = static_cast<uint16_t*>(ws);
     p.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + acc_bytes);
   }
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);

@@ -29,8 +29,10 @@
 //   All global reads are asynchronous copies into LDS (queries first, then a
 //   STAGES-deep K/V ring with separate K and V refills); two barriers per
 //   tile (K landed / previous P V done, and V landed / K reads done).
-//   Splits write (max, sum, unnormalised output) partials; a combine kernel
-//   merges them with the log-sum-exp rule. A single split normalises in place.
+//   Splits write (max, sum, normalised output) partials, the output in f16
+//   (half the bytes of the split's stores and the combine's reads); a combine
+//   kernel merges them with the log-sum-exp rule. A single split normalises
+//   in place.
 //
 // Fused grouped scores (optional, TokenSwift summary §3.3 "Dynamic KV Cache
 // Management"): the importance score of a committed row under GQA is the sum
@@ -615,10 +617,17 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 #pragma unroll
       for (int i = 0; i < CTW; ++i) *reinterpret_cast<f32x4*>(dst + (pg + i * PG) * 16) = om[i] * inv;
     } else {
+      // a split can see none of a row's positions (tree rows past its start
+      // that are not the row's ancestors): sum 0, weight 0 in the merge
+      const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
       const int64_t prow = ((int64_t)split * p.Hkv + g) * M + row;
-      float* dst = p.part_acc + prow * D + 4 * kgs;
+      uint16_t* dst = p.part_acc + prow * D + 4 * kgs;
 #pragma unroll
-      for (int i = 0; i < CTW; ++i) *reinterpret_cast<f32x4*>(dst + (pg + i * PG) * 16) = om[i];
+      for (int i = 0; i < CTW; ++i) {
+        const f32x4 x = om[i] * inv;
+        const f16x4 h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+        *reinterpret_cast<f16x4*>(dst + (pg + i * PG) * 16) = h;
+      }
       if (pg == 0 && kgs == 0) {
         p.part_ml[prow * 2 + 0] = mu;
         p.part_ml[prow * 2 + 1] = wsum;
@@ -702,31 +711,37 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 }
 
 // Log-sum-exp merge of the split partials: one wave per output row, no LDS.
-// Lane (sg, c4) holds float4 channel group c4 of the splits sg, sg + SG, ...
-// (SG = 64 / (d/4) split groups), merges them in one online pass with U
-// splits' loads in flight, then the split groups merge across lanes with the
-// gfx950 row / half swaps, in a fixed order (bitwise repeatable).
+// Lane (sg, cg) holds the CPL = d/16 channels of group cg (one 16- or 8-byte
+// f16 load per split) of the splits sg, sg + 4, ... (four split groups per
+// wave), merges them in one online pass with U splits' loads in flight, then
+// the split groups merge across lanes with the gfx950 row / half swaps, in a
+// fixed order (bitwise repeatable). A split's weight is l_s * 2^((m_s - m) c)
+// and its normalised output enters with that weight.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
-  constexpr int CG = D / 4;                 // float4 channel groups per row
-  constexpr int SG = 64 / CG;               // split groups per wave
+  constexpr int CPL = D / 16;               // channels per lane
+  constexpr int CG = D / CPL;               // channel groups per row (16)
+  constexpr int SG = 64 / CG;               // split groups per wave (4)
   constexpr int U = 8;                      // splits in flight per lane
-  static_assert(SG == 2 || SG == 4, "one row per wave");
+  static_assert(SG == 4, "one row per wave");
+  typedef _Float16 hv __attribute__((ext_vector_type(CPL)));
   const int lane = threadIdx.x & 63;
   const int nrows = p.Hkv * p.M;
   const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);   // g * M + r
   if (row >= nrows) return;   // wave-uniform
-  const int sg = lane / CG, c4 = lane % CG;
+  const int sg = lane / CG, cg = lane % CG;
   const float c = p.scale_log2e;
   const int64_t sstride = nrows;
 
   // Partial maxima are finite (running maxima start at a finite floor); -inf
-  // marks "no split here" and gets weight exp2(-inf) = 0.
+  // marks "no split here" and gets weight 0.
   float m_loc = -INFINITY, l_loc = 0.f;
-  f32x4 a_loc = {0.f, 0.f, 0.f, 0.f};
+  float a_loc[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) a_loc[j] = 0.f;
   for (int s0 = sg; s0 < p.n_split; s0 += SG * U) {
     float mv[U], lv[U];
-    f32x4 av[U];
+    hv av[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * SG;
@@ -735,23 +750,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
       const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + pr * 2);
       mv[u] = in ? ml.x : -INFINITY;
       lv[u] = in ? ml.y : 0.f;
-      av[u] = *reinterpret_cast<const f32x4*>(p.part_acc + pr * D + 4 * c4);
+      av[u] = *reinterpret_cast<const hv*>(p.part_acc + pr * D + CPL * cg);
     }
     float mn = m_loc;
 #pragma unroll
     for (int u = 0; u < U; ++u) mn = fmaxf(mn, mv[u]);
     const float sc = __builtin_amdgcn_exp2f((m_loc - mn) * c);   // 0 on the first round
     l_loc *= sc;
-    a_loc *= sc;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) a_loc[j] *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = __builtin_amdgcn_exp2f((mv[u] - mn) * c);
-      l_loc += w * lv[u];
-      a_loc += w * av[u];
+      const float w = __builtin_amdgcn_exp2f((mv[u] - mn) * c) * lv[u];
+      l_loc += w;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) a_loc[j] += w * (float)av[u][j];
     }
     m_loc = mn;
   }
-  // merge the split groups: lanes l and l ^ 32 (and l ^ 16 for d = 64)
+  // merge the split groups: lanes l and l ^ 16, then l and l ^ 32
   auto merge = [&](auto swap) {
     const auto mm = swap(__float_as_uint(m_loc));
     const float m0 = __uint_as_float(mm[0]), m1 = __uint_as_float(mm[1]);
@@ -762,16 +779,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
     const auto ll = swap(__float_as_uint(l_loc));
     l_loc = w0 * __uint_as_float(ll[0]) + w1 * __uint_as_float(ll[1]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto aa = swap(__float_as_uint(a_loc[i]));
-      a_loc[i] = w0 * __uint_as_float(aa[0]) + w1 * __uint_as_float(aa[1]);
+    for (int j = 0; j < CPL; ++j) {
+      const auto aa = swap(__float_as_uint(a_loc[j]));
+      a_loc[j] = w0 * __uint_as_float(aa[0]) + w1 * __uint_as_float(aa[1]);
     }
     m_loc = mu;
   };
-  if constexpr (SG == 4)
-    merge([](unsigned int x) { return __builtin_amdgcn_permlane16_swap(x, x, false, false); });
+  merge([](unsigned int x) { return __builtin_amdgcn_permlane16_swap(x, x, false, false); });
   merge([](unsigned int x) { return __builtin_amdgcn_permlane32_swap(x, x, false, false); });
-  if (sg == 0) *reinterpret_cast<f32x4*>(p.out + (int64_t)row * D + 4 * c4) = a_loc * (1.0f / l_loc);
+  if (sg == 0) {
+    const float inv = 1.0f / l_loc;
+    float* dst = p.out + (int64_t)row * D + CPL * cg;
+#pragma unroll
+    for (int j = 0; j < CPL; j += 4)
+      *reinterpret_cast<f32x4*>(dst + j) = f32x4{a_loc[j], a_loc[j + 1], a_loc[j + 2], a_loc[j + 3]} * inv;
+  }
 }
 
 struct KernelChoice {
@@ -875,7 +897,7 @@ size_t attn_workspace_bytes(int32_t rows_total, int32_t T, int32_t Hq, int32_t H
   attn_split_plan(rows_total, T, Hq, Hkv, d, n_split_req, &s, &tps);
   if (s <= 1) return 0;
   const size_t M = (size_t)(Hq / Hkv) * T;
-  return (size_t)s * Hkv * M * ((size_t)d + 2) * sizeof(float);
+  return (size_t)s * Hkv * M * ((size_t)d * 2 + 2 * sizeof(float));   // f16 outputs, then (m, l) pairs
 }
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {

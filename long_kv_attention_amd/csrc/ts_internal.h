@@ -14,7 +14,7 @@ struct AttnParams {
   const uint16_t* k;     // cache, element (g, j, c) at g*s_head + j*s_pos + c
   const uint16_t* v;
   float* out;            // [Hq][T][d] fp32
-  float* part_acc;       // [n_split][Hkv][M][d] unnormalised partial outputs
+  uint16_t* part_acc;    // [n_split][Hkv][M][d] f16 bits: each split's normalised partial output
   float* part_ml;        // [n_split][Hkv][M][2] running max (raw score units) and sum
   int64_t s_head, s_pos;
   int32_t n_ctx, T, Hq, Hkv, d;

@@ -50,7 +50,7 @@ def test_workspace_queries_depend_on_shapes_only():
     assert a > 0 and a == L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 0)
     assert L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 1) == 0   # one split: no partials
     forced = L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 7)
-    assert forced == 7 * 8 * 96 * 130 * 4
+    assert forced == 7 * 8 * 96 * (128 * 2 + 8)   # f16 partial outputs + (m, l) per row
     assert L.ts_verify_attn_workspace_size(100_000, 65, 32, 8, 128, 0) == 0   # unsupported -> 0
     assert L.ts_draft_attn_workspace_size(4164, 4, 32, 8, 128, 0) == L.ts_verify_attn_workspace_size(4164, 4, 32, 8, 128, 0)
     assert L.ts_partial_kv_select_workspace_size(100_000, 24, 32, 8, 128, 4096) >= 8 * 100_000 * 4
