@@ -303,6 +303,9 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   // the B-fragment reads are conflict-free; rows past M are outside the
   // descriptor and are zeroed here instead (the copy skips them).
   unsigned char* const alds = qlds + C::Q_BYTES;
+  // The first K tile is requested before the queries: the first tile's wait
+  // counts only the copies issued after the queries, so it still covers them.
+  if (t_begin < t_end) issue(t_begin, false);
   bool tile_on[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) tile_on[t] = (rt0 + t) * 16 < M;
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (t_begin + st < t_end) {
-      issue(t_begin + st, false);
+      if (st > 0) issue(t_begin + st, false);   // K of the first tile went out first
       issue(t_begin + st, true);
     }
   if (t_begin + STAGES - 1 < t_end) issue(t_begin + STAGES - 1, false);
