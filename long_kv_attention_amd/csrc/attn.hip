@@ -235,8 +235,13 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   const int pg = wave % PG;   // position group: which 32 positions of each KV tile
   const int l16 = lane & 15;
   const int kg = lane >> 4;
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
+  // Workgroups go to the XCDs round-robin in dispatch order, so taking the KV
+  // head from the low digits of the dispatch index keeps all splits of a head
+  // on one XCD (with 8 KV heads: head g on XCD g); the combine blocks of that
+  // head land there too and read its partials from that XCD's L2.
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int g = lin % p.Hkv;
+  const int split = lin / p.Hkv;
   const int M = p.M;
   const int T = p.T;
   const int n_ctx = p.n_ctx;
@@ -730,8 +735,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   typedef _Float16 hv __attribute__((ext_vector_type(CPL)));
   const int lane = threadIdx.x & 63;
   const int nrows = p.Hkv * p.M;
-  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);   // g * M + r
-  if (row >= nrows) return;   // wave-uniform
+  // block b: KV head b % Hkv (the split kernel placed that head's splits on
+  // the XCD this block lands on), rows 4 * (b / Hkv) .. + 3 of the head
+  const int gh = blockIdx.x % p.Hkv;
+  const int r = (blockIdx.x / p.Hkv) * 4 + (int)(threadIdx.x >> 6);
+  if (r >= p.M) return;   // wave-uniform
+  const int row = gh * p.M + r;   // g * M + r
   const int sg = lane / CG, cg = lane % CG;
   const float c = p.scale_log2e;
   const int64_t sstride = nrows;
@@ -910,7 +919,7 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {
   if (p.scores && nz != 1) return hipErrorInvalidValue;   // the host checks this first
   hipError_t e = p.d == 128 ? launch_split_d<128>(p, kc, nz, stream) : launch_split_d<64>(p, kc, nz, stream);
   if (e != hipSuccess || p.n_split == 1) return e;
-  const dim3 cgrid((p.Hkv * p.M + 3) / 4);   // one row per wave, four waves per block
+  const dim3 cgrid(p.Hkv * ((p.M + 3) / 4));   // one row per wave, four waves per block
   if (p.d == 128)
     hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, p);
   else
