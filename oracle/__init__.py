@@ -30,6 +30,7 @@ from .attention import verify_attention, draft_attention
 from .select import partial_kv_select, SelectResult
 from .penalty import penalty_sample, PenaltyResult
 from .accept import accept_path, kv_commit
+from .ngram import ngram_candidates, ngram_tree, splitmix64
 
 __all__ = [
     "bf16_to_f64",
@@ -42,4 +43,7 @@ __all__ = [
     "PenaltyResult",
     "accept_path",
     "kv_commit",
+    "ngram_candidates",
+    "ngram_tree",
+    "splitmix64",
 ]

@@ -16,6 +16,8 @@ shapes, so seeded Gaussian inputs of the pages' model shapes stand in for them.
 * Acceptance inputs: uniform target tokens over a small vocabulary; each
   draft token copies its parent's target token with probability p_match
   (default 1/2), so paths of every length occur.
+* N-gram windows: uniform tokens with a few fixed 4-token phrases copied in
+  at random positions (repeated phrases, as generated text has).
 * Parity inputs use NumPy's PCG64 (``default_rng(seed)``).
 """
 
@@ -27,7 +29,8 @@ from .inputs import (
     tree_parent,
     random_parent,
     accept_inputs,
+    ngram_window,
 )
 
 __all__ = ["bf16_round", "attention_inputs", "penalty_inputs", "CONFIGS", "tree_parent", "random_parent",
-           "accept_inputs"]
+           "accept_inputs", "ngram_window"]

@@ -134,3 +134,21 @@ def accept_inputs(seed, parent, vocab=50, p_match=0.5):
         if plant[i]:
             node[i] = target[parent[i]]
     return dict(node_token=node, target=target)
+
+
+def ngram_window(seed, W, vocab, repeat=0.5, n_phrases=6):
+    """A token window (int32 [W]) with repeated phrases, as generated text has.
+
+    Tokens are uniform over [0, vocab) except that, with probability
+    `repeat` at each position, one of `n_phrases` fixed 4-token phrases is
+    copied in; the last token is the root, drawn like the others.
+    """
+    rng = np.random.default_rng(seed)
+    phrases = rng.integers(0, vocab, size=(n_phrases, 4))
+    out = []
+    while len(out) < W:
+        if rng.random() < repeat:
+            out.extend(int(t) for t in phrases[rng.integers(0, n_phrases)])
+        else:
+            out.append(int(rng.integers(0, vocab)))
+    return np.asarray(out[:W], dtype=np.int32)
