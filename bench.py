@@ -9,6 +9,8 @@ working set):
     partial-KV selection (score/select/gather) x layers
     penalty / temperature / top-p / min-p over the step's logits rows
     tree acceptance and the KV commit of the accepted path (all layers, one launch)
+    the next step's draft tree: 4-gram retrieval over the last W tokens, random
+    choice of k = 20, head candidates and chains (one launch)
 The headline value is the verification attention time per layer-step,
 measured with HIP events around the layers' verification launches on the
 stream the library launches on. Inputs are seeded synthetic tensors of the
@@ -95,7 +97,7 @@ def main():
 
     import torch
     import long_kv_attention_amd as ts
-    from synth import CONFIGS, tree_parent
+    from synth import CONFIGS, ngram_window, tree_parent
 
     cfg = dict(CONFIGS[args.config])
     T = args.T or cfg["T"]
@@ -165,7 +167,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    # the committed tokens' window for the n-gram tree (repeated phrases, as generated text has)
+    ng_window = torch.from_numpy(ngram_window(cfg["seed"], W, vocab=V, repeat=0.5, n_phrases=8)).to(dev)
+    ng_head = torch.randint(0, V, (3, 3), generator=gen, device=dev, dtype=torch.int32)
+    ng_out = [torch.empty(T, dtype=torch.int32, device=dev), torch.empty(T, dtype=torch.int32, device=dev),
+              torch.empty(4, dtype=torch.int32, device=dev)]
     # Draft tokens of the tree: planted once so that the top head path (three
     # drafted tokens) matches the target's tokens, which the step recomputes
     # identically (same logits and u): 4 rows committed per step.
@@ -219,6 +226,10 @@ def main():
             ts.kv_commit(accept_res, T, K, Vc, n_ctx, KP, VP, n_part)
         if e:
             e[5].record(stream)
+        if not args.verify_only:
+            ts.ngram_tree(ng_window, 20, 12345, ng_head, T, parent=ng_out[0], node_token=ng_out[1], info=ng_out[2])
+        if e:
+            e[6].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -237,7 +248,8 @@ def main():
     select_us = avg(2, 3) / layers
     penalty_us = avg(3, 4)
     commit_us = avg(4, 5)
-    step_ms = avg(0, 5) / 1e3
+    ngram_us = avg(5, 6)
+    step_ms = avg(0, 6) / 1e3
     vb = verify_bytes(Hq, Hkv, d, n_ctx, T)
     achieved = vb / (verify_us * 1e-6) / 1e9
 
@@ -273,7 +285,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "kernels_us": {"verify_per_layer": round(verify_us, 3), "draft_per_layer": round(draft_us, 3),
                        "select_per_layer": round(select_us, 3), "penalty_per_step": round(penalty_us, 3),
-                       "accept_commit_per_step": round(commit_us, 3),
+                       "accept_commit_per_step": round(commit_us, 3), "ngram_tree_per_step": round(ngram_us, 3),
                        "verify_bytes_per_launch": vb},
         "wall_s": round(wall, 3),
     }

@@ -4,8 +4,9 @@
  * The library runs the per-step, data-parallel work of TokenSwift-style
  * lossless ultra-long generation on one GPU: tree-masked verification
  * attention over the full KV cache, draft attention over the partial cache,
- * the dynamic partial-KV update, the contextual-penalty logit pass, and the
- * acceptance of the verified tree with its KV commit.
+ * the dynamic partial-KV update, the contextual-penalty logit pass, the
+ * acceptance of the verified tree with its KV commit, and the n-gram draft
+ * tree.
  *
  * Citations name pages and sections, not files:
  *   "TokenSwift summary"  = the paperlayer.ai source-linked summary of
@@ -300,6 +301,42 @@ int ts_kv_commit(const int32_t* result, int32_t T, uint16_t* k, uint16_t* v,
                  int32_t Hkv, int32_t d, int32_t n_ctx,
                  uint16_t* k_part, uint16_t* v_part, int64_t sp_layer, int64_t sp_head,
                  int64_t sp_pos, int32_t n_part, int32_t part_rows, void* stream);
+
+/*
+ * ts_ngram_tree -- n-gram retrieval, random n-gram choice and the draft tree.
+ *
+ * TokenSwift summary §3.2 "Multi-token Generation and Token Reutilization":
+ * frequent 4-grams of the generated text are reused as draft candidates, at
+ * most k of them (k = 20 in the reproducibility checklist's Table 11); §3.4:
+ * a random choice among several valid n-grams keeps the output diverse;
+ * §4.4.1 and Appendix B.2: the tree is a simple ternary [1,3,3,3] tree of the
+ * draft heads' candidates, merged with the n-grams.
+ *
+ * The n-gram table is the multiset of 4-grams lying in `window` (the last W
+ * committed tokens; the root is window[W-1]). A 4-gram is valid iff its first
+ * token is the root; valid 4-grams are counted per distinct continuation
+ * (the last three tokens), numbered q = 0, 1, ... by first occurrence. If more
+ * than k are valid, the k with the smallest (r_q, q) are kept, r_q = output q
+ * of SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) started from state
+ * `seed`: a uniformly random subset. Kept chains are ordered by count
+ * (descending), then first occurrence.
+ * Tree: node 0 = root; for level l = 1..levels, nodes 3(l-1)+1 .. 3l carry
+ * head_cand[l-1][0..2] under node 0 (l = 1) or under node 3(l-2)+1; then each
+ * kept chain (a, b, c) adds three nodes in a line under node 0. Nodes past
+ * T_max are cut off.
+ *
+ *   window      [W] int32, 1 <= W <= 4096.     k >= 0.     seed: any.
+ *   head_cand   [levels][3] int32 (NULL when levels == 0); 0 <= levels <= 3.
+ *   T_max       1 <= T_max <= 64.
+ *   parent, node_token  [T_max] int32 outputs (parents-first tree as
+ *               ts_verify_attn takes it); slots past T hold -1.
+ *   info        [4] int32 output: T (nodes), chains with a node in the tree,
+ *               distinct valid continuations, valid occurrences.
+ * One workgroup; no workspace. parent and T reach the host by a copy.
+ */
+int ts_ngram_tree(const int32_t* window, int32_t W, int32_t k, uint64_t seed,
+                  const int32_t* head_cand, int32_t levels, int32_t T_max,
+                  int32_t* parent, int32_t* node_token, int32_t* info, void* stream);
 
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* ts_last_error(void);

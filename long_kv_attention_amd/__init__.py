@@ -13,6 +13,7 @@ from .binding import (
     kv_commit,
     lib,
     lib_path,
+    ngram_tree,
     partial_kv_select,
     partial_kv_select_scored,
     penalty_sample,
@@ -33,4 +34,5 @@ __all__ = [
     "penalty_sample",
     "tree_accept",
     "kv_commit",
+    "ngram_tree",
 ]

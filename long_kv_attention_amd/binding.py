@@ -42,6 +42,7 @@ _SIGNATURES = {
     "ts_tree_accept": (c_i32, [c_i32p, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "ts_kv_commit": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
                              c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
+    "ts_ngram_tree": (c_i32, [c_vp, c_i32, c_i32, ctypes.c_uint64, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "ts_last_error": (ctypes.c_char_p, []),
     "ts_abi_version": (c_i32, []),
 }
@@ -322,3 +323,28 @@ def kv_commit(result, T, k, v, n_ctx, k_part=None, v_part=None, n_part=0, stream
                             _ptr(k_part), _ptr(v_part), sp_layer, sp_head, sp_pos, n_part, part_rows,
                             _stream(stream))
     _check("ts_kv_commit", rc)
+
+
+def ngram_tree(window, k, seed, head_cand=None, T_max=24, parent=None, node_token=None, info=None, stream=None):
+    """N-gram retrieval, random choice and draft tree (ts_ngram_tree).
+
+    window: int32 [W] on the device (root = last token); head_cand: int32
+    [levels][3] or None. Returns device tensors (parent [T_max], node_token
+    [T_max], info [4] = T, chains, distinct, occurrences).
+    """
+    if window.dtype != torch.int32 or window.dim() != 1 or not window.is_contiguous():
+        raise ValueError("window must be a contiguous int32 vector")
+    dev = window.device
+    levels = 0
+    if head_cand is not None:
+        if head_cand.dtype != torch.int32 or head_cand.dim() != 2 or head_cand.shape[1] != 3 or \
+                not head_cand.is_contiguous():
+            raise ValueError("head_cand must be a contiguous int32 [levels][3] tensor")
+        levels = head_cand.shape[0]
+    parent = torch.empty(T_max, dtype=torch.int32, device=dev) if parent is None else parent
+    node_token = torch.empty(T_max, dtype=torch.int32, device=dev) if node_token is None else node_token
+    info = torch.empty(4, dtype=torch.int32, device=dev) if info is None else info
+    rc = lib().ts_ngram_tree(_ptr(window), window.shape[0], int(k), int(seed) & ((1 << 64) - 1), _ptr(head_cand),
+                             levels, int(T_max), _ptr(parent), _ptr(node_token), _ptr(info), _stream(stream))
+    _check("ts_ngram_tree", rc)
+    return parent, node_token, info

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libtokenswift.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["csrc/api.cpp", "csrc/attn.hip", "csrc/select.hip", "csrc/penalty.hip", "csrc/accept.hip"]
+SOURCES = ["csrc/api.cpp", "csrc/attn.hip", "csrc/select.hip", "csrc/penalty.hip", "csrc/accept.hip", "csrc/ngram.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 VALU instructions stay disabled (the compiler would otherwise

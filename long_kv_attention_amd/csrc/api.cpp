@@ -113,7 +113,7 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
 
 extern "C" {
 
-int ts_abi_version(void) { return 102; }
+int ts_abi_version(void) { return 103; }
 
 const char* ts_last_error(void) { return g_err; }
 
@@ -433,6 +433,36 @@ int ts_kv_commit(const int32_t* result, int32_t T, uint16_t* k, uint16_t* v, int
   p.sp_pos = sp_pos;
   p.n_part = n_part;
   const hipError_t e = ts::launch_commit(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
+
+int ts_ngram_tree(const int32_t* window, int32_t W, int32_t k, uint64_t seed, const int32_t* head_cand,
+                  int32_t levels, int32_t T_max, int32_t* parent, int32_t* node_token, int32_t* info, void* stream) {
+  const char* who = "ts_ngram_tree";
+  if (!window || !parent || !node_token || !info) return fail(TS_EINVAL, "%s: null pointer argument", who);
+  if (W < 1) return fail(TS_EINVAL, "%s: the window needs at least the root token (W=%d)", who, W);
+  if (W > ts::NG_MAX_WINDOW) return fail(TS_ENOTSUP, "%s: W=%d exceeds %d tokens", who, W, ts::NG_MAX_WINDOW);
+  if (k < 0) return fail(TS_EINVAL, "%s: k=%d is negative", who, k);
+  if (levels < 0 || levels > 3) return fail(TS_EINVAL, "%s: levels=%d must lie in [0, 3]", who, levels);
+  if (levels > 0 && !head_cand) return fail(TS_EINVAL, "%s: head_cand is null with %d levels", who, levels);
+  if (T_max < 1 || T_max > TS_MAX_TREE) return fail(TS_EINVAL, "%s: T_max=%d must lie in [1, %d]", who, T_max, TS_MAX_TREE);
+  if (!aligned(window, 4) || !aligned(parent, 4) || !aligned(node_token, 4) || !aligned(info, 4) ||
+      (head_cand && !aligned(head_cand, 4)))
+    return fail(TS_EINVAL, "%s: int32 arrays must be 4-byte aligned", who);
+  ts::NgramParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.window = window;
+  p.head = levels > 0 ? head_cand : nullptr;
+  p.parent = parent;
+  p.node_token = node_token;
+  p.info = info;
+  p.seed = seed;
+  p.W = W;
+  p.k = k;
+  p.levels = levels;
+  p.T_max = T_max;
+  const hipError_t e = ts::launch_ngram_tree(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
 }

@@ -106,4 +106,17 @@ struct CommitParams {
 };
 hipError_t launch_commit(const CommitParams& p, hipStream_t stream);
 
+// N-gram retrieval and draft tree.
+constexpr int NG_MAX_WINDOW = 4096;   // window tokens held in LDS
+struct NgramParams {
+  const int32_t* window;       // [W]
+  const int32_t* head;         // [levels][3] or null
+  int32_t* parent;             // [T_max]
+  int32_t* node_token;         // [T_max]
+  int32_t* info;               // [4]: T, chains placed, distinct continuations, occurrences
+  uint64_t seed;
+  int32_t W, k, levels, T_max;
+};
+hipError_t launch_ngram_tree(const NgramParams& p, hipStream_t stream);
+
 }  // namespace ts

@@ -41,7 +41,7 @@ def test_library_exports_every_header_symbol():
     L = _lib()
     missing = [s for s in header_symbols() if not hasattr(L, s)]
     assert not missing, missing
-    assert L.ts_abi_version() == 102
+    assert L.ts_abi_version() == 103
 
 
 def test_workspace_queries_depend_on_shapes_only():
@@ -238,3 +238,16 @@ def _commit(L, **kw):
 def test_kv_commit_rejects(kw, code):
     L = _lib()
     assert _commit(L, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=None), EINVAL), (dict(W=0), EINVAL), (dict(W=4097), ENOTSUP), (dict(k=-1), EINVAL),
+    (dict(levels=4), EINVAL), (dict(head=None), EINVAL), (dict(T_max=0), EINVAL), (dict(T_max=65), EINVAL),
+    (dict(info=FAKE_ODD), EINVAL),
+])
+def test_ngram_tree_rejects(kw, code):
+    L = _lib()
+    a = dict(window=FAKE, W=1024, k=20, seed=7, head=FAKE, levels=3, T_max=24, parent=FAKE, tok=FAKE, info=FAKE)
+    a.update(kw)
+    assert L.ts_ngram_tree(a["window"], a["W"], a["k"], a["seed"], a["head"], a["levels"], a["T_max"], a["parent"],
+                           a["tok"], a["info"], None) == code
