@@ -28,7 +28,7 @@ unpinned".
 from .common import bf16_to_f64, ancestor_sets
 from .attention import verify_attention, draft_attention
 from .select import partial_kv_select, SelectResult
-from .penalty import penalty_sample, PenaltyResult
+from .penalty import penalty_sample, PenaltyResult, eta_sample, EtaResult
 from .accept import accept_path, kv_commit
 from .ngram import ngram_candidates, ngram_tree, splitmix64
 
@@ -41,6 +41,8 @@ __all__ = [
     "SelectResult",
     "penalty_sample",
     "PenaltyResult",
+    "eta_sample",
+    "EtaResult",
     "accept_path",
     "kv_commit",
     "ngram_candidates",

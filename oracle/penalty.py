@@ -25,6 +25,13 @@ Readings taken where the pages are silent:
 * Min-p boundary is inclusive: keep i iff p_i >= min_p * max(p).
 * Sampling: with caller-supplied u in [0,1), the token is the smallest id t
   whose cumulative renormalised probability (ascending ids) exceeds u.
+
+The eta-sampling variant (Appendix D.1: the pool is the tokens whose
+probability reaches eta, a quantity built from the entropy and two
+constants alpha and epsilon) replaces the top-p and min-p masks. Readings:
+eta = min(epsilon, alpha * exp(-H)) with H = -sum p ln p in nats (the form of
+the truncation-sampling paper the citation map lists), and the most probable
+token is always kept, so the pool is {i : p_i >= min(eta, max p)}.
 """
 
 from dataclasses import dataclass
@@ -100,3 +107,47 @@ def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None):
             # u < 1 and the kept mass sums to 1; the guard covers rounding.
             token[r] = int(hits[0]) if len(hits) else int(np.nonzero(kr)[0][-1])
     return PenaltyResult(z=z, p=p, keep=keep, probs=probs, token=token, excl_mass=excl, ratio=ratio)
+
+
+@dataclass
+class EtaResult:
+    z: np.ndarray        # float64 [rows][V]
+    p: np.ndarray        # float64 [rows][V]
+    keep: np.ndarray     # bool [rows][V]
+    probs: np.ndarray    # float64 [rows][V]
+    token: np.ndarray    # int64 [rows]; -1 when no u was given
+    entropy: np.ndarray  # float64 [rows]; H in nats
+    eta: np.ndarray      # float64 [rows]
+    ratio: np.ndarray    # float64 [rows][V]; p_i / min(eta, max p), 1 at the cutoff
+
+
+def eta_sample(logits, window, penalty, temperature, epsilon, alpha, u=None):
+    """The logit pass with eta-sampling in place of top-p and min-p."""
+    x = np.asarray(logits, dtype=np.float64)
+    rows, V = x.shape
+    win = np.asarray(window, dtype=np.int64)
+    if win.ndim == 1:
+        win = np.broadcast_to(win, (rows, win.shape[0]))
+    if not (penalty > 0 and temperature > 0 and 0 < epsilon <= 1 and alpha >= 0):
+        raise ValueError("parameter out of range")
+    out = dict(z=np.empty_like(x), p=np.empty_like(x), keep=np.zeros(x.shape, dtype=bool), probs=np.zeros_like(x),
+               token=np.full(rows, -1, dtype=np.int64), entropy=np.empty(rows), eta=np.empty(rows),
+               ratio=np.empty_like(x))
+    for r in range(rows):
+        zr = apply_penalty(x[r], win[r], V, float(penalty)) / float(temperature)
+        e = np.exp(zr - zr.max())
+        pr = e / e.sum()
+        nz = pr > 0
+        H = -np.sum(pr[nz] * np.log(pr[nz]))
+        eta = min(float(epsilon), float(alpha) * np.exp(-H))
+        thr = min(eta, pr.max())
+        kr = pr >= thr
+        qr = np.where(kr, pr, 0.0)
+        qr = qr / qr.sum()
+        out["z"][r], out["p"][r], out["keep"][r], out["probs"][r] = zr, pr, kr, qr
+        out["entropy"][r], out["eta"][r], out["ratio"][r] = H, eta, pr / thr
+        if u is not None:
+            cdf = np.cumsum(qr)
+            hits = np.nonzero(cdf > float(u[r]))[0]
+            out["token"][r] = int(hits[0]) if len(hits) else int(np.nonzero(kr)[0][-1])
+    return EtaResult(**out)

@@ -133,3 +133,58 @@ def test_shared_window_equals_per_row_window():
     b = _run(x["logits"], np.broadcast_to(x["window"], (3, 64)).copy())
     np.testing.assert_array_equal(a.z, b.z)
     np.testing.assert_array_equal(a.keep, b.keep)
+
+
+# ---- eta-sampling variant ----
+
+from oracle import eta_sample  # noqa: E402
+
+
+def test_eta_entropy_matches_scipy():
+    from scipy.stats import entropy
+    x = penalty_inputs(31, 4, 5000, 64)
+    r = eta_sample(x["logits"], x["window"], 1.2, 1.0, 3e-4, 0.0173, x["u"])
+    for i in range(4):
+        assert abs(r.entropy[i] - entropy(r.p[i])) <= 1e-9 * r.entropy[i]
+        assert r.eta[i] == min(3e-4, 0.0173 * np.exp(-entropy(r.p[i]))) or \
+            abs(r.eta[i] - min(3e-4, 0.0173 * np.exp(-entropy(r.p[i])))) <= 1e-12
+
+
+@pytest.mark.parametrize("V", [10, 1000])
+def test_eta_uniform_row_closed_form(V):
+    # uniform probabilities: H = ln V, so eta = min(eps, alpha / V)
+    logits = np.zeros((1, V), dtype=np.float32)
+    r = eta_sample(logits, np.zeros(0, dtype=np.int32), 1.0, 1.0, 0.5, 0.9)
+    assert abs(r.entropy[0] - np.log(V)) <= 1e-12
+    assert abs(r.eta[0] - min(0.5, 0.9 / V)) <= 1e-15
+    assert r.keep.all()                                   # every p = 1/V >= 0.9 / V
+    np.testing.assert_allclose(r.probs[0], 1.0 / V, rtol=1e-12)
+
+
+def test_eta_two_level_row_closed_form():
+    # 4 tokens at logit ln 8 and 96 at 0: p_hi = 8/128, p_lo = 1/128
+    logits = np.zeros((1, 100), dtype=np.float32)
+    logits[0, :4] = np.log(8.0)
+    r = eta_sample(logits, np.zeros(0, dtype=np.int32), 1.0, 1.0, 1.0, 1.0)
+    z = 4 * 8 + 96
+    H = -(4 * (8 / z) * np.log(8 / z) + 96 * (1 / z) * np.log(1 / z))
+    assert abs(r.entropy[0] - H) <= 1e-6
+    eta = np.exp(-H)                                      # epsilon = 1 does not bind
+    assert abs(r.eta[0] - eta) <= 1e-8
+    assert (r.keep[0, :4].all() and not r.keep[0, 4:].any()) == (1 / z < eta <= 8 / z)
+
+
+def test_eta_keeps_the_top_token_when_eta_is_above_it():
+    logits = np.zeros((1, 50), dtype=np.float32)
+    logits[0, 7] = 0.5
+    r = eta_sample(logits, np.zeros(0, dtype=np.int32), 1.0, 1.0, 1.0, 1e6)   # eta = epsilon = 1 > max p
+    assert r.keep[0].sum() == 1 and r.keep[0, 7] and r.probs[0, 7] == 1.0
+
+
+def test_eta_with_alpha_zero_keeps_only_the_maximum_set():
+    x = penalty_inputs(32, 2, 3000, 32)
+    r = eta_sample(x["logits"], x["window"], 1.2, 1.0, 0.01, 0.0, x["u"])   # eta = 0: every token reaches it
+    assert r.keep.all()
+    q = penalty_sample(x["logits"], x["window"], 1.2, 1.0, 1.0, 0.0, x["u"])  # same as no truncation
+    np.testing.assert_allclose(r.probs, q.probs, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(r.token, q.token)
