@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--verify-only", action="store_true", help="time only the verification launches")
     ap.add_argument("--fused-scores", action="store_true",
                     help="verification also writes the selection scores; the selection reads them (no K pass)")
+    ap.add_argument("--eta", action="store_true",
+                    help="eta-sampling (epsilon 3e-4, alpha sqrt(epsilon)) in place of top-p and min-p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -218,7 +220,10 @@ def main():
         if e:
             e[3].record(stream)
         if not args.verify_only:
-            ts.penalty_sample(logits, window, 1.2, 1.0, 0.9, 0.05, u=u, out=z_out, token_out=token_out)
+            if args.eta:
+                ts.penalty_sample_eta(logits, window, 1.2, 1.0, 3e-4, 3e-4 ** 0.5, u=u, out=z_out, token_out=token_out)
+            else:
+                ts.penalty_sample(logits, window, 1.2, 1.0, 0.9, 0.05, u=u, out=z_out, token_out=token_out)
         if e:
             e[4].record(stream)
         if not args.verify_only:
@@ -280,7 +285,8 @@ def main():
         "config": {"workload": f"{args.config}-class {'GQA' if Hq != Hkv else 'MHA'} tree verification, "
                                f"{Hq} q / {Hkv} kv heads, d={d}, {n_ctx} context rows, T={T} tree nodes, {layers} layers",
                    "global_batch": 1, "seq_len": n_ctx, "tree_nodes": T, "layers": layers,
-                   "fused_scores": bool(args.fused_scores), "parallelism": "single-gpu"},
+                   "fused_scores": bool(args.fused_scores), "eta_sampling": bool(args.eta),
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "kernels_us": {"verify_per_layer": round(verify_us, 3), "draft_per_layer": round(draft_us, 3),

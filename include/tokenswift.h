@@ -245,6 +245,28 @@ int ts_penalty_sample(const float* logits, int32_t rows, int32_t V,
 size_t ts_penalty_sample_workspace_size(int32_t rows, int32_t V);
 
 /*
+ * ts_penalty_sample_eta -- the same pass with eta-sampling in place of top-p
+ * and min-p.
+ *
+ * TokenSwift summary Appendix D.1: eta-sampling's pool is the tokens whose
+ * probability reaches eta, a quantity built from the distribution's entropy
+ * and two constants alpha and epsilon; §D.2 reports TokenSwift under it.
+ * Here eta = min(epsilon, alpha * exp(-H)), H = -sum_i p_i ln p_i (nats), and
+ * the most probable token always stays:
+ *   keep(i) <=> p_i >= min(eta, max p);
+ * steps 1-3, 5 and 6 as for ts_penalty_sample.
+ *
+ *   0 < epsilon <= 1; alpha >= 0 and finite (alpha = 0 keeps every token).
+ *   Other arguments, outputs and the workspace as for ts_penalty_sample.
+ */
+int ts_penalty_sample_eta(const float* logits, int32_t rows, int32_t V,
+                          const int32_t* window, int32_t W, int64_t window_stride,
+                          float penalty, float temperature, float epsilon, float alpha,
+                          float* logits_out, uint8_t* keep, float* probs,
+                          const float* u, int32_t* token,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * ts_tree_accept -- the accepted path of a verified token tree.
  *
  * TokenSwift summary §3.1 (with Figure 2): after the target model verifies

@@ -17,6 +17,7 @@ from .binding import (
     partial_kv_select,
     partial_kv_select_scored,
     penalty_sample,
+    penalty_sample_eta,
     tree_accept,
     verify_attn,
     verify_attn_scored,
@@ -32,6 +33,7 @@ __all__ = [
     "partial_kv_select",
     "partial_kv_select_scored",
     "penalty_sample",
+    "penalty_sample_eta",
     "tree_accept",
     "kv_commit",
     "ngram_tree",

@@ -39,6 +39,8 @@ _SIGNATURES = {
     "ts_penalty_sample": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_i32, c_i64, c_f32, c_f32, c_f32, c_f32, c_vp, c_vp,
                                   c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ts_penalty_sample_workspace_size": (c_sz, [c_i32, c_i32]),
+    "ts_penalty_sample_eta": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_i32, c_i64, c_f32, c_f32, c_f32, c_f32, c_vp, c_vp,
+                                      c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ts_tree_accept": (c_i32, [c_i32p, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "ts_kv_commit": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
                              c_i64, c_i64, c_i64, c_i32, c_i32, c_vp]),
@@ -235,13 +237,8 @@ def partial_kv_select_scored(scores, k, v, n_ctx, n_sink, budget, n_recent, k_pa
     return sel_idx[:, :budget], k_part, v_part, n_part.value
 
 
-def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None, want_keep=True, want_probs=True,
-                   want_token=None, out=None, token_out=None, ws=None, stream=None):
-    """Contextual penalty + temperature + top-p + min-p (ts_penalty_sample).
-
-    logits [rows][V] fp32; window [rows][W] or [W] int32 (shared). Returns
-    (z, keep or None, probs or None, token or None).
-    """
+def _penalty_call(fn, filt, logits, window, penalty, temperature, u, want_keep, want_probs, want_token, out,
+                  token_out, ws, stream):
     rows, V = logits.shape
     dev = logits.device
     if window is None or window.numel() == 0:
@@ -267,11 +264,29 @@ def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None, w
     L = lib()
     need = L.ts_penalty_sample_workspace_size(rows, V)
     wst = _workspace(need, dev, ws)
-    rc = L.ts_penalty_sample(_ptr(logits), rows, V, _ptr(wptr), W, wstride, float(penalty), float(temperature),
-                             float(top_p), float(min_p), _ptr(z), _ptr(keep), _ptr(probs), _ptr(u), _ptr(token),
-                             _ptr(wst), need, _stream(stream))
-    _check("ts_penalty_sample", rc)
+    rc = getattr(L, fn)(_ptr(logits), rows, V, _ptr(wptr), W, wstride, float(penalty), float(temperature),
+                        float(filt[0]), float(filt[1]), _ptr(z), _ptr(keep), _ptr(probs), _ptr(u), _ptr(token),
+                        _ptr(wst), need, _stream(stream))
+    _check(fn, rc)
     return z, keep, probs, token
+
+
+def penalty_sample(logits, window, penalty, temperature, top_p, min_p, u=None, want_keep=True, want_probs=True,
+                   want_token=None, out=None, token_out=None, ws=None, stream=None):
+    """Contextual penalty + temperature + top-p + min-p (ts_penalty_sample).
+
+    logits [rows][V] fp32; window [rows][W] or [W] int32 (shared). Returns
+    (z, keep or None, probs or None, token or None).
+    """
+    return _penalty_call("ts_penalty_sample", (top_p, min_p), logits, window, penalty, temperature, u, want_keep,
+                         want_probs, want_token, out, token_out, ws, stream)
+
+
+def penalty_sample_eta(logits, window, penalty, temperature, epsilon, alpha, u=None, want_keep=True, want_probs=True,
+                       want_token=None, out=None, token_out=None, ws=None, stream=None):
+    """The same pass with eta-sampling in place of top-p and min-p (ts_penalty_sample_eta)."""
+    return _penalty_call("ts_penalty_sample_eta", (epsilon, alpha), logits, window, penalty, temperature, u,
+                         want_keep, want_probs, want_token, out, token_out, ws, stream)
 
 
 def tree_accept(parent, node_token, target, result=None, stream=None):

@@ -113,7 +113,7 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
 
 extern "C" {
 
-int ts_abi_version(void) { return 103; }
+int ts_abi_version(void) { return 104; }
 
 const char* ts_last_error(void) { return g_err; }
 
@@ -186,6 +186,56 @@ size_t ts_partial_kv_select_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq,
 }  // extern "C"
 
 namespace {
+
+// Shared by the two logit-pass entry points (top-p / min-p, or eta).
+int run_penalty(const char* who, const float* logits, int32_t rows, int32_t V, const int32_t* window, int32_t W,
+                int64_t window_stride, float penalty, float temperature, float top_p, float min_p, int eta_mode,
+                float eta_eps, float eta_alpha, float* logits_out, uint8_t* keep, float* probs, const float* u,
+                int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !logits_out) return fail(TS_EINVAL, "%s: null logits pointer", who);
+  if (rows < 1) return fail(TS_EINVAL, "%s: rows=%d must be >= 1", who, rows);
+  if (V < 1) return fail(TS_EINVAL, "%s: V=%d must be >= 1", who, V);
+  if (V > 262144) return fail(TS_ENOTSUP, "%s: V=%d exceeds 262144", who, V);
+  if (W < 0) return fail(TS_EINVAL, "%s: W=%d is negative", who, W);
+  if (W > 0 && !window) return fail(TS_EINVAL, "%s: window is null with W=%d", who, W);
+  if (window_stride < 0 || (window_stride > 0 && window_stride < W))
+    return fail(TS_EINVAL, "%s: window_stride=%lld must be 0 (shared) or >= W", who, (long long)window_stride);
+  if (!(penalty > 0.f) || std::isinf(penalty)) return fail(TS_EINVAL, "%s: penalty must be finite and > 0", who);
+  if (!(temperature > 0.f) || std::isinf(temperature)) return fail(TS_EINVAL, "%s: temperature must be finite and > 0", who);
+  if (token && !u) return fail(TS_EINVAL, "%s: token output needs u", who);
+  if (!aligned(logits, 4) || !aligned(logits_out, 4) || (probs && !aligned(probs, 4)) || (u && !aligned(u, 4)) ||
+      (token && !aligned(token, 4)) || (W > 0 && !aligned(window, 4)))
+    return fail(TS_EINVAL, "%s: float and int32 arrays must be 4-byte aligned", who);
+  const size_t need = ts::penalty_workspace_bytes(rows, V);
+  if (ws_bytes < need) return fail(TS_EWORKSPACE, "%s: workspace of %zu bytes, need %zu", who, ws_bytes, need);
+  if (need > 0 && (!ws || !aligned(ws, 256))) return fail(TS_EINVAL, "%s: workspace must be non-null and 256-byte aligned", who);
+
+  ts::PenaltyParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.logits = logits;
+  p.logits_out = logits_out;
+  p.window = window;
+  p.window_stride = window_stride;
+  p.rows = rows;
+  p.V = V;
+  p.W = W;
+  p.penalty = penalty;
+  p.temperature = temperature;
+  p.inv_temperature = 1.0f / temperature;
+  p.top_p = top_p;
+  p.min_p = min_p;
+  p.eta_mode = eta_mode;
+  p.eta_eps = eta_eps;
+  p.eta_alpha = eta_alpha;
+  p.keep = keep;
+  p.probs = probs;
+  p.u = u;
+  p.token = token;
+  p.ws = ws;
+  const hipError_t e = ts::launch_penalty(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ok();
+}
 
 // Shared by both selection entry points: q == nullptr means the scores are
 // given (scores_in) and no query pass runs.
@@ -319,48 +369,21 @@ int ts_penalty_sample(const float* logits, int32_t rows, int32_t V, const int32_
                       float* logits_out, uint8_t* keep, float* probs, const float* u, int32_t* token, void* ws,
                       size_t ws_bytes, void* stream) {
   const char* who = "ts_penalty_sample";
-  if (!logits || !logits_out) return fail(TS_EINVAL, "%s: null logits pointer", who);
-  if (rows < 1) return fail(TS_EINVAL, "%s: rows=%d must be >= 1", who, rows);
-  if (V < 1) return fail(TS_EINVAL, "%s: V=%d must be >= 1", who, V);
-  if (V > 262144) return fail(TS_ENOTSUP, "%s: V=%d exceeds 262144", who, V);
-  if (W < 0) return fail(TS_EINVAL, "%s: W=%d is negative", who, W);
-  if (W > 0 && !window) return fail(TS_EINVAL, "%s: window is null with W=%d", who, W);
-  if (window_stride < 0 || (window_stride > 0 && window_stride < W))
-    return fail(TS_EINVAL, "%s: window_stride=%lld must be 0 (shared) or >= W", who, (long long)window_stride);
-  if (!(penalty > 0.f) || std::isinf(penalty)) return fail(TS_EINVAL, "%s: penalty must be finite and > 0", who);
-  if (!(temperature > 0.f) || std::isinf(temperature)) return fail(TS_EINVAL, "%s: temperature must be finite and > 0", who);
   if (!(top_p >= 0.f && top_p <= 1.f)) return fail(TS_EINVAL, "%s: top_p must lie in [0, 1]", who);
   if (!(min_p >= 0.f && min_p <= 1.f)) return fail(TS_EINVAL, "%s: min_p must lie in [0, 1]", who);
-  if (token && !u) return fail(TS_EINVAL, "%s: token output needs u", who);
-  if (!aligned(logits, 4) || !aligned(logits_out, 4) || (probs && !aligned(probs, 4)) || (u && !aligned(u, 4)) ||
-      (token && !aligned(token, 4)) || (W > 0 && !aligned(window, 4)))
-    return fail(TS_EINVAL, "%s: float and int32 arrays must be 4-byte aligned", who);
-  const size_t need = ts::penalty_workspace_bytes(rows, V);
-  if (ws_bytes < need) return fail(TS_EWORKSPACE, "%s: workspace of %zu bytes, need %zu", who, ws_bytes, need);
-  if (need > 0 && (!ws || !aligned(ws, 256))) return fail(TS_EINVAL, "%s: workspace must be non-null and 256-byte aligned", who);
+  return run_penalty(who, logits, rows, V, window, W, window_stride, penalty, temperature, top_p, min_p, 0, 0.f, 0.f,
+                     logits_out, keep, probs, u, token, ws, ws_bytes, stream);
+}
 
-  ts::PenaltyParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.logits = logits;
-  p.logits_out = logits_out;
-  p.window = window;
-  p.window_stride = window_stride;
-  p.rows = rows;
-  p.V = V;
-  p.W = W;
-  p.penalty = penalty;
-  p.temperature = temperature;
-  p.inv_temperature = 1.0f / temperature;
-  p.top_p = top_p;
-  p.min_p = min_p;
-  p.keep = keep;
-  p.probs = probs;
-  p.u = u;
-  p.token = token;
-  p.ws = ws;
-  const hipError_t e = ts::launch_penalty(p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
-  return ok();
+int ts_penalty_sample_eta(const float* logits, int32_t rows, int32_t V, const int32_t* window, int32_t W,
+                          int64_t window_stride, float penalty, float temperature, float epsilon, float alpha,
+                          float* logits_out, uint8_t* keep, float* probs, const float* u, int32_t* token, void* ws,
+                          size_t ws_bytes, void* stream) {
+  const char* who = "ts_penalty_sample_eta";
+  if (!(epsilon > 0.f && epsilon <= 1.f)) return fail(TS_EINVAL, "%s: epsilon must lie in (0, 1]", who);
+  if (!(alpha >= 0.f) || std::isinf(alpha)) return fail(TS_EINVAL, "%s: alpha must be finite and >= 0", who);
+  return run_penalty(who, logits, rows, V, window, W, window_stride, penalty, temperature, 1.f, 0.f, 1, epsilon,
+                     alpha, logits_out, keep, probs, u, token, ws, ws_bytes, stream);
 }
 
 int ts_tree_accept(const int32_t* parent, int32_t T, const int32_t* node_token, const int32_t* target,

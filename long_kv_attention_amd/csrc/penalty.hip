@@ -37,6 +37,14 @@
 //           the kept mass (else from an ordered scan of the row by the first
 //           workgroup); then the chunk's keep mask and renormalised
 //           probabilities.
+// Eta-sampling variant (Appendix D.1: the pool is the tokens whose
+// probability reaches eta, built from the entropy and constants alpha and
+// epsilon): eta = min(epsilon, alpha exp(-H)), H in nats, and the most
+// probable token always stays, so the pool is p_i >= min(eta, max p), i.e.
+// z_i - max z >= ln(min(1, eta Z)). Pass 1 adds each chunk's sum of
+// exp(z - m_b) z, pass 2 merges it into H = ln Z + max z - (sum e z) / Z
+// (double) and runs the min-p machinery with that threshold and no top-p, on
+// the whole-row path (the threshold is not known when the lists are built).
 // The mass of one token is exp(z - max z) in fp32 taken to 2^-40 fixed point,
 // so every prefix mass is an exact integer sum, whatever the summation order.
 // The penalty and the temperature are applied as products with their fp32
@@ -104,11 +112,13 @@ namespace {
 //   pm   [rows][NBR_MAX] f32   chunk max of z
 //   ps   [rows][NBR_MAX] f32   chunk sum of exp(z - chunk max)
 //   pc   [rows][NBR_MAX] u32   chunk candidates (> CAP_B: the list overflowed)
+//   pz   [rows][NBR_MAX] f32   chunk sum of exp(z - chunk max) * z (eta mode)
 //   cand [rows][nb][CAP_B] u64 candidate sort keys
 struct PenWs {
   float* pm;
   float* ps;
   unsigned int* pc;
+  float* pz;
   u64* cand;
 };
 
@@ -121,13 +131,15 @@ __host__ __device__ inline PenWs carve(void* base, int rows) {
   w += round256((size_t)rows * NBR_MAX * 4);
   s.pc = reinterpret_cast<unsigned int*>(w);
   w += round256((size_t)rows * NBR_MAX * 4);
+  s.pz = reinterpret_cast<float*>(w);
+  w += round256((size_t)rows * NBR_MAX * 4);
   s.cand = reinterpret_cast<u64*>(w);
   return s;
 }
 
 size_t pen_ws_bytes(int rows, int V) {
   const int nb = penalty_blocks_per_row(rows, V);
-  return 3 * round256((size_t)rows * NBR_MAX * 4) + round256((size_t)rows * nb * CAP_B * 8);
+  return 4 * round256((size_t)rows * NBR_MAX * 4) + round256((size_t)rows * nb * CAP_B * 8);
 }
 
 // Chunk b of nb over ids [0, V): a multiple of 64 ids.
@@ -451,9 +463,25 @@ __global__ __launch_bounds__(PB) void pen_z_kernel(const PenaltyParams p, int nb
     mb = block_max(m, redf);
     sb = block_sum(m > -INFINITY ? s * __expf(m - mb) : 0.f, redf);
   }
+  // eta mode: the chunk's sum of exp(z - mb) * z (the entropy's numerator)
+  float szb = 0.f;
+  if (p.eta_mode) {
+    float sz = 0.f;
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) sz += v[u] > -INFINITY ? __expf(v[u] - mb) * v[u] : 0.f;
+    } else {
+      for (int i = i0 + tid; i < i1; i += PB) {   // the z this thread wrote above
+        const float w = z[i];
+        sz += w > -INFINITY ? __expf(w - mb) * w : 0.f;
+      }
+    }
+    szb = block_sum(sz, redf);
+  }
   // candidates z - mb >= ln(min_p), listed by one LDS atomic per wave step with takers
+  // (eta mode lists nothing: its threshold is known only in pass 2)
   const float ln_min_p = logf(p.min_p);   // -inf for min_p = 0
-  const bool listed = !(ln_min_p == -INFINITY && i1 - i0 > CAP_B);
+  const bool listed = !p.eta_mode && !(ln_min_p == -INFINITY && i1 - i0 > CAP_B);
   u64* out = ws.cand + ((int64_t)row * nb + blockIdx.x) * CAP_B;
   auto list_step = [&](int i, float w) {   // all lanes of the wave call it
     const bool take = i < i1 && w - mb >= ln_min_p;
@@ -494,6 +522,7 @@ __global__ __launch_bounds__(PB) void pen_z_kernel(const PenaltyParams p, int nb
     ws.pm[row * NBR_MAX + blockIdx.x] = mb;
     ws.ps[row * NBR_MAX + blockIdx.x] = sb;
     ws.pc[row * NBR_MAX + blockIdx.x] = listed ? s_n : 0xffffffffu;
+    ws.pz[row * NBR_MAX + blockIdx.x] = szb;
   }
 }
 
@@ -509,7 +538,7 @@ __global__ __launch_bounds__(PB) void pen_out_kernel(const PenaltyParams p, int 
   __shared__ u64 red64[NW], red64b[NW];
   __shared__ unsigned int redu[NW];
   __shared__ unsigned int s_cnt[NBR_MAX];
-  __shared__ float s_zmax;
+  __shared__ float s_zmax, s_lnthr;
   __shared__ double s_Z;
   __shared__ int s_over, s_low, s_k, s_first, s_last, s_tok, s_lastkept;
   __shared__ unsigned int s_n;
@@ -537,22 +566,32 @@ __global__ __launch_bounds__(PB) void pen_out_kernel(const PenaltyParams p, int 
     const float sb = lane < nb ? ws.ps[row * NBR_MAX + lane] : 0.f;
     const unsigned int cb = lane < nb ? ws.pc[row * NBR_MAX + lane] : 0u;
     const float zm = wave_reduce(mb, OpMax());
-    const double t = wave_reduce(mb > -INFINITY ? (double)sb * (double)__expf(mb - zm) : 0.0, OpAdd());
+    const double sc = mb > -INFINITY ? (double)__expf(mb - zm) : 0.0;
+    const double t = wave_reduce((double)sb * sc, OpAdd());
     const bool over = cb > (unsigned int)CAP_B;
     if (lane < nb) s_cnt[lane] = over ? 0u : cb;
     const u64 ob = __ballot(over);
+    float lnthr = 0.f;
+    if (p.eta_mode) {
+      const float zb = lane < nb ? ws.pz[row * NBR_MAX + lane] : 0.f;
+      const double ez = wave_reduce((double)zb * sc, OpAdd());
+      const double H = log(t) + (double)zm - ez / t;   // nats
+      const double eta = fmin((double)p.eta_eps, (double)p.eta_alpha * exp(-H));
+      lnthr = (float)log(fmin(1.0, eta * t));         // -inf when eta = 0
+    }
     if (lane == 0) {
       s_zmax = zm;
       s_Z = t;
       s_over = ob != 0ull;
+      s_lnthr = lnthr;
       s_n = 0u;
     }
   }
   bar();
   Cut c;
   c.zmax = s_zmax;
-  c.ln_min_p = logf(p.min_p);   // -inf for min_p = 0
-  c.all_top = p.top_p >= 1.0f;
+  c.ln_min_p = p.eta_mode ? s_lnthr : logf(p.min_p);   // -inf for min_p = 0
+  c.all_top = p.eta_mode || p.top_p >= 1.0f;
   c.cut = 0u;
   c.ties_kept = 0u;
   c.rank_ties = false;

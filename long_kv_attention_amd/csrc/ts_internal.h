@@ -73,6 +73,8 @@ struct PenaltyParams {
   int64_t window_stride;
   int32_t rows, V, W;
   float penalty, inv_temperature, temperature, top_p, min_p;
+  int32_t eta_mode;            // 1: eta-sampling replaces top-p and min-p
+  float eta_eps, eta_alpha;
   uint8_t* keep;
   float* probs;
   const float* u;

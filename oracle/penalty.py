@@ -145,7 +145,8 @@ def eta_sample(logits, window, penalty, temperature, epsilon, alpha, u=None):
         qr = np.where(kr, pr, 0.0)
         qr = qr / qr.sum()
         out["z"][r], out["p"][r], out["keep"][r], out["probs"][r] = zr, pr, kr, qr
-        out["entropy"][r], out["eta"][r], out["ratio"][r] = H, eta, pr / thr
+        with np.errstate(divide="ignore"):   # thr = 0 when alpha = 0: every ratio is +inf, far from the cutoff
+            out["entropy"][r], out["eta"][r], out["ratio"][r] = H, eta, pr / thr
         if u is not None:
             cdf = np.cumsum(qr)
             hits = np.nonzero(cdf > float(u[r]))[0]

@@ -41,7 +41,7 @@ def test_library_exports_every_header_symbol():
     L = _lib()
     missing = [s for s in header_symbols() if not hasattr(L, s)]
     assert not missing, missing
-    assert L.ts_abi_version() == 103
+    assert L.ts_abi_version() == 104
 
 
 def test_workspace_queries_depend_on_shapes_only():
@@ -251,3 +251,15 @@ def test_ngram_tree_rejects(kw, code):
     a.update(kw)
     assert L.ts_ngram_tree(a["window"], a["W"], a["k"], a["seed"], a["head"], a["levels"], a["T_max"], a["parent"],
                            a["tok"], a["info"], None) == code
+
+
+@pytest.mark.parametrize("eps,alpha,code", [(0.0, 0.1, EINVAL), (1.5, 0.1, EINVAL), (float("nan"), 0.1, EINVAL),
+                                            (0.1, -1.0, EINVAL), (0.1, float("inf"), EINVAL)])
+def test_penalty_sample_eta_rejects(eps, alpha, code):
+    L = _lib()
+    rc = L.ts_penalty_sample_eta(FAKE, 2, 1000, FAKE, 16, 16, 1.2, 1.0, eps, alpha, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 40, None)
+    assert rc == code
+    # the shared checks still run (V beyond the supported size)
+    assert L.ts_penalty_sample_eta(FAKE, 2, 300_000, FAKE, 16, 16, 1.2, 1.0, 0.1, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, 1 << 40, None) == ENOTSUP
