@@ -110,7 +110,7 @@ def main():
     n_part = n_sink + budget + n_recent
     V, W = cfg["V"], cfg["W"]
     rows_logits = T + Tq
-    parent = tree_parent("chain" if T <= 4 else "tokenswift", T)
+    parent = tree_parent("chain" if T <= 4 else ("wide" if T > 64 else "tokenswift"), T)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()

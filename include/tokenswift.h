@@ -54,8 +54,8 @@ extern "C" {
 #define TS_EWORKSPACE (-3) /* workspace smaller than the *_workspace_size() query            */
 #define TS_EHIP       (-4) /* the HIP runtime reported an error while launching               */
 
-/* Largest tree / draft-chain size: one 64-bit ancestor mask per node. */
-#define TS_MAX_TREE 64
+/* Largest tree / draft-chain size: two 64-bit ancestor words per node. */
+#define TS_MAX_TREE 128
 
 /*
  * ts_verify_attn -- tree-masked verification attention over the FULL cache.
@@ -75,7 +75,7 @@ extern "C" {
  *           T tree nodes' own keys/values at rows n_ctx..n_ctx+T-1 (the caller
  *           writes them before the call, as in any decode step).
  *   parent  (host) [T] int32: parent[0] = -1 (root), 0 <= parent[i] < i.
- *   Hq, Hkv Hq % Hkv == 0.      d: 64 or 128.      1 <= T <= 64.  n_ctx >= 0.
+ *   Hq, Hkv Hq % Hkv == 0.      d: 64 or 128.      1 <= T <= 128.  n_ctx >= 0.
  *   scale   softmax scale; <= 0 selects 1/sqrt(d).
  *   out     [Hq][T][d] float32, contiguous (row (h, i) at (h*T + i)*d).
  *   n_split number of cache chunks per KV head processed in parallel before
@@ -137,7 +137,7 @@ int ts_verify_attn_scored(const uint16_t* q, const uint16_t* k, const uint16_t* 
  *   q               [Hq][Tq][d] bf16.
  *   k_part, v_part  partial caches (layout above; strides s_head, s_pos) with
  *                   n_part rows then the Tq new tokens' rows.
- *   1 <= Tq <= 64.  Other arguments as for ts_verify_attn.
+ *   1 <= Tq <= 128.  Other arguments as for ts_verify_attn.
  */
 int ts_draft_attn(const uint16_t* q, const uint16_t* k_part, const uint16_t* v_part,
                   int64_t s_head, int64_t s_pos, int32_t n_part, int32_t Tq,
@@ -170,7 +170,7 @@ size_t ts_draft_attn_workspace_size(int32_t n_part, int32_t Tq, int32_t Hq, int3
  *           head); it is computed on the host from the scalars.
  *   scores  optional [Hkv][n_ctx] float32 output of sigma (NULL = not written).
  *
- *   q [Hq][T][d] bf16 contiguous, 1 <= T <= 64; d 64 or 128; n_sink, budget,
+ *   q [Hq][T][d] bf16 contiguous, 1 <= T <= 128; d 64 or 128; n_sink, budget,
  *   n_recent >= 0. The partial cache must not overlap the full cache.
  */
 int ts_partial_kv_select(const uint16_t* q, int32_t T, const uint16_t* k, const uint16_t* v,
@@ -283,14 +283,14 @@ int ts_penalty_sample_eta(const float* logits, int32_t rows, int32_t V,
  * the smaller node index); node 0 (the root) is always accepted.
  *
  *   parent      (host) [T] int32, a tree listed parents-first as for
- *               ts_verify_attn.   1 <= T <= 64.
+ *               ts_verify_attn.   1 <= T <= 128.
  *   node_token  [T] int32: the token of each node (node 0's is not read).
  *   target      [T] int32: the target model's token at each node.
  *   result      [T + 2] int32 output: result[0] = n = m + 1 nodes accepted,
  *               result[1] = target[a_m] (the next token, emitted after the
  *               accepted ones), result[2 .. 2+n) = a_0 = 0 < a_1 < ... < a_m,
  *               result[2+n .. 2+T) = -1.
- * One wave; no workspace. The host learns n only by reading result[0].
+ * Two waves; no workspace. The host learns n only by reading result[0].
  */
 int ts_tree_accept(const int32_t* parent, int32_t T, const int32_t* node_token,
                    const int32_t* target, int32_t* result, void* stream);
@@ -349,7 +349,7 @@ int ts_kv_commit(const int32_t* result, int32_t T, uint16_t* k, uint16_t* v,
  *
  *   window      [W] int32, 1 <= W <= 4096.     k >= 0.     seed: any.
  *   head_cand   [levels][3] int32 (NULL when levels == 0); 0 <= levels <= 3.
- *   T_max       1 <= T_max <= 64.
+ *   T_max       1 <= T_max <= 128.
  *   parent, node_token  [T_max] int32 outputs (parents-first tree as
  *               ts_verify_attn takes it); slots past T hold -1.
  *   info        [4] int32 output: T (nodes), chains with a node in the tree,

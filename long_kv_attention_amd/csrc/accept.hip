@@ -13,9 +13,10 @@
 //     layer and KV head, and the same rows are appended to the partial cache.
 //
 // Kernels:
-//   accept  one wave, lane i = node i: edge test, one ballot, validity as
-//           "no invalid edge among my ancestors" (ancestor masks from the
-//           host), then a wave max of (depth, -index).
+//   accept  two waves, thread i = node i (up to 128): edge test, one ballot
+//           per wave, validity as "no invalid edge among my ancestors" (two
+//           ancestor words per node from the host), then a max of
+//           (depth, -index) over both waves.
 //   commit  grid (Hkv, layers, {K, V}): a workgroup loads its slice's m + 1
 //           accepted rows into registers, waits for all of them, then stores
 //           them (destination rows can be later source rows, so every load
@@ -33,8 +34,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 static_assert(std::is_standard_layout<AcceptParams>::value, "kernarg offsets via offsetof");
 
-__global__ __launch_bounds__(64) void accept_kernel(const AcceptParams p) {
+__global__ __launch_bounds__(128) void accept_kernel(const AcceptParams p) {
+  __shared__ u64 s_ok[2];
+  __shared__ int s_key[2];
   const int i = threadIdx.x;
+  const int wave = i >> 6;
   const bool in = i < p.T;
   // p is the kernel's only argument, so it starts the kernarg segment; the
   // per-node tables are read there with lane-varying indices
@@ -44,25 +48,36 @@ __global__ __launch_bounds__(64) void accept_kernel(const AcceptParams p) {
   const int pi = in && i > 0 ? par[i] : 0;   // the host checked 0 <= parent[i] < i
   const bool ok = in && (i == 0 || p.node_token[i] == p.target[pi]);
   const u64 okm = __ballot(ok);
-  const u64 mine = in ? anc[i] : 0ull;
-  const bool valid = in && (mine & ~okm) == 0ull;
-  const int depth = __popcll(mine) - 1;
-  const int key = wave_reduce(valid ? (depth << 8) | (255 - i) : -1, OpMaxI());   // node 0 is always valid
+  if ((i & 63) == 0) s_ok[wave] = okm;
+  __syncthreads();
+  const u64 ok0 = s_ok[0], ok1 = s_ok[1];
+  const u64 m0 = in ? anc[2 * i] : 0ull, m1 = in ? anc[2 * i + 1] : 0ull;
+  const bool valid = in && (m0 & ~ok0) == 0ull && (m1 & ~ok1) == 0ull;
+  const int depth = __popcll(m0) + __popcll(m1) - 1;
+  const int wkey = wave_reduce(valid ? (depth << 8) | (255 - i) : -1, OpMaxI());
+  if ((i & 63) == 0) s_key[wave] = wkey;
+  __syncthreads();
+  const int key = s_key[0] > s_key[1] ? s_key[0] : s_key[1];   // node 0 is always valid
   const int best = 255 - (key & 255);
-  const u64 path = anc[best];
-  const int n = __popcll(path);
+  const u64 pa0 = anc[2 * best], pa1 = anc[2 * best + 1];
+  const int n = __popcll(pa0) + __popcll(pa1);
   if (i == 0) {
     p.result[0] = n;
     p.result[1] = p.target[best];
   }
   if (in) {
-    if ((path >> i) & 1ull) p.result[2 + __popcll(path & ((1ull << i) - 1ull))] = i;
+    const bool on = i < 64 ? ((pa0 >> i) & 1ull) != 0ull : ((pa1 >> (i - 64)) & 1ull) != 0ull;
+    if (on) {
+      const int rank = i < 64 ? __popcll(pa0 & ((1ull << i) - 1ull))
+                              : __popcll(pa0) + __popcll(pa1 & ((1ull << (i - 64)) - 1ull));
+      p.result[2 + rank] = i;
+    }
     if (i >= n) p.result[2 + i] = -1;
   }
 }
 
 constexpr int CT = 256;   // threads per commit workgroup
-constexpr int CPT = 4;    // 16-byte chunks per thread: 64 rows x 16 chunks (d = 128)
+constexpr int CPT = 8;    // 16-byte chunks per thread: 128 rows x 16 chunks (d = 128)
 
 __global__ __launch_bounds__(CT) void commit_kernel(const CommitParams p) {
   const int g = blockIdx.x;
@@ -99,12 +114,12 @@ __global__ __launch_bounds__(CT) void commit_kernel(const CommitParams p) {
   }
 }
 
-static_assert(CT * CPT >= 64 * 16, "one pass covers 64 rows of 16 chunks");
+static_assert(CT * CPT >= 128 * 16, "one pass covers 128 rows of 16 chunks");
 
 }  // namespace
 
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 

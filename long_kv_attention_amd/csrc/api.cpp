@@ -28,10 +28,11 @@ int ok() {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Ancestor-or-self masks of a token tree (TokenSwift summary, Appendix E:
-// each tree token attends only to its predecessors). Returns false when
+// each tree token attends only to its predecessors), two 64-bit words per
+// node (anc[2i] nodes 0-63, anc[2i+1] nodes 64-127). Returns false when
 // parent[] is not a tree listed parents-first.
 bool build_masks(const int32_t* parent, int32_t T, uint64_t* anc, char* why, size_t why_len) {
-  for (int i = 0; i < 64; ++i) anc[i] = 0;
+  for (int i = 0; i < 2 * TS_MAX_TREE; ++i) anc[i] = 0;
   if (parent[0] != -1) {
     snprintf(why, why_len, "parent[0] must be -1 (node 0 is the root), got %d", parent[0]);
     return false;
@@ -43,7 +44,9 @@ bool build_masks(const int32_t* parent, int32_t T, uint64_t* anc, char* why, siz
       snprintf(why, why_len, "parent[%d] = %d must lie in [0, %d)", i, pi, i);
       return false;
     }
-    anc[i] = anc[pi] | (1ull << i);
+    anc[2 * i] = anc[2 * pi];
+    anc[2 * i + 1] = anc[2 * pi + 1];
+    anc[2 * i + (i >> 6)] |= 1ull << (i & 63);
   }
   return true;
 }
@@ -103,7 +106,7 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
   }
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
   p.scale_log2e = sc * 1.4426950408889634f;
-  for (int i = 0; i < 64; ++i) p.anc[i] = anc[i];
+  for (int i = 0; i < 2 * TS_MAX_TREE; ++i) p.anc[i] = anc[i];
   const hipError_t e = ts::launch_attention(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(TS_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
@@ -113,7 +116,7 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
 
 extern "C" {
 
-int ts_abi_version(void) { return 104; }
+int ts_abi_version(void) { return 105; }
 
 const char* ts_last_error(void) { return g_err; }
 
@@ -136,7 +139,7 @@ int ts_verify_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int6
   int rc = check_attention(who, q, k, v, out, s_head, s_pos, n_ctx, T, Hq, Hkv, d, scale, n_split);
   if (rc) return rc;
   if (!parent) return fail(TS_EINVAL, "%s: parent is null", who);
-  uint64_t anc[64];
+  uint64_t anc[2 * TS_MAX_TREE];
   char why[160];
   if (!build_masks(parent, T, anc, why, sizeof(why))) return fail(TS_EINVAL, "%s: %s", who, why);
   return run_attention(who, q, k, v, s_head, s_pos, n_ctx, T, anc, Hq, Hkv, d, scale, out, nullptr, n_split, ws,
@@ -156,7 +159,7 @@ int ts_verify_attn_scored(const uint16_t* q, const uint16_t* k, const uint16_t* 
   if (ts::attn_row_blocks(T, Hq, Hkv) != 1)
     return fail(TS_ENOTSUP, "%s: the %d query rows of a KV head ((Hq/Hkv)*T) exceed the 256 that one workgroup sums",
                 who, (Hq / Hkv) * T);
-  uint64_t anc[64];
+  uint64_t anc[2 * TS_MAX_TREE];
   char why[160];
   if (!build_masks(parent, T, anc, why, sizeof(why))) return fail(TS_EINVAL, "%s: %s", who, why);
   return run_attention(who, q, k, v, s_head, s_pos, n_ctx, T, anc, Hq, Hkv, d, scale, out, scores, n_split, ws,
@@ -170,8 +173,12 @@ int ts_draft_attn(const uint16_t* q, const uint16_t* k_part, const uint16_t* v_p
   int rc = check_attention(who, q, k_part, v_part, out, s_head, s_pos, n_part, Tq, Hq, Hkv, d, scale, n_split);
   if (rc) return rc;
   // The drafting tokens form a chain: token t sees tokens 0..t.
-  uint64_t anc[64];
-  for (int i = 0; i < 64; ++i) anc[i] = (i < Tq) ? ((i == 63) ? ~0ull : ((1ull << (i + 1)) - 1)) : 0ull;
+  uint64_t anc[2 * TS_MAX_TREE];
+  for (int i = 0; i < TS_MAX_TREE; ++i) {   // token i sees tokens 0..i
+    const bool in = i < Tq;
+    anc[2 * i] = !in ? 0ull : (i >= 63 ? ~0ull : (1ull << (i + 1)) - 1);
+    anc[2 * i + 1] = !in || i < 64 ? 0ull : (i == 127 ? ~0ull : (1ull << (i - 63)) - 1);
+  }
   return run_attention(who, q, k_part, v_part, s_head, s_pos, n_part, Tq, anc, Hq, Hkv, d, scale, out, nullptr,
                        n_split, ws, ws_bytes, stream);
 }

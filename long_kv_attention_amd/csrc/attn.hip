@@ -88,7 +88,7 @@ struct Cfg {
   // f16 by that many waves: convert the tile once in LDS instead (one more
   // barrier per tile; measured: T = 64 shapes -6%, no gain at RG = 2).
   static constexpr bool V_SHARED = RG >= 3;
-  static constexpr int ANC_BYTES = 1024;  // ancestor words of the tree nodes (one full 64-lane copy)
+  static constexpr int ANC_BYTES = 2048;  // ancestor words of the tree nodes (two 64-lane copies)
   // fused scores: the row sums of row groups 1.. for row group 0 (32 positions per wave)
   static constexpr int SC_BYTES = SCORE && RG > 1 ? (RG - 1) * PG * 32 * 4 : 0;
   // At the end of a split each wave keeps the CT / PG channel tiles it merges
@@ -318,9 +318,11 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     // p is the kernel's only argument, so it starts the kernarg segment; its
     // ancestor words are read there (taking p's address would copy it to scratch)
     const unsigned char* kargs = (const unsigned char*)__builtin_amdgcn_kernarg_segment_ptr();
-    if (wave == 0)
-      dma16(buffer_desc(kargs + offsetof(AttnParams, anc), (unsigned int)(T * 8)), (unsigned int)(lane * 16),
-            ring_off + C::KV_BYTES + C::Q_BYTES);
+    if (wave == 0) {   // two words per node: one copy per 64 nodes
+      const i32x4 adesc = buffer_desc(kargs + offsetof(AttnParams, anc), (unsigned int)(T * 16));
+      dma16(adesc, (unsigned int)(lane * 16), ring_off + C::KV_BYTES + C::Q_BYTES);
+      if (T > 64) dma16(adesc, (unsigned int)(1024 + lane * 16), ring_off + C::KV_BYTES + C::Q_BYTES + 1024);
+    }
     constexpr int QD = C::ROWS_PER_BLOCK / C::ROWS_PER_DMA;   // copies of 1 KB
     const int q_rows = M - rt_blk * 16;
     for (int id = tid; id < C::ROWS_PER_BLOCK * C::NCH; id += C::NT)
@@ -511,13 +513,19 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int row = (rt0 + t) * 16 + l16;
-        const uint64_t m = reinterpret_cast<const uint64_t*>(alds)[row < M ? row % T : 0];
+        // bit j of win = tree node a0 + j visible to this row (two words per
+        // node: nodes 0-63, 64-127); the lane's positions lie in [a0, a0 + 20)
+        const int node = row < M ? row % T : 0;
+        const unsigned __int128 m = (unsigned __int128)reinterpret_cast<const uint64_t*>(alds)[2 * node] |
+                                    ((unsigned __int128)reinterpret_cast<const uint64_t*>(alds)[2 * node + 1] << 64);
+        const unsigned int win = a0 >= 0 ? (a0 < 128 ? (unsigned int)(m >> a0) : 0u)
+                                         : (-a0 < 32 ? (unsigned int)(m << -a0) : 0u);
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int a = a0 + 16 * pt + i;
-            const unsigned int bit = (unsigned int)(m >> ((unsigned int)a & 63u)) & 1u;
+            const unsigned int bit = (win >> (16 * pt + i)) & 1u;
             const unsigned int vis = (unsigned int)(a < 0) | ((unsigned int)(a < T) & bit);
             s[t][pt][i] = vis ? s[t][pt][i] : -INFINITY;
           }

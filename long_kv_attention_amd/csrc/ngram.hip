@@ -32,7 +32,7 @@ namespace {
 
 constexpr int NG_T = 1024;                  // threads
 constexpr int NG_SEG = NG_MAX_WINDOW / NG_T;  // window positions per thread in the scans
-constexpr int NG_MAX_NODES = 64;                      // largest tree
+constexpr int NG_MAX_NODES = 128;                     // largest tree
 constexpr int NG_MAX_CHAINS = (NG_MAX_NODES - 1) / 3 + 1;   // chains that can start inside a tree
 
 __device__ inline u64 splitmix64(u64 seed, u64 j) {

@@ -23,7 +23,7 @@ struct AttnParams {
   int32_t rows_per_split;  // cache rows per split (a multiple of 128)
   float scale_log2e;     // softmax scale * log2(e)
   float* scores;         // [Hkv][n_ctx] grouped scores of the committed rows, or null
-  uint64_t anc[64];      // anc[i] bit a set <=> tree node a is i or an ancestor of i
+  uint64_t anc[256];     // words 2i, 2i+1: bit a set <=> tree node a is i or an ancestor of i
 };
 
 // Automatic split count: a pure function of the shapes (so the workspace
@@ -90,8 +90,8 @@ struct AcceptParams {
   const int32_t* target;       // [T]
   int32_t* result;             // [T + 2]: n accepted, next token, path, -1 padding
   int32_t T;
-  int32_t parent[64];
-  uint64_t anc[64];            // ancestor-or-self masks
+  int32_t parent[128];
+  uint64_t anc[256];           // ancestor-or-self masks, two words per node
 };
 hipError_t launch_accept(const AcceptParams& p, hipStream_t stream);
 

@@ -48,6 +48,8 @@ def tree_parent(kind, T=None):
     * "tiny8": a root, a chain of depth 3 under it and 4 more children of the
       root: [-1, 0, 1, 2, 0, 0, 0, 0].
     * "chain": T nodes in a line (plain causal decode of T tokens).
+    * "wide": the same with the [1,9,9,9] head part (nodes 1-9, 10-18 under
+      node 1, 19-27 under node 10), then chains; 88 nodes hold 20 chains.
     * "tokenswift": the [1,3,3,3] head part along the top-1 path (nodes 1-3
       under the root, 4-6 under node 1, 7-9 under node 4), then reused
       4-gram continuations as chains of 3 nodes under the root until T nodes
@@ -57,6 +59,20 @@ def tree_parent(kind, T=None):
         return [-1, 0, 1, 2, 0, 0, 0, 0]
     if kind == "chain":
         return [-1] + list(range(T - 1))
+    if kind == "wide":
+        # [1,9,9,9]: nodes 1-9 under the root, 10-18 under node 1, 19-27 under
+        # node 10, then 4-gram chains of 3 under the root until T nodes
+        par = [-1] + [0] * 9 + [1] * 9 + [10] * 9
+        if T <= len(par):
+            return par[:T]
+        while len(par) < T:
+            prev = 0
+            for _ in range(3):
+                if len(par) >= T:
+                    break
+                par.append(prev)
+                prev = len(par) - 1
+        return par
     if kind == "tokenswift":
         head = [-1, 0, 0, 0, 1, 1, 1, 4, 4, 4]
         if T <= len(head):

@@ -41,7 +41,7 @@ def test_library_exports_every_header_symbol():
     L = _lib()
     missing = [s for s in header_symbols() if not hasattr(L, s)]
     assert not missing, missing
-    assert L.ts_abi_version() == 104
+    assert L.ts_abi_version() == 105
 
 
 def test_workspace_queries_depend_on_shapes_only():
@@ -51,7 +51,7 @@ def test_workspace_queries_depend_on_shapes_only():
     assert L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 1) == 0   # one split: no partials
     forced = L.ts_verify_attn_workspace_size(100_000, 24, 32, 8, 128, 7)
     assert forced == 7 * 8 * 96 * (128 * 2 + 8)   # f16 partial outputs + (m, l) per row
-    assert L.ts_verify_attn_workspace_size(100_000, 65, 32, 8, 128, 0) == 0   # unsupported -> 0
+    assert L.ts_verify_attn_workspace_size(100_000, 129, 32, 8, 128, 0) == 0   # unsupported -> 0
     assert L.ts_draft_attn_workspace_size(4164, 4, 32, 8, 128, 0) == L.ts_verify_attn_workspace_size(4164, 4, 32, 8, 128, 0)
     assert L.ts_partial_kv_select_workspace_size(100_000, 24, 32, 8, 128, 4096) >= 8 * 100_000 * 4
     # chunk partials plus 1024 candidate keys (8 bytes) per chunk; 28 rows -> 9 chunks per row
@@ -71,7 +71,7 @@ def _verify(L, **kw):
 @pytest.mark.parametrize("kw,code,text", [
     (dict(q=None), EINVAL, "null"),
     (dict(d=96), ENOTSUP, "head dim"),
-    (dict(T=65, parent=[-1] + list(range(64))), ENOTSUP, "65"),
+    (dict(T=129, parent=[-1] + list(range(128))), ENOTSUP, "129"),
     (dict(T=0, parent=[]), EINVAL, "at least one"),
     (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
     (dict(parent=[0, 0, 1]), EINVAL, "parent[0]"),
@@ -120,7 +120,7 @@ def test_verify_attn_scored_rejects(kw, code, text):
 
 def test_draft_attn_rejects():
     L = _lib()
-    assert L.ts_draft_attn(FAKE, FAKE, FAKE, 128 * 100, 128, 50, 65, 8, 2, 128, 0.0, FAKE, 0, None, 0, None) == ENOTSUP
+    assert L.ts_draft_attn(FAKE, FAKE, FAKE, 128 * 100, 128, 50, 129, 8, 2, 128, 0.0, FAKE, 0, None, 0, None) == ENOTSUP
     assert L.ts_draft_attn(FAKE, FAKE, None, 128 * 100, 128, 50, 4, 8, 2, 128, 0.0, FAKE, 0, None, 0, None) == EINVAL
     assert L.ts_draft_attn(FAKE, FAKE, FAKE, 128 * 100, 128, 50_000, 4, 8, 2, 128, 0.0, FAKE, 0, None, 0, None) == EWORKSPACE
 
@@ -138,7 +138,7 @@ def _select(L, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(sel=None), EINVAL), (dict(budget=-1), EINVAL), (dict(n_sink=-1), EINVAL), (dict(d=80), ENOTSUP),
-    (dict(T=70), ENOTSUP), (dict(Hq=7), EINVAL), (dict(sp_head=128 * 50), EINVAL), (dict(kp=FAKE_ODD), EINVAL),
+    (dict(T=130), ENOTSUP), (dict(Hq=7), EINVAL), (dict(sp_head=128 * 50), EINVAL), (dict(kp=FAKE_ODD), EINVAL),
     (dict(), EWORKSPACE),
 ])
 def test_partial_kv_select_rejects(kw, code):
@@ -213,7 +213,7 @@ def test_tree_accept_rejects():
     par = (ctypes.c_int32 * 3)(-1, 0, 1)
     assert L.ts_tree_accept(par, 3, FAKE, FAKE, None, None) == EINVAL
     assert L.ts_tree_accept(par, 0, FAKE, FAKE, FAKE, None) == EINVAL
-    assert L.ts_tree_accept(par, 65, FAKE, FAKE, FAKE, None) == ENOTSUP
+    assert L.ts_tree_accept(par, 129, FAKE, FAKE, FAKE, None) == ENOTSUP
     assert L.ts_tree_accept(par, 3, FAKE_ODD, FAKE, FAKE, None) == EINVAL
     bad = (ctypes.c_int32 * 3)(-1, 0, 2)
     assert L.ts_tree_accept(bad, 3, FAKE, FAKE, FAKE, None) == EINVAL
@@ -231,7 +231,7 @@ def _commit(L, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(result=None), EINVAL), (dict(T=0), EINVAL), (dict(T=65), ENOTSUP), (dict(d=96), ENOTSUP),
+    (dict(result=None), EINVAL), (dict(T=0), EINVAL), (dict(T=129), ENOTSUP), (dict(d=96), ENOTSUP),
     (dict(layers=0), EINVAL), (dict(s_pos=64), EINVAL), (dict(s_layer=0), EINVAL), (dict(k=FAKE_ODD), EINVAL),
     (dict(vp=None), EINVAL), (dict(n_part=41), EINVAL), (dict(sp_head=0), EINVAL), (dict(n_ctx=-1), EINVAL),
 ])
@@ -242,7 +242,7 @@ def test_kv_commit_rejects(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(window=None), EINVAL), (dict(W=0), EINVAL), (dict(W=4097), ENOTSUP), (dict(k=-1), EINVAL),
-    (dict(levels=4), EINVAL), (dict(head=None), EINVAL), (dict(T_max=0), EINVAL), (dict(T_max=65), EINVAL),
+    (dict(levels=4), EINVAL), (dict(head=None), EINVAL), (dict(T_max=0), EINVAL), (dict(T_max=129), EINVAL),
     (dict(info=FAKE_ODD), EINVAL),
 ])
 def test_ngram_tree_rejects(kw, code):

@@ -32,16 +32,16 @@ def _check_accept(parent, node, target):
     return res, path
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(40))
 def test_accept_random_trees(seed):
-    T = [1, 2, 3, 5, 8, 24, 37, 63, 64][seed % 9]
+    T = [1, 2, 3, 5, 8, 24, 37, 63, 64, 65, 100, 127, 128][seed % 13]
     parent = random_parent(seed, T)
     x = accept_inputs(seed, parent, vocab=2 + seed % 5, p_match=0.4 + 0.15 * (seed % 4))
     _check_accept(parent, x["node_token"], x["target"])
 
 
 @pytest.mark.parametrize("kind,T", [("tokenswift", 24), ("tokenswift", 64), ("chain", 64), ("chain", 1),
-                                    ("tiny8", 8)])
+                                    ("tiny8", 8), ("wide", 88), ("chain", 128), ("wide", 128)])
 @pytest.mark.parametrize("p_match", [0.0, 0.5, 1.0])
 def test_accept_tree_shapes(kind, T, p_match):
     parent = tree_parent(kind, T)
@@ -55,7 +55,8 @@ def _rand_bf16(shape, gen):
 
 @pytest.mark.parametrize("layers,Hkv,d,n_ctx,T,part,pad", [
     (1, 2, 128, 100, 24, True, 0), (3, 2, 64, 517, 8, True, 8), (4, 8, 128, 0, 64, False, 0),
-    (2, 1, 128, 33, 1, True, 16), (5, 3, 64, 1000, 64, True, 0),
+    (2, 1, 128, 33, 1, True, 16), (5, 3, 64, 1000, 64, True, 0), (2, 2, 128, 300, 128, True, 8),
+    (3, 2, 64, 99, 88, True, 0),
 ])
 def test_commit_matches_oracle(layers, Hkv, d, n_ctx, T, part, pad):
     banner(f"commit layers={layers} Hkv={Hkv} d={d} n_ctx={n_ctx} T={T} part={part} pad={pad}")
@@ -64,7 +65,7 @@ def test_commit_matches_oracle(layers, Hkv, d, n_ctx, T, part, pad):
     rows = n_ctx + T + 5
     kf, vf = _rand_bf16((layers, Hkv, rows, d + pad), gen), _rand_bf16((layers, Hkv, rows, d + pad), gen)
     k, v = kf[..., :d], vf[..., :d]
-    parent = tree_parent("tokenswift", T) if T > 1 else [-1]
+    parent = (tree_parent("wide", T) if T > 64 else tree_parent("tokenswift", T)) if T > 1 else [-1]
     x = accept_inputs(T, parent, vocab=3, p_match=0.8)
     res, path = _check_accept(parent, x["node_token"], x["target"])
     res_d = _i32(res)

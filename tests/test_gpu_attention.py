@@ -58,12 +58,19 @@ SHAPES = [
     (8, 2, 128, 65, "ts24"), (32, 8, 128, 1000, "chain4"), (12, 2, 128, 777, "ts24"), (32, 32, 128, 300, "ts24"),
     (40, 8, 128, 1500, "ts64"), (32, 8, 128, 2049, "ts64"), (8, 8, 64, 129, "rand17"), (6, 2, 64, 5000, "rand64"),
     (64, 2, 128, 333, "rand40"), (16, 1, 128, 96, "rand9"), (24, 4, 64, 4097, "ts24"),
+    # trees past 64 nodes (two ancestor words per node)
+    (8, 2, 128, 1000, "wide88"), (32, 8, 128, 3001, "wide88"), (8, 2, 64, 77, "rand128"), (4, 1, 128, 200, "chain128"),
+    (40, 8, 128, 500, "rand100"), (8, 2, 128, 64, "rand65"),
 ]
 
 
 def _tree(name, seed):
     if name == "chain4":
         return tree_parent("chain", 4)
+    if name.startswith("chain"):
+        return tree_parent("chain", int(name[5:]))
+    if name.startswith("wide"):
+        return tree_parent("wide", int(name[4:]))
     if name == "tiny8":
         return tree_parent("tiny8")
     if name.startswith("ts"):
@@ -123,7 +130,8 @@ def test_verify_rejects_bad_tree_on_device_path():
 
 
 FULL = [("8b", 24, "tokenswift", [0, 5]), ("8b", 64, "tokenswift", [3]), ("8b", 4, "chain", [7]),
-        ("1.5b", 24, "tokenswift", [1]), ("7b", 24, "tokenswift", [0, 31]), ("14b", 64, "tokenswift", [2])]
+        ("1.5b", 24, "tokenswift", [1]), ("7b", 24, "tokenswift", [0, 31]), ("14b", 64, "tokenswift", [2]),
+        ("8b", 88, "wide", [6])]
 
 
 @pytest.mark.parametrize("name,T,tree,heads", FULL, ids=[f"{f[0]}_T{f[1]}" for f in FULL])

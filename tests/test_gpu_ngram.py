@@ -35,7 +35,7 @@ def test_random_windows(seed):
     window = ngram_window(seed, W, vocab=vocab, repeat=0.1 + 0.1 * (seed % 8))
     k = [0, 1, 3, 20, 100][seed % 5]
     levels = seed % 4
-    T_max = [1, 10, 24, 64][seed % 4]
+    T_max = [1, 10, 24, 64, 128][seed % 5]
     banner(f"ngram W={W} vocab={vocab} k={k} levels={levels} T_max={T_max}")
     _check(window, k, 1000 + seed, HEAD[:levels], T_max)
 
@@ -56,3 +56,4 @@ def test_workload_window():
     window = ngram_window(3, 1024, vocab=128256, repeat=0.5, n_phrases=8)
     _check(window, 20, 123, HEAD, 24)
     _check(window, 20, 123, HEAD, 64)
+    _check(window, 40, 123, HEAD, 128)
