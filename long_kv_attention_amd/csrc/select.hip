@@ -401,11 +401,13 @@ __device__ inline void load_hist(unsigned int* hist, const unsigned int* src) {
   for (int i = 0; i < PER; ++i) reinterpret_cast<u32x4*>(hist)[threadIdx.x + i * NT] = v[i];
 }
 
-// Keys of rows j0 .. j0+RPT-1 (rows at or past c1 read as key 0 and are invalid).
+// Keys of rows j0 .. j0+RPT-1. Rows at or past c1 are invalid (every caller
+// tests j < c1) and read row c1 - 1 (c1 >= 1), so the loads issue without
+// branches.
 __device__ inline void load_keys(const float* sc, int j0, int c1, unsigned int (&key)[RPT]) {
   float v[RPT];
 #pragma unroll
-  for (int e = 0; e < RPT; ++e) v[e] = j0 + e < c1 ? sc[j0 + e] : 0.f;
+  for (int e = 0; e < RPT; ++e) v[e] = sc[min(j0 + e, c1 - 1)];
 #pragma unroll
   for (int e = 0; e < RPT; ++e) key[e] = f2key(v[e]);
 }
@@ -585,6 +587,7 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
   __shared__ unsigned int s_above, s_gt, s_tie, s_bin1, s_above1;
   const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = p.b_eff;
   const int n_sink_eff = min(p.n_sink, p.n_ctx);
   int32_t* out = p.sel_idx + (int64_t)g * p.budget;
@@ -592,41 +595,60 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
   int c0, c1;
   chunk_of(p, nb, blockIdx.x, &c0, &c1);
   const float* sc = p.scores + (int64_t)g * p.n_ctx;
-  unsigned int key[RPT];
-  load_keys(sc, c0 + RPT * tid, c1, key);   // in flight with the loads below
-  {
-    constexpr int PER = HIST2 / 4 / PT;
-    u32x4 v[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) v[i] = reinterpret_cast<const u32x4*>(ws.hist2 + g * HIST2)[tid + i * PT];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) reinterpret_cast<u32x4*>(hist)[tid + i * PT] = v[i];
+  // Every load the cut needs goes out at once: lane b of every wave takes
+  // block b's list length and higher-bin count, then the second-digit
+  // histogram, each wave the first 64 slots of the lists of blocks wave,
+  // wave + 4, ... (read before their lengths are known; slots past a list's
+  // end are dropped) and this block's keys.
+  const unsigned int* cand_g = ws.cand + (int64_t)g * p.n_ctx;
+  unsigned int cl = 0, hl = 0;   // lane b < nb: block b's list length, its keys in higher first-digit bins
+  if (lane < nb) {
+    const uint2 v = *reinterpret_cast<const uint2*>(ws.ccnt + (g * NB_MAX + lane) * 2);
+    cl = v.x;
+    hl = v.y;
   }
-  if (tid < 64) {   // list offsets: one wave scans the per-block list lengths
-    unsigned int c = 0;
+  constexpr int PER = HIST2 / 4 / PT;
+  u32x4 h2v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) h2v[i] = reinterpret_cast<const u32x4*>(ws.hist2 + g * HIST2)[tid + i * PT];
+  int lc0, lc1;   // lane b < nb: block b's chunk
+  chunk_of(p, nb, lane < nb ? lane : 0, &lc0, &lc1);
+  constexpr int SPEC = NB_MAX / (PT / 64);   // lists per wave
+  unsigned int spec[SPEC];
+#pragma unroll
+  for (int u = 0; u < SPEC; ++u) {
+    const int b = wave + u * (PT / 64);
+    if (b < nb) {
+      const int bc0 = __builtin_amdgcn_readlane(lc0, b);
+      spec[u] = cand_g[min(bc0 + lane, p.n_ctx - 1)];
+    }
+  }
+  unsigned int key[RPT];
+  load_keys(sc, c0 + RPT * tid, c1, key);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) reinterpret_cast<u32x4*>(hist)[tid + i * PT] = h2v[i];
+  // list offsets: every wave scans the list lengths (lanes >= nb hold 0)
+  unsigned int incl = cl;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  const unsigned int loff = incl - cl;   // lane b: offset of block b's list in the concatenation
+  const unsigned int n = __builtin_amdgcn_readlane(incl, 63);
+  if (wave == 0) {
     if (lane < nb) {
-      int b0, b1;
-      chunk_of(p, nb, lane, &b0, &b1);
-      seg_c0[lane] = (unsigned int)b0;
-      c = ws.ccnt[(g * NB_MAX + lane) * 2 + 0];
-      seg_hi[lane] = ws.ccnt[(g * NB_MAX + lane) * 2 + 1];
+      seg_off[lane] = loff;
+      seg_c0[lane] = (unsigned int)lc0;
+      seg_hi[lane] = hl;
     }
-    unsigned int incl = c;
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    if (lane < nb) seg_off[lane] = incl - c;
-    if (lane == 63) seg_off[nb] = incl;
+    if (lane == 63) seg_off[nb] = n;
     if (lane == 0) {
       s_gt = s_tie = 0;
       s_bin1 = ws.cut1[g * 2 + 0];
       s_above1 = ws.cut1[g * 2 + 1];
     }
   }
-  bar();
-  const unsigned int n = seg_off[nb];
-  const unsigned int* cand_g = ws.cand + (int64_t)g * p.n_ctx;
   auto seg_of = [&](unsigned int i) {   // list owning key i: the last b with seg_off[b] <= i
     int lo = 0, hi = nb - 1;
     while (lo < hi) {
@@ -641,19 +663,49 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
   };
   const bool in_lds = n <= (unsigned int)CAND_CAP;
   if (in_lds) {
+    // the speculative slots that lie inside their list, then the lists' slots
+    // past 64 in 64-slot pieces (piece q of the concatenation of those tails
+    // belongs to the first block whose pieces end after q)
+#pragma unroll
+    for (int u = 0; u < SPEC; ++u) {
+      const int b = wave + u * (PT / 64);
+      if (b < nb) {
+        const unsigned int len = __builtin_amdgcn_readlane(cl, b);
+        if ((unsigned int)lane < len) cand_l[__builtin_amdgcn_readlane(loff, b) + lane] = spec[u];
+      }
+    }
+    const unsigned int np = cl > 64 ? (cl - 1) / 64 : 0;   // pieces past the first 64 slots
+    unsigned int pend = np;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned int y = __shfl_up(pend, off);
+      if (lane >= off) pend += y;
+    }
+    const unsigned int n_pieces = __builtin_amdgcn_readlane(pend, 63);
     constexpr int BATCH = 8;
-    for (unsigned int i0 = tid; i0 < n; i0 += PT * BATCH) {
+    for (unsigned int q0 = wave; q0 < n_pieces; q0 += (PT / 64) * BATCH) {
       unsigned int v[BATCH];
+      int dst[BATCH];
 #pragma unroll
       for (int u = 0; u < BATCH; ++u) {
-        const unsigned int i = i0 + u * PT;
-        v[u] = i < n ? key_at(i) : 0u;
+        const unsigned int q = q0 + u * (PT / 64);
+        dst[u] = -1;
+        if (q < n_pieces) {
+          const int b = (int)popc64(__ballot(pend <= q));
+          const unsigned int i = 64u * (1u + q - (__builtin_amdgcn_readlane(pend, b) - __builtin_amdgcn_readlane(np, b))) +
+                                 (unsigned int)lane;
+          if (i < __builtin_amdgcn_readlane(cl, b)) {
+            v[u] = cand_g[__builtin_amdgcn_readlane(lc0, b) + i];
+            dst[u] = (int)(__builtin_amdgcn_readlane(loff, b) + i);
+          }
+        }
       }
 #pragma unroll
       for (int u = 0; u < BATCH; ++u)
-        if (i0 + u * PT < n) cand_l[i0 + u * PT] = v[u];
+        if (dst[u] >= 0) cand_l[dst[u]] = v[u];
     }
   }
+  bar();   // histogram, list offsets and lists in LDS
   // second digit from the head's histogram of the cut bin's keys
   unsigned int rank = (unsigned int)k - s_above1;   // rank of the cut key inside the first-digit bin
   find_bin<PT>(hist, HIST2, rank, tmp, &s_bin, &s_above);
@@ -712,10 +764,7 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
       const bool tie = j < c1 && key[e] == cut;
       if (gt || (tie && tie_i < need)) {
         const unsigned int idx = gt_i + min(tie_i, need);
-        if (idx < (unsigned int)k) {
-          out[idx] = j;
-          srcs[idx - base] = j;
-        }
+        if (idx < (unsigned int)k) srcs[idx - base] = j;
       }
       gt_i += gt;
       tie_i += tie;
@@ -728,6 +777,9 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
       *src = srcs[i];
       *dst = n_sink_eff + (int)base + i;
     });
+    // the indices go out after the row copies, whose loads would otherwise
+    // wait for these stores
+    for (int i = tid; i < (int)(end - base); i += PT) out[base + i] = srcs[i];
     bar();
   }
 }
