@@ -41,10 +41,16 @@
 // probability reaches eta, built from the entropy and constants alpha and
 // epsilon): eta = min(epsilon, alpha exp(-H)), H in nats, and the most
 // probable token always stays, so the pool is p_i >= min(eta, max p), i.e.
-// z_i - max z >= ln(min(1, eta Z)). Pass 1 adds each chunk's sum of
-// exp(z - m_b) z, pass 2 merges it into H = ln Z + max z - (sum e z) / Z
-// (double) and runs the min-p machinery with that threshold and no top-p, on
-// the whole-row path (the threshold is not known when the lists are built).
+// z_i - max z >= ln(min(1, eta Z)). Three launches, same grid:
+//   1. z     as above, plus each chunk's sum of exp(z - m_b) z (no lists: the
+//            threshold is not known yet);
+//   2. mass  every workgroup merges the partials into H = ln Z + max z -
+//            (sum e z) / Z (double) and the threshold, then stores its
+//            chunk's kept mass and last kept id;
+//   3. out   the row's kept mass W and the mass below the chunk (exact
+//            fixed-point sums), the chunk's keep mask and probabilities, and
+//            the token from the one workgroup whose chunk holds the crossing
+//            of u W (an ordered scan of that chunk only).
 // The mass of one token is exp(z - max z) in fp32 taken to 2^-40 fixed point,
 // so every prefix mass is an exact integer sum, whatever the summation order.
 // The penalty and the temperature are applied as products with their fp32
@@ -113,12 +119,16 @@ namespace {
 //   ps   [rows][NBR_MAX] f32   chunk sum of exp(z - chunk max)
 //   pc   [rows][NBR_MAX] u32   chunk candidates (> CAP_B: the list overflowed)
 //   pz   [rows][NBR_MAX] f32   chunk sum of exp(z - chunk max) * z (eta mode)
+//   pw   [rows][NBR_MAX] u64   chunk kept mass, fixed point (eta mode)
+//   pl   [rows][NBR_MAX] i32   chunk's last kept id, -1 if none (eta mode)
 //   cand [rows][nb][CAP_B] u64 candidate sort keys
 struct PenWs {
   float* pm;
   float* ps;
   unsigned int* pc;
   float* pz;
+  u64* pw;
+  int* pl;
   u64* cand;
 };
 
@@ -133,13 +143,18 @@ __host__ __device__ inline PenWs carve(void* base, int rows) {
   w += round256((size_t)rows * NBR_MAX * 4);
   s.pz = reinterpret_cast<float*>(w);
   w += round256((size_t)rows * NBR_MAX * 4);
+  s.pw = reinterpret_cast<u64*>(w);
+  w += round256((size_t)rows * NBR_MAX * 8);
+  s.pl = reinterpret_cast<int*>(w);
+  w += round256((size_t)rows * NBR_MAX * 4);
   s.cand = reinterpret_cast<u64*>(w);
   return s;
 }
 
 size_t pen_ws_bytes(int rows, int V) {
   const int nb = penalty_blocks_per_row(rows, V);
-  return 4 * round256((size_t)rows * NBR_MAX * 4) + round256((size_t)rows * nb * CAP_B * 8);
+  return 5 * round256((size_t)rows * NBR_MAX * 4) + round256((size_t)rows * NBR_MAX * 8) +
+         round256((size_t)rows * nb * CAP_B * 8);
 }
 
 // Chunk b of nb over ids [0, V): a multiple of 64 ids.
@@ -526,6 +541,68 @@ __global__ __launch_bounds__(PB) void pen_z_kernel(const PenaltyParams p, int nb
   }
 }
 
+// Ordered scan of ids [lo, hi) by the whole workgroup: the smallest id whose
+// kept mass, counted from `run` (the kept mass below lo) and inclusive,
+// exceeds target (INT_MAX if none), and in *last_out the last kept id of the
+// range (-1 if none). Stops at the sub-chunk that holds the crossing.
+// Scratch: red64[NW], redu[NW] and two LDS ints.
+__device__ inline int ordered_token(const float* z, int lo, int hi, u64 run, u64 target, const Cut& c, u64* red64,
+                                    unsigned int* redu, int* s_tok, int* s_lastkept, int* last_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    *s_tok = INT_MAX;
+    *s_lastkept = -1;
+  }
+  bar();
+  unsigned int tie_run = 0;
+  for (int s0 = lo; s0 < hi; s0 += SUBC) {
+    float v[RPT];
+    load_run(z, s0, hi, v);
+    unsigned int tie_i = c.rank_ties ? wave_tie_base(v, s0, hi, c.cut, redu, tie_run) : 0u;
+    u64 ev[RPT];
+    u64 esum = 0;
+    int last_kept = -1;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      const int i = seg_id(s0, e);
+      const bool k = keep_step(c, v[e], i < hi, tie_i);
+      ev[e] = k ? to_fix(__expf(v[e] - c.zmax)) : 0ull;
+      esum += ev[e];
+      if (k) last_kept = i;
+    }
+    for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);
+    if (lane == 0) red64[wave] = esum;
+    bar();
+    u64 acc = run, tot = 0;
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) acc += red64[w];
+      tot += red64[w];
+    }
+    bar();
+    int hit = INT_MAX;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) {
+      u64 incl = ev[e];   // inclusive prefix over the step's lanes
+      for (int off = 1; off < 64; off <<= 1) {
+        const u64 y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const u64 h = __ballot(ev[e] > 0ull && acc + incl > target);
+      if (h && hit == INT_MAX) hit = seg_id(s0, e) - lane + __ffsll((long long)h) - 1;
+      acc += __shfl(incl, 63);
+    }
+    if (lane == 0 && hit != INT_MAX) atomicMin(s_tok, hit);
+    if (last_kept >= 0) atomicMax(s_lastkept, last_kept);
+    bar();
+    run += tot;
+    const bool found = *s_tok != INT_MAX;
+    bar();
+    if (found) break;
+  }
+  *last_out = *s_lastkept;
+  return *s_tok;
+}
+
 // ---- pass 2: the row's cut, keep mask, probabilities and token ----
 constexpr int SPEC_R = 8;   // list entries per thread loaded together with the partials
 
@@ -538,7 +615,7 @@ __global__ __launch_bounds__(PB) void pen_out_kernel(const PenaltyParams p, int 
   __shared__ u64 red64[NW], red64b[NW];
   __shared__ unsigned int redu[NW];
   __shared__ unsigned int s_cnt[NBR_MAX];
-  __shared__ float s_zmax, s_lnthr;
+  __shared__ float s_zmax;
   __shared__ double s_Z;
   __shared__ int s_over, s_low, s_k, s_first, s_last, s_tok, s_lastkept;
   __shared__ unsigned int s_n;
@@ -571,27 +648,18 @@ __global__ __launch_bounds__(PB) void pen_out_kernel(const PenaltyParams p, int 
     const bool over = cb > (unsigned int)CAP_B;
     if (lane < nb) s_cnt[lane] = over ? 0u : cb;
     const u64 ob = __ballot(over);
-    float lnthr = 0.f;
-    if (p.eta_mode) {
-      const float zb = lane < nb ? ws.pz[row * NBR_MAX + lane] : 0.f;
-      const double ez = wave_reduce((double)zb * sc, OpAdd());
-      const double H = log(t) + (double)zm - ez / t;   // nats
-      const double eta = fmin((double)p.eta_eps, (double)p.eta_alpha * exp(-H));
-      lnthr = (float)log(fmin(1.0, eta * t));         // -inf when eta = 0
-    }
     if (lane == 0) {
       s_zmax = zm;
       s_Z = t;
       s_over = ob != 0ull;
-      s_lnthr = lnthr;
       s_n = 0u;
     }
   }
   bar();
   Cut c;
   c.zmax = s_zmax;
-  c.ln_min_p = p.eta_mode ? s_lnthr : logf(p.min_p);   // -inf for min_p = 0
-  c.all_top = p.eta_mode || p.top_p >= 1.0f;
+  c.ln_min_p = logf(p.min_p);   // -inf for min_p = 0
+  c.all_top = p.top_p >= 1.0f;
   c.cut = 0u;
   c.ties_kept = 0u;
   c.rank_ties = false;
@@ -936,58 +1004,146 @@ __global__ __launch_bounds__(PB) void pen_out_kernel(const PenaltyParams p, int 
 
   // radix-select path: the first workgroup scans the whole row, ids ascending
   if (blockIdx.x != 0) return;
-  if (tid == 0) {
-    s_tok = INT_MAX;
-    s_lastkept = -1;
+  int last_kept;
+  const int tok = ordered_token(z, 0, V, 0ull, target, c, red64, redu, &s_tok, &s_lastkept, &last_kept);
+  if (tid == 0) p.token[row] = tok != INT_MAX ? tok : last_kept;
+}
+
+// ---- eta mode, passes 2 and 3 ----
+// Row statistics from the chunk partials, computed by each calling wave (all
+// lanes get them): row max, mass Z (chunk sums rescaled to the row max, fixed
+// order) and the pool threshold ln(min(1, eta Z)). Both passes compute them
+// from the same partials in the same order, so they agree bit for bit.
+struct EtaStats {
+  float zmax, lnthr;
+};
+__device__ inline EtaStats eta_row_stats(const PenaltyParams& p, const PenWs& ws, int row, int nb) {
+  const int lane = threadIdx.x & 63;
+  const float mb = lane < nb ? ws.pm[row * NBR_MAX + lane] : -INFINITY;
+  const float sb = lane < nb ? ws.ps[row * NBR_MAX + lane] : 0.f;
+  const float zb = lane < nb ? ws.pz[row * NBR_MAX + lane] : 0.f;
+  const float zm = wave_reduce(mb, OpMax());
+  const double sc = mb > -INFINITY ? (double)__expf(mb - zm) : 0.0;
+  const double t = wave_reduce((double)sb * sc, OpAdd());
+  const double ez = wave_reduce((double)zb * sc, OpAdd());
+  const double H = log(t) + (double)zm - ez / t;   // nats
+  const double eta = fmin((double)p.eta_eps, (double)p.eta_alpha * exp(-H));
+  EtaStats r;
+  r.zmax = zm;
+  r.lnthr = (float)log(fmin(1.0, eta * t));   // -inf when eta = 0
+  return r;
+}
+
+// z of the chunk: in registers (ZR per thread, -inf past i1) when it fits,
+// the loads issued before the row statistics are formed.
+__device__ inline void load_chunk(const float* z, int i0, int i1, float (&v)[ZR]) {
+#pragma unroll
+  for (int u = 0; u < ZR; ++u) {
+    const int i = i0 + (int)threadIdx.x + u * PB;
+    v[u] = i < i1 ? z[i] : -INFINITY;
   }
+}
+
+// Pass 2: the chunk's kept mass (fixed point) and last kept id.
+__global__ __launch_bounds__(PB) void pen_eta_mass_kernel(const PenaltyParams p, int nb) {
+  __shared__ u64 red64[NW];
+  __shared__ int redi[NW];
+  const int row = blockIdx.y, tid = threadIdx.x;
+  const PenWs ws = carve(p.ws, p.rows);
+  int i0, i1;
+  chunk_of(p.V, nb, blockIdx.x, &i0, &i1);
+  const float* z = p.logits_out + (int64_t)row * p.V;
+  const bool in_regs = i1 - i0 <= ZR * PB;
+  float v[ZR];
+  if (in_regs) load_chunk(z, i0, i1, v);
+  const EtaStats st = eta_row_stats(p, ws, row, nb);
+  u64 m = 0;
+  int last = -1;
+  auto take = [&](int i, float w) {
+    if (w - st.zmax >= st.lnthr) {   // the keep test of the other passes
+      m += to_fix(__expf(w - st.zmax));
+      last = i;
+    }
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) {
+      const int i = i0 + tid + u * PB;
+      if (i < i1) take(i, v[u]);
+    }
+  } else {
+    strided_pass(z, i0, i1, take);
+  }
+  m = block_sum(m, red64);
+  last = wave_reduce(last, OpMaxI());
+  if ((tid & 63) == 0) redi[tid >> 6] = last;
   bar();
-  u64 run = 0;
-  unsigned int tie_run = 0;
-  for (int s0 = 0; s0 < V; s0 += SUBC) {
-    float v[RPT];
-    load_run(z, s0, V, v);
-    unsigned int tie_i = c.rank_ties ? wave_tie_base(v, s0, V, c.cut, redu, tie_run) : 0u;
-    u64 ev[RPT];
-    u64 esum = 0;
-    int last_kept = -1;
-#pragma unroll
-    for (int e = 0; e < RPT; ++e) {
-      const int i = seg_id(s0, e);
-      const bool k = keep_step(c, v[e], i < V, tie_i);
-      ev[e] = k ? to_fix(__expf(v[e] - c.zmax)) : 0ull;
-      esum += ev[e];
-      if (k) last_kept = i;
-    }
-    for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);
-    if (lane == 0) red64[wave] = esum;
-    bar();
-    u64 acc = run, tot = 0;
-    for (int w = 0; w < NW; ++w) {
-      if (w < wave) acc += red64[w];
-      tot += red64[w];
-    }
-    bar();
-    int hit = INT_MAX;
-#pragma unroll
-    for (int e = 0; e < RPT; ++e) {
-      u64 incl = ev[e];   // inclusive prefix over the step's lanes
-      for (int off = 1; off < 64; off <<= 1) {
-        const u64 y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const u64 h = __ballot(ev[e] > 0ull && acc + incl > target);
-      if (h && hit == INT_MAX) hit = seg_id(s0, e) - lane + __ffsll((long long)h) - 1;
-      acc += __shfl(incl, 63);
-    }
-    if (lane == 0 && hit != INT_MAX) atomicMin(&s_tok, hit);
-    if (last_kept >= 0) atomicMax(&s_lastkept, last_kept);
-    bar();
-    run += tot;
-    const bool found = s_tok != INT_MAX;
-    bar();
-    if (found) break;
+  if (tid == 0) {
+    for (int w = 0; w < NW; ++w) last = max(last, redi[w]);
+    ws.pw[row * NBR_MAX + blockIdx.x] = m;
+    ws.pl[row * NBR_MAX + blockIdx.x] = last;
   }
-  if (tid == 0) p.token[row] = s_tok != INT_MAX ? s_tok : s_lastkept;
+}
+
+// Pass 3: keep mask, probabilities and token of the chunk.
+__global__ __launch_bounds__(PB) void pen_eta_out_kernel(const PenaltyParams p, int nb) {
+  __shared__ u64 red64[NW];
+  __shared__ unsigned int redu[NW];
+  __shared__ int s_tok, s_lastkept;
+  const int row = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const PenWs ws = carve(p.ws, p.rows);
+  const int V = p.V;
+  int i0, i1;
+  chunk_of(V, nb, blockIdx.x, &i0, &i1);
+  const float* z = p.logits_out + (int64_t)row * V;
+  const bool in_regs = i1 - i0 <= ZR * PB;
+  float v[ZR];
+  if (in_regs && (p.keep || p.probs)) load_chunk(z, i0, i1, v);
+  const EtaStats st = eta_row_stats(p, ws, row, nb);
+  // kept mass of the row and below the chunk, the row's last kept id (every wave)
+  const u64 wb = lane < nb ? ws.pw[row * NBR_MAX + lane] : 0ull;
+  const int lb = lane < nb ? ws.pl[row * NBR_MAX + lane] : -1;
+  const u64 W = wave_reduce(wb, OpAdd());
+  const u64 below = wave_reduce(lane < (int)blockIdx.x ? wb : 0ull, OpAdd());
+  const u64 inside = __shfl(wb, (int)blockIdx.x);
+  const int last = wave_reduce(lb, OpMaxI());
+  Cut c;
+  c.zmax = st.zmax;
+  c.ln_min_p = st.lnthr;
+  c.all_top = true;
+  c.rank_ties = false;
+  c.cut = 0u;
+  c.ties_kept = 0u;
+  const float inv = (float)((double)FIX_SCALE / (double)W);
+  uint8_t* keep = p.keep ? p.keep + (int64_t)row * V : nullptr;
+  float* probs = p.probs ? p.probs + (int64_t)row * V : nullptr;
+  auto put = [&](int i, float w) {
+    const bool k = w - c.zmax >= c.ln_min_p;
+    if (keep) keep[i] = (uint8_t)k;
+    if (probs) probs[i] = k ? __expf(w - c.zmax) * inv : 0.f;
+  };
+  if (keep || probs) {
+    if (in_regs) {
+#pragma unroll
+      for (int u = 0; u < ZR; ++u) {
+        const int i = i0 + tid + u * PB;
+        if (i < i1) put(i, v[u]);
+      }
+    } else {
+      strided_pass(z, i0, i1, put);
+    }
+  }
+  if (!p.token) return;
+  // the smallest id whose inclusive kept mass exceeds u W; the last kept id
+  // when rounding leaves no mass above the target
+  const u64 target = (u64)((double)p.u[row] * (double)W);
+  if (target >= W) {   // the chunk holding the last kept id writes it (-1 from the first chunk if none)
+    if (tid == 0 && ((last >= i0 && last < i1) || (last < 0 && blockIdx.x == 0))) p.token[row] = last;
+  } else if (below <= target && target < below + inside) {   // workgroup-uniform
+    int lk;
+    const int tok = ordered_token(z, i0, i1, below, target, c, red64, redu, &s_tok, &s_lastkept, &lk);
+    if (tid == 0) p.token[row] = tok != INT_MAX ? tok : lk;
+  }
 }
 
 }  // namespace
@@ -998,7 +1154,13 @@ hipError_t launch_penalty(const PenaltyParams& p, hipStream_t stream) {
   const int nb = penalty_blocks_per_row(p.rows, p.V);
   const dim3 grid(nb, p.rows);
   hipLaunchKernelGGL(pen_z_kernel, grid, dim3(PB), 0, stream, p, nb);
-  if (p.keep || p.probs || p.token) hipLaunchKernelGGL(pen_out_kernel, grid, dim3(PB), 0, stream, p, nb);
+  if (!(p.keep || p.probs || p.token)) return hipGetLastError();
+  if (p.eta_mode) {
+    hipLaunchKernelGGL(pen_eta_mass_kernel, grid, dim3(PB), 0, stream, p, nb);
+    hipLaunchKernelGGL(pen_eta_out_kernel, grid, dim3(PB), 0, stream, p, nb);
+  } else {
+    hipLaunchKernelGGL(pen_out_kernel, grid, dim3(PB), 0, stream, p, nb);
+  }
   return hipGetLastError();
 }
 

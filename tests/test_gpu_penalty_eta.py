@@ -80,3 +80,14 @@ def test_exact_logit_ties_at_the_top():
     x["logits"][:, 100:110] = 30.0     # ten tied maxima (above every N(0, 4) draw), all kept whatever eta is
     keep, _ = _compare(x, 1.0, 1.0, 1.0, 1e6)
     assert np.all(keep[:, 100:110])
+
+
+@pytest.mark.parametrize("sigma", [1.0, 4.0])
+def test_u_at_the_ends(sigma):
+    """u = 0 takes the first kept id; u just below 1 the last kept one (the
+    target can round up to the whole kept mass)."""
+    x = penalty_inputs(64, 6, 128256, 1024, sigma=sigma)
+    x["u"] = np.array([0.0, 1e-12, 0.5, 1.0 - 2.0 ** -24, 1.0 - 2.0 ** -20, 0.999], dtype=np.float32)
+    keep, r = _compare(x, 1.2, 1.0, 3e-4, 0.0173)
+    tok_first = np.argmax(keep[0])
+    assert keep[0, tok_first]
