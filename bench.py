@@ -47,6 +47,8 @@ def parse():
                     help="eta-sampling (epsilon 3e-4, alpha sqrt(epsilon)) in place of top-p and min-p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-copy-bw", action="store_true",
+                    help="skip the streaming-copy bandwidth measured after the timed steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (reference for HBM byte counters)")
     return ap.parse_args()
@@ -258,6 +260,23 @@ def main():
     vb = verify_bytes(Hq, Hkv, d, n_ctx, T)
     achieved = vb / (verify_us * 1e-6) / 1e9
 
+    # streaming-copy bandwidth measured in the same process after the timed
+    # region (a secondary denominator next to the vendor peak): device-to-device
+    # copies of 1 GiB, read + write bytes over event time
+    copy_gbps = None
+    if not args.no_copy_bw:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
+
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "verify_attn_traffic.json")
     if os.path.exists(tpath):
@@ -289,6 +308,10 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "stream_copy": None if copy_gbps is None else
+                       {"GBps": round(copy_gbps, 1), "bytes_per_copy": 2 * (1 << 30),
+                        "verify_frac_of_copy": round(achieved / copy_gbps, 4)},
+        "env": _gpu_env(torch),
         "kernels_us": {"verify_per_layer": round(verify_us, 3), "draft_per_layer": round(draft_us, 3),
                        "select_per_layer": round(select_us, 3), "penalty_per_step": round(penalty_us, 3),
                        "accept_commit_per_step": round(commit_us, 3), "ngram_tree_per_step": round(ngram_us, 3),
@@ -298,6 +321,32 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, T, n_ctx, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def _gpu_env(torch):
+    """Device name, ROCm / HIP / torch versions and the engine and memory
+    clocks' top DPM levels (read from sysfs; None where not readable)."""
+    import glob
+    import re
+    env = {"gpu": torch.cuda.get_device_name(0), "hip": torch.version.hip, "torch": torch.__version__, "rocm": None,
+           "sclk_max_mhz": None, "mclk_max_mhz": None}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name, key in (("pp_dpm_sclk", "sclk_max_mhz"), ("pp_dpm_mclk", "mclk_max_mhz")):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    levels = [int(m) for m in re.findall(r"(\d+)\s*Mhz", f.read(), re.I)]
+            except OSError:
+                continue
+            if levels:
+                env[key] = max(levels)
+        if env["sclk_max_mhz"] is not None:
+            break
+    return env
 
 
 def _attn_source_sha():
