@@ -101,6 +101,25 @@ def test_massive_ties_span_blocks(kind):
         _check(x, n_ctx, Hq, Hkv, 4, 5_000, 64, strict=True)
 
 
+def test_crowded_cut_bin_with_long_lists():
+    """About 5900 keys in the cut's first-digit bin (under the 8192 refined in
+    LDS) spread over all 30 blocks of a head: every block's list of cut-bin
+    keys runs past 64 entries (47 to 205), and the keys take only ~16 distinct
+    values, so the row order decides exactly."""
+    n_ctx, Hq, Hkv = 30_000, 8, 2
+    banner("select crowded cut bin")
+    x = attention_inputs(22, Hq, Hkv, 128, n_ctx, 4)
+    G = Hq // Hkv
+    rng = np.random.default_rng(22)
+    for g in range(Hkv):
+        qbar = bf16_to_f64(x["q"][g * G:(g + 1) * G]).sum(axis=(0, 1))
+        u = np.where(qbar >= 0, 3.0, -3.0)
+        rows = np.arange(7, n_ctx, 5)    # every fifth row: 6000 rows over all blocks
+        k = u[None, :] * (1.0 + 0.01 * rng.standard_normal((rows.size, 1)))
+        x["k"][g, rows] = bf16_round(k.astype(np.float32))
+    _check(x, n_ctx, Hq, Hkv, 4, 3000, 64, strict=True)
+
+
 def test_full_budget_draft_equals_verification():
     Hq, Hkv, d, n_ctx, Tq = 8, 2, 128, 1234, 4
     x = attention_inputs(13, Hq, Hkv, d, n_ctx, Tq)
