@@ -322,12 +322,10 @@ int run_select(const char* who, const uint16_t* q, int32_t T, int32_t Hq, const 
     p.scores = const_cast<float*>(scores_in);
     p.scores_given = 1;
   } else {
-    // workspace: scores (if not user-provided) | qbar | selection passes
+    // workspace: scores (if not user-provided) | selection passes
     const size_t score_bytes = ((size_t)Hkv * n_ctx * sizeof(float) + 255) / 256 * 256;
     p.scores = scores_out ? scores_out : reinterpret_cast<float*>(w);
     w += score_bytes;
-    p.qbar = reinterpret_cast<float*>(w);
-    w += ((size_t)Hkv * d * sizeof(float) + 255) / 256 * 256;
   }
   p.sel_ws = reinterpret_cast<int32_t*>(w);
   *n_part_out = n_part;

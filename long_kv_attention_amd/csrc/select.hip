@@ -9,10 +9,12 @@
 // sink U selected U recent.
 //
 // Kernels (one stream, in order):
-//   1. prologue  grid Hkv:  qbar_g in fp32; clear the head's histograms.
-//   2. score     grid (chunks, Hkv): one HBM pass over K. 16 lanes x 16 B per
-//                row (d=128), lane-local FMAs then a 16-lane reduction; the
-//                block also histograms the top 12 bits of each candidate's
+//   1. clear     grid Hkv: clears the head's histograms.
+//   2. score     grid (chunks, Hkv): qbar_g in fp32 from the group's query
+//                rows (copied to LDS while the first K tile is in flight),
+//                then one HBM pass over K. 16 lanes x 16 B per row (d=128),
+//                lane-local FMAs then a 16-lane reduction; the block also
+//                histograms the top 12 bits of each candidate's
 //                order-preserving key and adds its non-empty bins to the
 //                head's global histogram.
 //   3. cutbin    grid (nb, Hkv): every block finds the top-12-bit bin holding
@@ -29,8 +31,8 @@
 // Passes 3 and 4 read the L2-resident scores, not K.
 //
 // With the scores given (computed by the verification pass over the same
-// queries), passes 1 and 2 become a clear of the histograms and one read of
-// the scores that fills the first-digit histogram.
+// queries), pass 2 becomes one read of the scores that fills the first-digit
+// histogram.
 #include "ts_device.h"
 #include "ts_internal.h"
 
@@ -61,49 +63,6 @@ __device__ inline unsigned long long lanemask_lt() {
 }
 __device__ inline unsigned int popc64(unsigned long long x) { return (unsigned int)__popcll(x); }
 
-// qbar_g[c] = sum over the group's query rows (G heads x T queries) in fp32.
-// Each thread sums 8 channels of every 256/(D/8)-th row, then an LDS
-// reduction over the row slots (fixed order: deterministic).
-template <int D>
-__global__ __launch_bounds__(256) void select_prologue_kernel(const SelectParams p, unsigned int* hist,
-                                                              unsigned int* hist2) {
-  constexpr int LPR = D / 8;          // lanes per row
-  constexpr int RS = 256 / LPR;       // row slots
-  __shared__ float part[RS][D];
-  const int g = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int cg = tid % LPR, rs = tid / LPR;
-  const int rows = (p.Hq / p.Hkv) * p.T;
-  const uint16_t* qg = p.q + (int64_t)g * rows * D + cg * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int QB = 8;   // rows whose loads are in flight together
-  for (int r0 = rs; r0 < rows; r0 += RS * QB) {
-    u32x4 w[QB];
-#pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      const int r = r0 + u * RS;
-      w[u] = r < rows ? *reinterpret_cast<const u32x4*>(qg + (int64_t)r * D) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      acc[0] += bf16_lo(w[u].x); acc[1] += bf16_hi(w[u].x);
-      acc[2] += bf16_lo(w[u].y); acc[3] += bf16_hi(w[u].y);
-      acc[4] += bf16_lo(w[u].z); acc[5] += bf16_hi(w[u].z);
-      acc[6] += bf16_lo(w[u].w); acc[7] += bf16_hi(w[u].w);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) part[rs][cg * 8 + e] = acc[e];
-  for (int b = tid; b < HIST1; b += 256) hist[g * HIST1 + b] = 0u;
-  for (int b = tid; b < HIST2; b += 256) hist2[g * HIST2 + b] = 0u;
-  __syncthreads();
-  if (tid < D) {
-    float t = 0.f;
-    for (int q = 0; q < RS; ++q) t += part[q][tid];
-    p.qbar[g * D + tid] = t;
-  }
-}
-
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource (gfx9 layout): 48-bit base, stride 0, num_records bytes.
@@ -119,6 +78,13 @@ __device__ inline i32x4 buffer_desc(const void* base, unsigned int num_records) 
 // Callers order the LDS write with explicit vmcnt waits and barriers.
 __device__ inline void dma16_nt(i32x4 desc, unsigned int off, unsigned int soff, unsigned int lds_off) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
+}
+
+// The same copy with the default cache policy (data that other workgroups read too).
+__device__ inline void dma16(i32x4 desc, unsigned int off, unsigned int soff, unsigned int lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc),
                   "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
@@ -150,7 +116,10 @@ __device__ inline float row16_sum(float x) {
 // through an LDS ring of SC_STAGES tiles of SC_ROWS rows (asynchronous
 // copies), each row is scored from LDS by LPR lanes holding 8
 // channels (lane-local FMAs, then an LPR-lane reduction), and candidate rows
-// are histogrammed by the top 12 bits of their order-preserving key.
+// are histogrammed by the top 12 bits of their order-preserving key. Before
+// the first tile, the workgroup forms qbar_g itself: the group's query rows
+// are copied into the ring's last slot (free until the loop refills it)
+// ahead of the first K tile, so the sum runs while that tile is in flight.
 template <int D>
 __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const SelectParams p, unsigned int* ghist,
                                                                     int rows_per_block) {
@@ -172,7 +141,6 @@ __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const Selec
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sub = lane % LPR;
   const int rsub = lane / LPR;
-  for (int b = tid; b < HIST1; b += NT) lhist[b] = 0u;
 
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(r0 + rows_per_block, p.n_ctx);
@@ -191,14 +159,62 @@ __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const Selec
 #pragma unroll
     for (int jj = 0; jj < DPW; ++jj) dma16_nt(desc, loff, jj * jj_step, slot + (wave + jj * SC_WAVES) * 1024);
   };
-  // q-bar by the same copy, first, so the first tile's wait covers it (a plain
-  // load would make the compiler wait for every copy in flight before the loop)
-  if (wave == 0)
-    dma16_nt(buffer_desc(p.qbar + g * D, (unsigned int)(D * 4)), (unsigned int)(lane * 16), 0u,
-             (unsigned int)(uintptr_t)(const __attribute__((address_space(3))) void*)qlds);
+  // qbar_g: the group's query rows, QCH at a time, go to the ring's last slot
+  // by the same copy (a plain load would make the compiler wait for every
+  // copy in flight); the first round's copies go out before the first K tile
+  // so that a wait for them leaves that tile in flight.
+  static_assert(SC_STAGES == 2, "the first round's wait counts one K tile behind the query rows");
+  constexpr int QCH = TILE_BYTES / ROWB;   // query rows per round
+  constexpr int QRS = NT / LPR;            // row slots (LPR threads per row)
+  const int qrows = (p.Hq / p.Hkv) * p.T;
+  const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q + (int64_t)g * qrows * D);
+  const unsigned int qslot = ring_off + (unsigned int)((SC_STAGES - 1) * TILE_BYTES);
+  auto issue_q = [&](int c) {   // rows [c QCH, c QCH + nr) to the slot, densely
+    const unsigned int bytes = (unsigned int)(min(QCH, qrows - c * QCH) * ROWB);
+    const i32x4 desc = buffer_desc(qbase + (int64_t)c * QCH * ROWB, bytes);
+    for (int j = wave; j < (int)((bytes + 1023) / 1024); j += SC_WAVES)
+      dma16(desc, (unsigned int)(lane * 16), (unsigned int)(j * 1024), qslot + (unsigned int)(j * 1024));
+  };
+  issue_q(0);
+  if (ntiles > 0) issue(0);
+  float qa[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // channels [8 sub', 8 sub' + 8) of this thread's row slots
+  const int nqc = (qrows + QCH - 1) / QCH;
+  for (int c = 0; c < nqc; ++c) {
+    if (c > 0) {
+      __syncthreads();   // the previous round's rows are read
+      issue_q(c);
+    }
+    if (c == 0 && ntiles > 0) wait_vm<DPW>();   // copies retire in order: the rows, not the K tile
+    else wait_vm<0>();
+    __syncthreads();
+    const int nr = min(QCH, qrows - c * QCH);
+    for (int r = tid / LPR; r < nr; r += QRS) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(ring + (SC_STAGES - 1) * TILE_BYTES + r * ROWB + (tid % LPR) * 16);
+      qa[0] += bf16_lo(w.x); qa[1] += bf16_hi(w.x);
+      qa[2] += bf16_lo(w.y); qa[3] += bf16_hi(w.y);
+      qa[4] += bf16_lo(w.z); qa[5] += bf16_hi(w.z);
+      qa[6] += bf16_lo(w.w); qa[7] += bf16_hi(w.w);
+    }
+  }
+  // row slots of a wave, then the waves, in a fixed order (deterministic);
+  // the histogram's LDS holds the per-wave sums until it is cleared
 #pragma unroll
-  for (int t = 0; t < SC_STAGES - 1; ++t)
-    if (t < ntiles) issue(t);
+  for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qa[e] += __shfl_xor(qa[e], m);
+  static_assert(SC_WAVES * D <= HIST1, "per-wave sums fit the histogram's LDS");
+  float* qpart = reinterpret_cast<float*>(lhist);
+  if (lane < LPR)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qpart[wave * D + lane * 8 + e] = qa[e];
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.f;
+    for (int w = 0; w < SC_WAVES; ++w) t += qpart[w * D + tid];
+    qlds[tid] = t;
+  }
+  __syncthreads();
+  for (int b = tid; b < HIST1; b += NT) lhist[b] = 0u;   // ordered before the atomics by the first tile's barrier
 
   float* sc = p.scores + (int64_t)g * p.n_ctx;
   for (int t = 0; t < ntiles; ++t) {
@@ -285,7 +301,7 @@ __global__ __launch_bounds__(256) void select_hist_kernel(const SelectParams p, 
   }
 }
 
-// Workspace after the scores and qbar (all 256-byte aligned):
+// Workspace after the scores (all 256-byte aligned):
 //   hist   [Hkv][HIST1]     first-digit histogram (filled by the scoring pass)
 //   hist2  [Hkv][HIST2]     second-digit histogram of the cut bin's keys
 //   cut1   [Hkv][2]         the cut bin of the first digit and the keys above it
@@ -802,16 +818,16 @@ size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv,
   (void)T;
   (void)Hq;
   (void)budget;
-  return round256((size_t)Hkv * n_ctx * sizeof(float)) + round256((size_t)Hkv * d * sizeof(float)) +
-         sel_ws_bytes(Hkv, n_ctx);
+  (void)d;
+  return round256((size_t)Hkv * n_ctx * sizeof(float)) + sel_ws_bytes(Hkv, n_ctx);
 }
 
 size_t select_passes_workspace_bytes(int32_t n_ctx, int32_t Hkv) { return sel_ws_bytes(Hkv, n_ctx); }
 
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
+  hipLaunchKernelGGL(select_clear_kernel, dim3(p.Hkv), dim3(256), 0, stream, ws.hist, ws.hist2);
   if (p.scores_given) {
-    hipLaunchKernelGGL(select_clear_kernel, dim3(p.Hkv), dim3(256), 0, stream, ws.hist, ws.hist2);
     const int n_cand = p.cand_hi - p.cand_lo;
     if (n_cand > 0) {
       int chunks = (256 + p.Hkv - 1) / p.Hkv;
@@ -820,10 +836,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
       chunks = (n_cand + rpb - 1) / rpb;
       hipLaunchKernelGGL(select_hist_kernel, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, ws.hist, rpb);
     }
-  } else if (p.d == 128)
-    hipLaunchKernelGGL(select_prologue_kernel<128>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist, ws.hist2);
-  else
-    hipLaunchKernelGGL(select_prologue_kernel<64>, dim3(p.Hkv), dim3(256), 0, stream, p, ws.hist, ws.hist2);
+  }
   if (!p.scores_given && p.n_ctx > 0) {
     // about one scoring workgroup per compute unit over all heads, at least
     // one tile each

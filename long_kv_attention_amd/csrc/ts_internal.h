@@ -56,7 +56,6 @@ struct SelectParams {
   int64_t sp_head, sp_pos;
   float* scores;              // [Hkv][n_ctx] (user buffer or workspace; read-only when scores_given)
   int32_t scores_given;       // 1: scores come from the caller (no query pass)
-  float* qbar;                // [Hkv][d] workspace
   int32_t* sel_ws;            // workspace of the selection passes (histograms, cut-bin lists)
 };
 size_t select_workspace_bytes(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
