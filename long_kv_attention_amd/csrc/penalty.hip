@@ -544,55 +544,64 @@ __global__ __launch_bounds__(PB) void pen_z_kernel(const PenaltyParams p, int nb
 // Ordered scan of ids [lo, hi) by the whole workgroup: the smallest id whose
 // kept mass, counted from `run` (the kept mass below lo) and inclusive,
 // exceeds target (INT_MAX if none), and in *last_out the last kept id of the
-// range (-1 if none). Stops at the sub-chunk that holds the crossing.
-// Scratch: red64[NW], redu[NW] and two LDS ints.
+// scanned range (-1 if none). Sub-chunks of PB * RPT ids; thread t holds the
+// RPT consecutive ids from s0 + t * RPT, so one block scan of the threads'
+// kept masses (and, when the cut ranks its ties, one of their tie counts)
+// puts the crossing inside one thread, which walks its ids. Stops at the
+// sub-chunk that holds the crossing. Scratch: red64[NW], redu[NW], two LDS ints.
 __device__ inline int ordered_token(const float* z, int lo, int hi, u64 run, u64 target, const Cut& c, u64* red64,
                                     unsigned int* redu, int* s_tok, int* s_lastkept, int* last_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   if (tid == 0) {
     *s_tok = INT_MAX;
     *s_lastkept = -1;
   }
   bar();
-  unsigned int tie_run = 0;
+  unsigned int tie_run = 0;   // ties at the cut below the sub-chunk
   for (int s0 = lo; s0 < hi; s0 += SUBC) {
+    const int j0 = s0 + tid * RPT;
     float v[RPT];
-    load_run(z, s0, hi, v);
-    unsigned int tie_i = c.rank_ties ? wave_tie_base(v, s0, hi, c.cut, redu, tie_run) : 0u;
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) v[e] = z[min(j0 + e, hi - 1)];   // ids past hi are invalid below
+    unsigned int tie_i = 0;
+    if (c.rank_ties) {   // workgroup-uniform
+      unsigned int nt = 0;
+#pragma unroll
+      for (int e = 0; e < RPT; ++e) nt += (j0 + e < hi && f2key(v[e]) == c.cut) ? 1u : 0u;
+      unsigned int tot_t;
+      tie_i = tie_run + block_scan(nt, redu, &tot_t);
+      tie_run += tot_t;
+    }
     u64 ev[RPT];
-    u64 esum = 0;
-    int last_kept = -1;
+    u64 sum = 0;
+    int last = -1;
 #pragma unroll
     for (int e = 0; e < RPT; ++e) {
-      const int i = seg_id(s0, e);
-      const bool k = keep_step(c, v[e], i < hi, tie_i);
-      ev[e] = k ? to_fix(__expf(v[e] - c.zmax)) : 0ull;
-      esum += ev[e];
-      if (k) last_kept = i;
-    }
-    for (int m = 32; m >= 1; m >>= 1) esum += __shfl_xor(esum, m);
-    if (lane == 0) red64[wave] = esum;
-    bar();
-    u64 acc = run, tot = 0;
-    for (int w = 0; w < NW; ++w) {
-      if (w < wave) acc += red64[w];
-      tot += red64[w];
-    }
-    bar();
-    int hit = INT_MAX;
-#pragma unroll
-    for (int e = 0; e < RPT; ++e) {
-      u64 incl = ev[e];   // inclusive prefix over the step's lanes
-      for (int off = 1; off < 64; off <<= 1) {
-        const u64 y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+      const bool valid = j0 + e < hi;
+      const unsigned int key = f2key(v[e]);
+      bool top = c.all_top || key > c.cut;
+      if (!c.all_top && valid && key == c.cut) {   // ties ranked by id
+        top = !c.rank_ties || tie_i < c.ties_kept;
+        ++tie_i;
       }
-      const u64 h = __ballot(ev[e] > 0ull && acc + incl > target);
-      if (h && hit == INT_MAX) hit = seg_id(s0, e) - lane + __ffsll((long long)h) - 1;
-      acc += __shfl(incl, 63);
+      const bool k = valid && top && (v[e] - c.zmax >= c.ln_min_p);
+      ev[e] = k ? to_fix(__expf(v[e] - c.zmax)) : 0ull;
+      sum += ev[e];
+      if (k) last = j0 + e;
     }
-    if (lane == 0 && hit != INT_MAX) atomicMin(s_tok, hit);
-    if (last_kept >= 0) atomicMax(s_lastkept, last_kept);
+    u64 tot;
+    const u64 excl = run + block_scan(sum, red64, &tot);
+    if (sum > 0ull && excl <= target && target < excl + sum) {   // one thread at most
+      u64 acc = excl;
+      int hit = INT_MAX;
+#pragma unroll
+      for (int e = 0; e < RPT; ++e) {
+        acc += ev[e];
+        if (hit == INT_MAX && ev[e] > 0ull && acc > target) hit = j0 + e;
+      }
+      *s_tok = hit;
+    }
+    if (last >= 0) atomicMax(s_lastkept, last);
     bar();
     run += tot;
     const bool found = *s_tok != INT_MAX;
