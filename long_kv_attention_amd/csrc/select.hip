@@ -455,6 +455,11 @@ __device__ inline void copy_rows(const SelectParams& p, int g, int n, int item0,
         val[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
       }
     }
+    // one wait for all the loads: stores count in the same counter, so the
+    // compiler's wait before each store would otherwise hold it for the
+    // previous store's acknowledgement
+#pragma unroll
+    for (int u = 0; u < CP; ++u) asm volatile("" ::"v"(val[u]));
 #pragma unroll
     for (int u = 0; u < CP; ++u)
       if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
