@@ -13,7 +13,8 @@
 //     layer and KV head, and the same rows are appended to the partial cache.
 //
 // Kernels:
-//   accept  two waves, thread i = node i (up to 128): edge test, one ballot
+//   accept  two waves, thread i = node i (up to 128): the target tokens to
+//           LDS (one read of each), edge test, one ballot
 //           per wave, validity as "no invalid edge among my ancestors" (two
 //           ancestor words per node from the host), then a max of
 //           (depth, -index) over both waves.
@@ -37,6 +38,7 @@ static_assert(std::is_standard_layout<AcceptParams>::value, "kernarg offsets via
 __global__ __launch_bounds__(128) void accept_kernel(const AcceptParams p) {
   __shared__ u64 s_ok[2];
   __shared__ int s_key[2];
+  __shared__ int32_t s_target[128];   // the target tokens, read once (ancestors' and the winner's come from here)
   const int i = threadIdx.x;
   const int wave = i >> 6;
   const bool in = i < p.T;
@@ -46,7 +48,10 @@ __global__ __launch_bounds__(128) void accept_kernel(const AcceptParams p) {
   const int32_t* par = reinterpret_cast<const int32_t*>(ka + offsetof(AcceptParams, parent));
   const u64* anc = reinterpret_cast<const u64*>(ka + offsetof(AcceptParams, anc));
   const int pi = in && i > 0 ? par[i] : 0;   // the host checked 0 <= parent[i] < i
-  const bool ok = in && (i == 0 || p.node_token[i] == p.target[pi]);
+  const int32_t tok = in ? p.node_token[i] : 0;
+  if (in) s_target[i] = p.target[i];
+  __syncthreads();
+  const bool ok = in && (i == 0 || tok == s_target[pi]);
   const u64 okm = __ballot(ok);
   if ((i & 63) == 0) s_ok[wave] = okm;
   __syncthreads();
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(128) void accept_kernel(const AcceptParams p) {
   const int n = __popcll(pa0) + __popcll(pa1);
   if (i == 0) {
     p.result[0] = n;
-    p.result[1] = p.target[best];
+    p.result[1] = s_target[best];
   }
   if (in) {
     const bool on = i < 64 ? ((pa0 >> i) & 1ull) != 0ull : ((pa1 >> (i - 64)) & 1ull) != 0ull;
@@ -89,16 +94,21 @@ __global__ __launch_bounds__(CT) void commit_kernel(const CommitParams p) {
   n = n < 1 ? 1 : (n > p.T ? p.T : n);   // a foreign buffer cannot push the copies out of range
   const int64_t off = (int64_t)layer * p.s_layer + (int64_t)g * p.s_head;
   uint16_t* base = (is_v ? p.v : p.k) + off;
+  // the path entries, then the rows, each batch in flight together: items past
+  // n * nch read clamped, valid entries and rows and store nothing (the
+  // compiler would otherwise wait after each guarded load)
+  int a[CPT];
+#pragma unroll
+  for (int it = 0; it < CPT; ++it) {
+    const int r = (tid + it * CT) / nch;
+    a[it] = p.result[2 + (r < p.T ? r : p.T - 1)];
+  }
   u32x4 buf[CPT];
 #pragma unroll
   for (int it = 0; it < CPT; ++it) {
-    const int idx = tid + it * CT;
-    if (idx < n * nch) {
-      const int r = idx / nch, c = idx % nch;
-      int a = p.result[2 + r];
-      a = a < 0 ? 0 : (a >= p.T ? p.T - 1 : a);
-      buf[it] = *reinterpret_cast<const u32x4*>(base + (int64_t)(p.n_ctx + a) * p.s_pos + c * 8);
-    }
+    const int c = (tid + it * CT) % nch;
+    const int ar = a[it] < 0 ? 0 : (a[it] >= p.T ? p.T - 1 : a[it]);
+    buf[it] = *reinterpret_cast<const u32x4*>(base + (int64_t)(p.n_ctx + ar) * p.s_pos + c * 8);
   }
   __syncthreads();   // every source row is read before any row is overwritten
   uint16_t* pbase = p.k_part ? (is_v ? p.v_part : p.k_part) + (int64_t)layer * p.sp_layer + (int64_t)g * p.sp_head
