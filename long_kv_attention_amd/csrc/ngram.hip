@@ -81,6 +81,9 @@ __global__ __launch_bounds__(NG_T) void ngram_tree_kernel(const NgramParams p) {
 
   for (int i = tid; i < W; i += NG_T) w[i] = p.window[i];
   if (tid < NG_MAX_CHAINS) chain_of[tid] = -1;
+  // this thread's head candidate (node tid of the head part), read with the window
+  const int head_nodes = 1 + 3 * p.levels;
+  const int head_tok = tid >= 1 && tid < head_nodes && tid < p.T_max ? p.head[tid - 1] : -1;
   __syncthreads();
   const int root = w[W - 1];
 
@@ -200,7 +203,6 @@ __global__ __launch_bounds__(NG_T) void ngram_tree_kernel(const NgramParams p) {
 
   // the tree, one thread per node slot
   const int L = p.levels;
-  const int head_nodes = 1 + 3 * L;
   int T = head_nodes + 3 * kept;
   T = T < p.T_max ? T : p.T_max;
   if (tid < p.T_max) {
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(NG_T) void ngram_tree_kernel(const NgramParams p) {
       tok = root;
     } else if (tid < T && tid < head_nodes) {
       const int l = (tid - 1) / 3;
-      tok = p.head[tid - 1];
+      tok = head_tok;
       par = l == 0 ? 0 : 3 * (l - 1) + 1;
     } else if (tid < T) {
       const int m = tid - head_nodes, c = m / 3, pos = m % 3;
