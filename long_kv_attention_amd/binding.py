@@ -83,7 +83,28 @@ def _check(fn, rc):
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    if t is None:
+        return ctypes.c_void_p(0)
+    if t.device.type != "cuda":   # a host pointer handed to a kernel would fault the GPU
+        raise ValueError("tensors handed to the library must be on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dense(t, dtype, name, shape=None):
+    """t itself if it has the dtype, is contiguous and (when given) has the shape."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _out(out, shape, device, name="out"):
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    return _dense(out, torch.float32, name, shape)
 
 
 def _stream(stream):
@@ -111,12 +132,11 @@ def _workspace(nbytes, device, ws):
 
 def verify_attn(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, ws=None, stream=None):
     """Tree verification attention (ts_verify_attn). q [Hq][T][d] bf16; k, v [Hkv][rows][d] bf16."""
-    Hq, T, d = q.shape
+    Hq, T, d = _dense(q, torch.bfloat16, "q").shape
     Hkv = k.shape[0]
     s_head, s_pos = _cache_strides(k, v)
     par = (ctypes.c_int32 * T)(*[int(x) for x in parent])
-    if out is None:
-        out = torch.empty((Hq, T, d), dtype=torch.float32, device=q.device)
+    out = _out(out, (Hq, T, d), q.device)
     L = lib()
     need = L.ts_verify_attn_workspace_size(n_ctx, T, Hq, Hkv, d, n_split)
     wst = _workspace(need, q.device, ws)
@@ -141,12 +161,11 @@ def verify_attn_scored(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, s
 
     Returns (out [Hq][T][d] fp32, scores [Hkv][n_ctx] fp32).
     """
-    Hq, T, d = q.shape
+    Hq, T, d = _dense(q, torch.bfloat16, "q").shape
     Hkv = k.shape[0]
     s_head, s_pos = _cache_strides(k, v)
     par = (ctypes.c_int32 * T)(*[int(x) for x in parent])
-    if out is None:
-        out = torch.empty((Hq, T, d), dtype=torch.float32, device=q.device)
+    out = _out(out, (Hq, T, d), q.device)
     scores = _score_buffer(scores, Hkv, n_ctx, q.device)
     L = lib()
     need = L.ts_verify_attn_workspace_size(n_ctx, T, Hq, Hkv, d, n_split)
@@ -159,11 +178,10 @@ def verify_attn_scored(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, s
 
 def draft_attn(q, k_part, v_part, n_part, scale=0.0, n_split=0, out=None, ws=None, stream=None):
     """Draft attention over the partial cache (ts_draft_attn)."""
-    Hq, Tq, d = q.shape
+    Hq, Tq, d = _dense(q, torch.bfloat16, "q").shape
     Hkv = k_part.shape[0]
     s_head, s_pos = _cache_strides(k_part, v_part)
-    if out is None:
-        out = torch.empty((Hq, Tq, d), dtype=torch.float32, device=q.device)
+    out = _out(out, (Hq, Tq, d), q.device)
     L = lib()
     need = L.ts_draft_attn_workspace_size(n_part, Tq, Hq, Hkv, d, n_split)
     wst = _workspace(need, q.device, ws)
@@ -181,7 +199,7 @@ def partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, k_part=None, v_p
     ``extra_rows`` (room for the draft tokens' own keys/values).
     Returns (sel_idx [Hkv][budget] int32, k_part, v_part, n_part, scores or None).
     """
-    Hq, T, d = q.shape
+    Hq, T, d = _dense(q, torch.bfloat16, "q").shape
     Hkv = k.shape[0]
     s_head, s_pos = _cache_strides(k, v)
     dev = q.device
@@ -193,6 +211,8 @@ def partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, k_part=None, v_p
     sp_head, sp_pos = _cache_strides(k_part, v_part)
     if sel_idx is None:
         sel_idx = torch.empty((Hkv, max(budget, 1)), dtype=torch.int32, device=dev)
+    else:
+        _dense(sel_idx, torch.int32, "sel_idx", (Hkv, max(budget, 1)))
     if want_scores and scores is None:
         scores = torch.empty((Hkv, max(n_ctx, 1)), dtype=torch.float32, device=dev)
     L = lib()
@@ -226,6 +246,8 @@ def partial_kv_select_scored(scores, k, v, n_ctx, n_sink, budget, n_recent, k_pa
     sp_head, sp_pos = _cache_strides(k_part, v_part)
     if sel_idx is None:
         sel_idx = torch.empty((Hkv, max(budget, 1)), dtype=torch.int32, device=dev)
+    else:
+        _dense(sel_idx, torch.int32, "sel_idx", (Hkv, max(budget, 1)))
     L = lib()
     need = L.ts_partial_kv_select_scored_workspace_size(n_ctx, Hkv, d, budget)
     wst = _workspace(need, dev, ws)
@@ -239,8 +261,10 @@ def partial_kv_select_scored(scores, k, v, n_ctx, n_sink, budget, n_recent, k_pa
 
 def _penalty_call(fn, filt, logits, window, penalty, temperature, u, want_keep, want_probs, want_token, out,
                   token_out, ws, stream):
-    rows, V = logits.shape
+    rows, V = _dense(logits, torch.float32, "logits").shape
     dev = logits.device
+    if u is not None and (_dense(u, torch.float32, "u").numel() < rows):
+        raise ValueError(f"u must hold at least {rows} entries")
     if window is None or window.numel() == 0:
         W, wstride, wptr = 0, 0, None
     elif window.dim() == 1:
@@ -252,7 +276,7 @@ def _penalty_call(fn, filt, logits, window, penalty, temperature, u, want_keep, 
     if wptr is not None and (wptr.dtype != torch.int32 or wptr.stride(-1) != 1):
         raise ValueError("window must be int32 with contiguous rows")
     want_token = (u is not None) if want_token is None else want_token
-    z = torch.empty_like(logits) if out is None else out
+    z = torch.empty_like(logits) if out is None else _dense(out, torch.float32, "out", (rows, V))
     keep = torch.empty((rows, V), dtype=torch.uint8, device=dev) if want_keep else None
     probs = torch.empty((rows, V), dtype=torch.float32, device=dev) if want_probs else None
     if token_out is not None:

@@ -263,3 +263,23 @@ def test_penalty_sample_eta_rejects(eps, alpha, code):
     # the shared checks still run (V beyond the supported size)
     assert L.ts_penalty_sample_eta(FAKE, 2, 300_000, FAKE, 16, 16, 1.2, 1.0, 0.1, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    FAKE, 1 << 40, None) == ENOTSUP
+
+
+def test_binding_checks_tensors_before_any_launch():
+    """Host tensors, wrong dtypes and non-contiguous buffers are refused by
+    the binding itself (a host pointer handed to a kernel would fault)."""
+    import torch
+
+    q = torch.zeros((8, 4, 64), dtype=torch.bfloat16)
+    k = torch.zeros((2, 100, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on the GPU"):
+        binding.verify_attn(q, k, k, 96, [-1, 0, 1, 2])
+    with pytest.raises(TypeError, match="q must be"):
+        binding.verify_attn(q.float(), k, k, 96, [-1, 0, 1, 2])
+    with pytest.raises(ValueError, match="contiguous"):
+        binding.draft_attn(q.transpose(0, 1), k, k, 96)
+    logits = torch.zeros((4, 1024), dtype=torch.float32)
+    with pytest.raises(ValueError, match="contiguous"):
+        binding.penalty_sample(logits.t(), None, 1.2, 1.0, 0.9, 0.05)
+    with pytest.raises(ValueError, match="shape"):
+        binding.penalty_sample(logits, None, 1.2, 1.0, 0.9, 0.05, out=torch.zeros((4, 1000)))
