@@ -2,9 +2,10 @@
 
 Bar: max|O_gpu - O_ref| / max|O_ref| <= 2e-3 per call (bf16 inputs, fp32
 accumulation). Covers the small workload in full, ragged context lengths
-around the 64-row tiles, empty context, random trees of up to 64 nodes,
-MHA/GQA groupings, both head sizes, forced split counts, NaN-poisoned rows
-past the tree, and sampled KV heads of the full-size workloads.
+around the 64-row tiles, empty context, random and wide trees of up to 128
+nodes (two ancestor words past 64), MHA/GQA groupings, both head sizes,
+forced split counts, NaN-poisoned rows past the tree, and sampled KV heads of
+the full-size workloads (up to the 128-node tree at 100K rows).
 """
 
 import numpy as np
@@ -131,7 +132,7 @@ def test_verify_rejects_bad_tree_on_device_path():
 
 FULL = [("8b", 24, "tokenswift", [0, 5]), ("8b", 64, "tokenswift", [3]), ("8b", 4, "chain", [7]),
         ("1.5b", 24, "tokenswift", [1]), ("7b", 24, "tokenswift", [0, 31]), ("14b", 64, "tokenswift", [2]),
-        ("8b", 88, "wide", [6])]
+        ("8b", 88, "wide", [6]), ("8b", 128, "wide", [1])]
 
 
 @pytest.mark.parametrize("name,T,tree,heads", FULL, ids=[f"{f[0]}_T{f[1]}" for f in FULL])
