@@ -138,3 +138,10 @@ def test_min_p_set_larger_than_lds():
         x["logits"][r, hot] = rng.uniform(0.0, 1.0, 4500).astype(F32)
     x["window"][:] = -1
     _compare(x, 1.2, 1.0, 0.9, 0.05)
+
+
+def test_rows_of_a_128_node_tree():
+    """The logit rows of a step with a 128-node tree (128 + 4 draft rows)."""
+    banner("penalty 132 rows")
+    x = penalty_inputs(29, 132, 128256, 1024)
+    _compare(x, 1.2, 1.0, 0.9, 0.05)

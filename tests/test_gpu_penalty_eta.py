@@ -91,3 +91,10 @@ def test_u_at_the_ends(sigma):
     keep, r = _compare(x, 1.2, 1.0, 3e-4, 0.0173)
     tok_first = np.argmax(keep[0])
     assert keep[0, tok_first]
+
+
+def test_rows_of_a_128_node_tree():
+    """The logit rows of a step with a 128-node tree (128 + 4 draft rows)."""
+    banner("eta 132 rows")
+    x = penalty_inputs(65, 132, 128256, 1024)
+    _compare(x, 1.2, 1.0, 3e-4, 0.0173)
