@@ -251,6 +251,8 @@ def main():
         return sum(ev[s][i].elapsed_time(ev[s][j]) for s in range(args.steps)) / args.steps * 1e3  # us
 
     verify_us = avg(0, 1) / layers
+    per_step = sorted(ev[s][0].elapsed_time(ev[s][1]) * 1e3 / layers for s in range(args.steps))
+    verify_med = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     draft_us = avg(1, 2) / layers
     select_us = avg(2, 3) / layers
     penalty_us = avg(3, 4)
@@ -312,7 +314,9 @@ def main():
                        {"GBps": round(copy_gbps, 1), "bytes_per_copy": 2 * (1 << 30),
                         "verify_frac_of_copy": round(achieved / copy_gbps, 4)},
         "env": _gpu_env(torch),
-        "kernels_us": {"verify_per_layer": round(verify_us, 3), "draft_per_layer": round(draft_us, 3),
+        "kernels_us": {"verify_per_layer": round(verify_us, 3),
+                       "verify_per_layer_median": round(verify_med, 3), "verify_per_layer_min": round(per_step[0], 3),
+                       "verify_per_layer_max": round(per_step[-1], 3), "draft_per_layer": round(draft_us, 3),
                        "select_per_layer": round(select_us, 3), "penalty_per_step": round(penalty_us, 3),
                        "accept_commit_per_step": round(commit_us, 3), "ngram_tree_per_step": round(ngram_us, 3),
                        "verify_bytes_per_launch": vb},
