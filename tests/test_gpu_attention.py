@@ -111,7 +111,7 @@ def test_repeatable_bitwise():
 
 
 @pytest.mark.parametrize("Tq,n_part,Hq,Hkv", [(1, 4164, 32, 8), (4, 4164, 32, 8), (4, 8260, 40, 8), (4, 4164, 12, 2),
-                                              (3, 10, 8, 2), (5, 0, 8, 8)])
+                                              (3, 10, 8, 2), (5, 0, 8, 8), (64, 8260, 40, 8), (128, 4164, 32, 8)])
 def test_draft_attention(Tq, n_part, Hq, Hkv):
     banner(f"draft Tq={Tq} n_part={n_part} Hq={Hq} Hkv={Hkv}")
     x = attention_inputs(77 + n_part, Hq, Hkv, 128, n_part, Tq, cap=n_part + Tq + 32, poison_tail=True)
