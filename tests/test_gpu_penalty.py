@@ -145,3 +145,11 @@ def test_rows_of_a_128_node_tree():
     banner("penalty 132 rows")
     x = penalty_inputs(29, 132, 128256, 1024)
     _compare(x, 1.2, 1.0, 0.9, 0.05)
+
+
+def test_largest_vocabulary():
+    """V at the header's limit (262144 ids): the most chunks per row."""
+    banner("penalty V=262144")
+    x = penalty_inputs(30, 2, 262144, 1024)
+    _compare(x, 1.2, 1.0, 0.9, 0.05)
+    _compare(x, 1.2, 1.0, 0.5, 0.0)

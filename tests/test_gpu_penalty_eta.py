@@ -98,3 +98,10 @@ def test_rows_of_a_128_node_tree():
     banner("eta 132 rows")
     x = penalty_inputs(65, 132, 128256, 1024)
     _compare(x, 1.2, 1.0, 3e-4, 0.0173)
+
+
+def test_largest_vocabulary():
+    """V at the header's limit (262144 ids)."""
+    banner("eta V=262144")
+    x = penalty_inputs(66, 2, 262144, 1024)
+    _compare(x, 1.2, 1.0, 3e-4, 0.0173)
