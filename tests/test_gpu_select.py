@@ -120,6 +120,16 @@ def test_crowded_cut_bin_with_long_lists():
     _check(x, n_ctx, Hq, Hkv, 4, 3000, 64, strict=True)
 
 
+def test_long_chunks_span_several_sub_chunks():
+    """300K rows over 8 KV heads: each block's chunk (about 9400 rows) spans
+    three 4096-row sub-chunks in the cut-bin and emit passes (later keys
+    reloaded, output runs carried across sub-chunks); sampled heads."""
+    n_ctx, Hq, Hkv = 300_000, 32, 8
+    banner("select 300K rows")
+    x = attention_inputs(31, Hq, Hkv, 128, n_ctx, 24)
+    _check(x, n_ctx, Hq, Hkv, 4, 4096, 64, heads=[0, 7])
+
+
 def test_full_budget_draft_equals_verification():
     Hq, Hkv, d, n_ctx, Tq = 8, 2, 128, 1234, 4
     x = attention_inputs(13, Hq, Hkv, d, n_ctx, Tq)
