@@ -130,6 +130,16 @@ def test_long_chunks_span_several_sub_chunks():
     _check(x, n_ctx, Hq, Hkv, 4, 4096, 64, heads=[0, 7])
 
 
+@pytest.mark.parametrize("T,Hq,Hkv", [(128, 8, 2), (100, 40, 8)])
+def test_many_query_rows_per_head(T, Hq, Hkv):
+    """More than 256 query rows per KV head (512 and 500): the score pass sums
+    the group's queries in two rounds of 256 rows."""
+    n_ctx = 5000
+    banner(f"select T={T} Hq={Hq} Hkv={Hkv}")
+    x = attention_inputs(40 + T, Hq, Hkv, 128, n_ctx, T)
+    _check(x, n_ctx, Hq, Hkv, 4, 700, 64)
+
+
 def test_full_budget_draft_equals_verification():
     Hq, Hkv, d, n_ctx, Tq = 8, 2, 128, 1234, 4
     x = attention_inputs(13, Hq, Hkv, d, n_ctx, Tq)
