@@ -1044,12 +1044,29 @@ __device__ inline EtaStats eta_row_stats(const PenaltyParams& p, const PenWs& ws
 }
 
 // z of the chunk: in registers (ZR per thread, -inf past i1) when it fits,
-// the loads issued before the row statistics are formed.
-__device__ inline void load_chunk(const float* z, int i0, int i1, float (&v)[ZR]) {
+// the loads issued before the row statistics are formed. With `vec` (rows of
+// a multiple of 4 ids, 16-byte aligned, so chunk bounds are multiples of 4)
+// slot u holds id i0 + 4 (tid + (u / 4) PB) + u % 4 and four ids move per
+// access; otherwise slot u holds id i0 + tid + u PB.
+__device__ inline int chunk_slot(bool vec, int i0, int u) {
+  const int tid = (int)threadIdx.x;
+  return vec ? i0 + 4 * (tid + (u >> 2) * PB) + (u & 3) : i0 + tid + u * PB;
+}
+__device__ inline void load_chunk(const float* z, int i0, int i1, bool vec, float (&v)[ZR]) {
+  if (vec) {
 #pragma unroll
-  for (int u = 0; u < ZR; ++u) {
-    const int i = i0 + (int)threadIdx.x + u * PB;
-    v[u] = i < i1 ? z[i] : -INFINITY;
+    for (int q = 0; q < ZR / 4; ++q) {
+      const int g = chunk_slot(true, i0, 4 * q);
+      const f32x4 t = g < i1 ? *reinterpret_cast<const f32x4*>(z + g) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[4 * q + c] = t[c];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < ZR; ++u) {
+      const int i = chunk_slot(false, i0, u);
+      v[u] = i < i1 ? z[i] : -INFINITY;
+    }
   }
 }
 
@@ -1063,8 +1080,9 @@ __global__ __launch_bounds__(PB) void pen_eta_mass_kernel(const PenaltyParams p,
   chunk_of(p.V, nb, blockIdx.x, &i0, &i1);
   const float* z = p.logits_out + (int64_t)row * p.V;
   const bool in_regs = i1 - i0 <= ZR * PB;
+  const bool vec = (p.V & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits_out) & 15) == 0;
   float v[ZR];
-  if (in_regs) load_chunk(z, i0, i1, v);
+  if (in_regs) load_chunk(z, i0, i1, vec, v);
   const EtaStats st = eta_row_stats(p, ws, row, nb);
   u64 m = 0;
   int last = -1;
@@ -1077,7 +1095,7 @@ __global__ __launch_bounds__(PB) void pen_eta_mass_kernel(const PenaltyParams p,
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < ZR; ++u) {
-      const int i = i0 + tid + u * PB;
+      const int i = chunk_slot(vec, i0, u);
       if (i < i1) take(i, v[u]);
     }
   } else {
@@ -1106,8 +1124,11 @@ __global__ __launch_bounds__(PB) void pen_eta_out_kernel(const PenaltyParams p, 
   chunk_of(V, nb, blockIdx.x, &i0, &i1);
   const float* z = p.logits_out + (int64_t)row * V;
   const bool in_regs = i1 - i0 <= ZR * PB;
+  // four ids per access when the rows and the outputs allow it
+  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits_out) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.keep) & 3) == 0 && (reinterpret_cast<uintptr_t>(p.probs) & 15) == 0;
   float v[ZR];
-  if (in_regs && (p.keep || p.probs)) load_chunk(z, i0, i1, v);
+  if (in_regs && (p.keep || p.probs)) load_chunk(z, i0, i1, vec, v);
   const EtaStats st = eta_row_stats(p, ws, row, nb);
   // kept mass of the row and below the chunk, the row's last kept id (every wave)
   const u64 wb = lane < nb ? ws.pw[row * NBR_MAX + lane] : 0ull;
@@ -1132,10 +1153,28 @@ __global__ __launch_bounds__(PB) void pen_eta_out_kernel(const PenaltyParams p, 
     if (probs) probs[i] = k ? __expf(w - c.zmax) * inv : 0.f;
   };
   if (keep || probs) {
-    if (in_regs) {
+    if (in_regs && vec) {
+#pragma unroll
+      for (int q = 0; q < ZR / 4; ++q) {
+        const int g = chunk_slot(true, i0, 4 * q);
+        if (g < i1) {
+          unsigned int kb = 0;
+          f32x4 pr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float w = v[4 * q + e];
+            const bool k = w - c.zmax >= c.ln_min_p;
+            kb |= (k ? 1u : 0u) << (8 * e);
+            pr[e] = k ? __expf(w - c.zmax) * inv : 0.f;
+          }
+          if (keep) *reinterpret_cast<unsigned int*>(keep + g) = kb;
+          if (probs) *reinterpret_cast<f32x4*>(probs + g) = pr;
+        }
+      }
+    } else if (in_regs) {
 #pragma unroll
       for (int u = 0; u < ZR; ++u) {
-        const int i = i0 + tid + u * PB;
+        const int i = chunk_slot(false, i0, u);
         if (i < i1) put(i, v[u]);
       }
     } else {
