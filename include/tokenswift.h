@@ -50,7 +50,7 @@ extern "C" {
 /* Return codes. */
 #define TS_OK          0
 #define TS_EINVAL     (-1) /* null pointer, bad stride/alignment/shape/parameter, bad parent[] */
-#define TS_ENOTSUP    (-2) /* a shape the kernels do not handle (d not 64/128, T > 64, ...)   */
+#define TS_ENOTSUP    (-2) /* a shape the kernels do not handle (d not 64/128, T > 128, ...)  */
 #define TS_EWORKSPACE (-3) /* workspace smaller than the *_workspace_size() query            */
 #define TS_EHIP       (-4) /* the HIP runtime reported an error while launching               */
 
@@ -184,6 +184,16 @@ size_t ts_partial_kv_select_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq,
                                            int32_t d, int32_t budget);
 
 /*
+ * ts_partial_kv_rows -- the number of partial-cache rows (n_part) that
+ * ts_partial_kv_select and ts_partial_kv_select_scored write for these
+ * scalars: min(n_sink, n_ctx) + B' + the recent rows (TokenSwift summary
+ * §3.3: the initial pairs, the selected pairs, and the latest ones). A shape
+ * query (no device); the partial caches k_part / v_part must hold at least
+ * this many rows per head. Returns -1 when an argument is negative.
+ */
+int32_t ts_partial_kv_rows(int32_t n_ctx, int32_t n_sink, int32_t budget, int32_t n_recent);
+
+/*
  * ts_partial_kv_select_scored -- the select and gather steps of
  * ts_partial_kv_select on scores the caller provides (for instance those
  * ts_verify_attn_scored wrote in the same step), so no query or key pass runs.
@@ -211,9 +221,9 @@ size_t ts_partial_kv_select_scored_workspace_size(int32_t n_ctx, int32_t Hkv, in
  * ts_penalty_sample -- contextual penalty, temperature, min-p and top-p.
  *
  * TokenSwift summary §3.4: a repetition penalty restricted to the tokens of
- * the most recent W positions; Appendix D.1: top-p keeps the smallest set of
- * tokens whose cumulative probability exceeds top_p, min-p keeps tokens whose
- * probability reaches min_p times the largest; Reproducibility checklist,
+ * the most recent W positions; Appendix D.1: top-p samples from the shortest
+ * probability-ordered head of the vocabulary with mass above top_p, min-p
+ * from the tokens at or above min_p * max p; Reproducibility checklist,
  * Table 11: penalty 1.2, penalty length 1024, temperature 1.0, top-p 0.9,
  * min-p 0.05.
  *

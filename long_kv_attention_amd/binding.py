@@ -33,6 +33,7 @@ _SIGNATURES = {
                                      c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32p, c_vp, c_vp, c_sz,
                                      c_vp]),
     "ts_partial_kv_select_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "ts_partial_kv_rows": (c_i32, [c_i32, c_i32, c_i32, c_i32]),
     "ts_partial_kv_select_scored": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
                                             c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32p, c_vp, c_sz, c_vp]),
     "ts_partial_kv_select_scored_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32]),
@@ -112,12 +113,43 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _cache_strides(k, v):
+def _cache_strides(k, v, rows=None, d=None, Hkv=None, name="k/v"):
+    """Strides of a [Hkv][rows][d] cache pair, after checking that the tensors
+    hold what the call will touch: at least ``rows`` rows per head, ``d``
+    channels and ``Hkv`` heads (the library sees only pointers, so a short
+    tensor would be read or written past its end)."""
     if k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise TypeError("caches must be bfloat16")
-    if k.dim() != 3 or k.stride() != v.stride() or k.stride(2) != 1:
-        raise ValueError("caches must be [Hkv][rows][d] with contiguous channels and equal strides")
+        raise TypeError(f"{name} caches must be bfloat16")
+    if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.stride(2) != 1:
+        raise ValueError(f"{name} caches must be [Hkv][rows][d] of equal shapes, with contiguous channels and "
+                         "equal strides")
+    if Hkv is not None and k.shape[0] != Hkv:
+        raise ValueError(f"{name} caches have {k.shape[0]} heads, expected {Hkv}")
+    if d is not None and k.shape[2] != d:
+        raise ValueError(f"{name} caches have {k.shape[2]} channels, the queries {d}")
+    if rows is not None and k.shape[1] < rows:
+        raise ValueError(f"{name} caches hold {k.shape[1]} rows per head, the call needs {rows}")
     return k.stride(0), k.stride(1)
+
+
+def _parent_array(parent, T):
+    if len(parent) != T:
+        raise ValueError(f"parent has {len(parent)} entries for {T} tree nodes")
+    return (ctypes.c_int32 * T)(*[int(x) for x in parent])
+
+
+def _int_buffer(t, n, name):
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be a contiguous int32 buffer of at least {n} entries")
+    return t
+
+
+def partial_rows(n_ctx, n_sink, budget, n_recent):
+    """Rows of the partial cache a selection writes (ts_partial_kv_rows)."""
+    n = lib().ts_partial_kv_rows(n_ctx, n_sink, budget, n_recent)
+    if n < 0:
+        raise ValueError("n_ctx, n_sink, budget and n_recent must be >= 0")
+    return n
 
 
 def _workspace(nbytes, device, ws):
@@ -134,8 +166,8 @@ def verify_attn(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, ws=None,
     """Tree verification attention (ts_verify_attn). q [Hq][T][d] bf16; k, v [Hkv][rows][d] bf16."""
     Hq, T, d = _dense(q, torch.bfloat16, "q").shape
     Hkv = k.shape[0]
-    s_head, s_pos = _cache_strides(k, v)
-    par = (ctypes.c_int32 * T)(*[int(x) for x in parent])
+    s_head, s_pos = _cache_strides(k, v, rows=n_ctx + T, d=d)
+    par = _parent_array(parent, T)
     out = _out(out, (Hq, T, d), q.device)
     L = lib()
     need = L.ts_verify_attn_workspace_size(n_ctx, T, Hq, Hkv, d, n_split)
@@ -151,7 +183,7 @@ def _score_buffer(scores, Hkv, n_ctx, device):
         return torch.empty((Hkv, max(n_ctx, 1)), dtype=torch.float32, device=device)
     if scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != Hkv or scores.shape[1] < n_ctx:
         raise ValueError(f"scores must be float32 [{Hkv}][{n_ctx}]")
-    if n_ctx > 0 and scores.stride() != (n_ctx, 1):
+    if n_ctx > 0 and (scores.stride(1) != 1 or (Hkv > 1 and scores.stride(0) != n_ctx)):
         raise ValueError("scores must be contiguous with row stride n_ctx")
     return scores
 
@@ -163,8 +195,8 @@ def verify_attn_scored(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, s
     """
     Hq, T, d = _dense(q, torch.bfloat16, "q").shape
     Hkv = k.shape[0]
-    s_head, s_pos = _cache_strides(k, v)
-    par = (ctypes.c_int32 * T)(*[int(x) for x in parent])
+    s_head, s_pos = _cache_strides(k, v, rows=n_ctx + T, d=d)
+    par = _parent_array(parent, T)
     out = _out(out, (Hq, T, d), q.device)
     scores = _score_buffer(scores, Hkv, n_ctx, q.device)
     L = lib()
@@ -180,7 +212,7 @@ def draft_attn(q, k_part, v_part, n_part, scale=0.0, n_split=0, out=None, ws=Non
     """Draft attention over the partial cache (ts_draft_attn)."""
     Hq, Tq, d = _dense(q, torch.bfloat16, "q").shape
     Hkv = k_part.shape[0]
-    s_head, s_pos = _cache_strides(k_part, v_part)
+    s_head, s_pos = _cache_strides(k_part, v_part, rows=n_part + Tq, d=d, name="partial")
     out = _out(out, (Hq, Tq, d), q.device)
     L = lib()
     need = L.ts_draft_attn_workspace_size(n_part, Tq, Hq, Hkv, d, n_split)
@@ -201,20 +233,20 @@ def partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, k_part=None, v_p
     """
     Hq, T, d = _dense(q, torch.bfloat16, "q").shape
     Hkv = k.shape[0]
-    s_head, s_pos = _cache_strides(k, v)
+    s_head, s_pos = _cache_strides(k, v, rows=n_ctx, d=d)
     dev = q.device
+    n_part_need = partial_rows(n_ctx, n_sink, budget, n_recent)
     if k_part is None:
         k_part = torch.empty((Hkv, max(n_sink + budget + n_recent + extra_rows, 1), d), dtype=torch.bfloat16,
                              device=dev)
     if v_part is None:
         v_part = torch.empty_like(k_part)
-    sp_head, sp_pos = _cache_strides(k_part, v_part)
+    sp_head, sp_pos = _cache_strides(k_part, v_part, rows=n_part_need, d=d, Hkv=Hkv, name="partial")
     if sel_idx is None:
         sel_idx = torch.empty((Hkv, max(budget, 1)), dtype=torch.int32, device=dev)
     else:
         _dense(sel_idx, torch.int32, "sel_idx", (Hkv, max(budget, 1)))
-    if want_scores and scores is None:
-        scores = torch.empty((Hkv, max(n_ctx, 1)), dtype=torch.float32, device=dev)
+    scores = _score_buffer(scores, Hkv, n_ctx, dev) if want_scores else None
     L = lib()
     need = L.ts_partial_kv_select_workspace_size(n_ctx, T, Hq, Hkv, d, budget)
     wst = _workspace(need, dev, ws)
@@ -235,15 +267,18 @@ def partial_kv_select_scored(scores, k, v, n_ctx, n_sink, budget, n_recent, k_pa
     (sel_idx [Hkv][budget] int32, k_part, v_part, n_part).
     """
     Hkv, d = k.shape[0], k.shape[2]
-    s_head, s_pos = _cache_strides(k, v)
+    s_head, s_pos = _cache_strides(k, v, rows=n_ctx)
     dev = k.device
+    if scores is None:
+        raise ValueError("scores are required")
     scores = _score_buffer(scores, Hkv, n_ctx, dev)
+    n_part_need = partial_rows(n_ctx, n_sink, budget, n_recent)
     if k_part is None:
         k_part = torch.empty((Hkv, max(n_sink + budget + n_recent + extra_rows, 1), d), dtype=torch.bfloat16,
                              device=dev)
     if v_part is None:
         v_part = torch.empty_like(k_part)
-    sp_head, sp_pos = _cache_strides(k_part, v_part)
+    sp_head, sp_pos = _cache_strides(k_part, v_part, rows=n_part_need, d=d, Hkv=Hkv, name="partial")
     if sel_idx is None:
         sel_idx = torch.empty((Hkv, max(budget, 1)), dtype=torch.int32, device=dev)
     else:
@@ -323,9 +358,11 @@ def tree_accept(parent, node_token, target, result=None, stream=None):
     for name, t in (("node_token", node_token), ("target", target)):
         if t.dtype != torch.int32 or t.dim() != 1 or t.shape[0] != T or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 vector of {T} tokens")
-    par = (ctypes.c_int32 * T)(*[int(x) for x in parent])
+    par = _parent_array(parent, T)
     if result is None:
         result = torch.empty(T + 2, dtype=torch.int32, device=node_token.device)
+    else:
+        _int_buffer(result, T + 2, "result")
     rc = lib().ts_tree_accept(par, T, _ptr(node_token), _ptr(target), _ptr(result), _stream(stream))
     _check("ts_tree_accept", rc)
     return result
@@ -350,10 +387,19 @@ def kv_commit(result, T, k, v, n_ctx, k_part=None, v_part=None, n_part=0, stream
     """
     layers, s_layer, s_head, s_pos = _layer_strides(k, v)
     Hkv, d = k.shape[-3], k.shape[-1]
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if k.shape[-2] < n_ctx + T:
+        raise ValueError(f"caches hold {k.shape[-2]} rows per head, the tree rows end at {n_ctx + T}")
+    _int_buffer(result, T + 2, "result")
+    if (k_part is None) != (v_part is None):
+        raise ValueError("give both k_part and v_part or neither")
     if k_part is not None:
         pl, sp_layer, sp_head, sp_pos = _layer_strides(k_part, v_part)
         if pl != layers:
             raise ValueError("partial caches need the same number of layers")
+        if k_part.shape != v_part.shape or k_part.shape[-3] != Hkv or k_part.shape[-1] != d:
+            raise ValueError("partial caches must have the full caches' heads and channels, and equal shapes")
         part_rows = k_part.shape[-2]
     else:
         sp_layer = sp_head = sp_pos = 0
@@ -380,9 +426,11 @@ def ngram_tree(window, k, seed, head_cand=None, T_max=24, parent=None, node_toke
                 not head_cand.is_contiguous():
             raise ValueError("head_cand must be a contiguous int32 [levels][3] tensor")
         levels = head_cand.shape[0]
-    parent = torch.empty(T_max, dtype=torch.int32, device=dev) if parent is None else parent
-    node_token = torch.empty(T_max, dtype=torch.int32, device=dev) if node_token is None else node_token
-    info = torch.empty(4, dtype=torch.int32, device=dev) if info is None else info
+    parent = torch.empty(T_max, dtype=torch.int32, device=dev) if parent is None else \
+        _int_buffer(parent, T_max, "parent")
+    node_token = torch.empty(T_max, dtype=torch.int32, device=dev) if node_token is None else \
+        _int_buffer(node_token, T_max, "node_token")
+    info = torch.empty(4, dtype=torch.int32, device=dev) if info is None else _int_buffer(info, 4, "info")
     rc = lib().ts_ngram_tree(_ptr(window), window.shape[0], int(k), int(seed) & ((1 << 64) - 1), _ptr(head_cand),
                              levels, int(T_max), _ptr(parent), _ptr(node_token), _ptr(info), _stream(stream))
     _check("ts_ngram_tree", rc)

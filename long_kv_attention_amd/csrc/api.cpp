@@ -51,6 +51,24 @@ bool build_masks(const int32_t* parent, int32_t T, uint64_t* anc, char* why, siz
   return true;
 }
 
+// Candidate range and partial-cache row count of a selection (TokenSwift
+// summary §3.3: the initial pairs are always kept, the budget's worth of
+// candidates is selected, and the most recent rows are kept).
+struct PartialRows {
+  int32_t cand_lo, cand_hi, b_eff, n_part;
+};
+PartialRows partial_rows(int32_t n_ctx, int32_t n_sink, int32_t budget, int32_t n_recent) {
+  PartialRows r;
+  r.cand_lo = n_sink;
+  r.cand_hi = (n_ctx - n_recent > n_sink) ? n_ctx - n_recent : n_sink;
+  const int32_t n_cand = r.cand_hi - r.cand_lo;
+  r.b_eff = budget < n_cand ? budget : n_cand;
+  const int32_t n_sink_eff = n_sink < n_ctx ? n_sink : n_ctx;
+  const int32_t n_rec_eff = n_ctx > r.cand_hi ? n_ctx - r.cand_hi : 0;
+  r.n_part = n_sink_eff + r.b_eff + n_rec_eff;
+  return r;
+}
+
 // Checks shared by the attention entry points.
 int check_attention(const char* who, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const float* out, int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t T,
@@ -116,7 +134,7 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
 
 extern "C" {
 
-int ts_abi_version(void) { return 105; }
+int ts_abi_version(void) { return 106; }
 
 const char* ts_last_error(void) { return g_err; }
 
@@ -181,6 +199,11 @@ int ts_draft_attn(const uint16_t* q, const uint16_t* k_part, const uint16_t* v_p
   }
   return run_attention(who, q, k_part, v_part, s_head, s_pos, n_part, Tq, anc, Hq, Hkv, d, scale, out, nullptr,
                        n_split, ws, ws_bytes, stream);
+}
+
+int32_t ts_partial_kv_rows(int32_t n_ctx, int32_t n_sink, int32_t budget, int32_t n_recent) {
+  if (n_ctx < 0 || n_sink < 0 || budget < 0 || n_recent < 0) return -1;
+  return partial_rows(n_ctx, n_sink, budget, n_recent).n_part;
 }
 
 size_t ts_partial_kv_select_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
@@ -276,14 +299,8 @@ int run_select(const char* who, const uint16_t* q, int32_t T, int32_t Hq, const 
       !aligned(sel_idx, 4) || (scores_out && !aligned(scores_out, 4)) || (scores_in && !aligned(scores_in, 4)))
     return fail(TS_EINVAL, "%s: tensors must be 16-byte aligned (indices and scores 4-byte)", who);
 
-  const int32_t cand_lo = n_sink;
-  const int32_t cand_hi = (n_ctx - n_recent > n_sink) ? n_ctx - n_recent : n_sink;
-  const int32_t n_cand = cand_hi - cand_lo;
-  const int32_t b_eff = budget < n_cand ? budget : n_cand;
-  const int32_t n_sink_eff = n_sink < n_ctx ? n_sink : n_ctx;
-  const int32_t rec_lo = (n_ctx - n_recent > n_sink) ? n_ctx - n_recent : n_sink;
-  const int32_t n_rec_eff = n_ctx > rec_lo ? n_ctx - rec_lo : 0;
-  const int32_t n_part = n_sink_eff + b_eff + n_rec_eff;
+  const PartialRows pr = partial_rows(n_ctx, n_sink, budget, n_recent);
+  const int32_t cand_lo = pr.cand_lo, cand_hi = pr.cand_hi, b_eff = pr.b_eff, n_part = pr.n_part;
   if (Hkv > 1 && sp_head < (int64_t)n_part * sp_pos)
     return fail(TS_EINVAL, "%s: partial heads overlap (sp_head=%lld < n_part*sp_pos)", who, (long long)sp_head);
 

@@ -41,6 +41,7 @@
 // holds all query rows of its KV head sums each tile over its rows (lanes,
 // then row tiles, then row groups through LDS) and writes sigma for the
 // tile's committed rows: no second pass over K.
+#include "ts_device.h"
 #include "ts_internal.h"
 
 #include <cmath>
@@ -56,8 +57,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_AS __attribute__((address_space(3)))
 
 template <int D, int RG, int PG, int TPW, int STAGES, bool SCORE = false>
 struct Cfg {
@@ -150,52 +149,6 @@ __device__ inline unsigned int bf16x2_to_f16x2(unsigned int w) {
   float hi = __uint_as_float(w & 0xffff0000u);
   auto h = __builtin_amdgcn_cvt_pkrtz(lo, hi);
   return __builtin_bit_cast(unsigned int, h);
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource (gfx9 layout): 48-bit base, stride 0, num_records bytes.
-// Reads at offsets >= num_records are out of range and do not touch memory.
-__device__ inline i32x4 buffer_desc(const void* base, unsigned int num_records) {
-  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
-  return i32x4{(int)(unsigned int)b, (int)((unsigned int)(b >> 32) & 0xffffu), (int)num_records, 0x00020000};
-}
-
-// One wave-wide asynchronous copy global -> LDS (16 B per lane): lane l's 16
-// bytes come from the buffer at its per-lane byte offset `off` and land at LDS
-// byte offset lds_off + 16 * l. The compiler does not see the LDS write;
-// callers order it with explicit vmcnt waits and barriers. One wait state
-// separates the M0 write from the load that reads it.
-__device__ inline void dma16(i32x4 desc, unsigned int off, unsigned int lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc) : "memory", "m0");
-}
-
-// The same copy with the non-temporal cache policy, for the K/V stream that
-// is read once: measured on the LDS-copy ring over a 100K-row cache, it
-// streams at 6.8-7.0 TB/s instead of 5.8-6.1 TB/s with the default policy.
-// `soff` is a wave-uniform byte offset added to every lane's.
-__device__ inline void dma16_nt(i32x4 desc, unsigned int off, unsigned int soff, unsigned int lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc),
-                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
-}
-
-template <int N>
-__device__ inline void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
-}
-
-// Workgroup barrier that orders LDS accesses only (no wait for global stores).
-__device__ inline void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ inline unsigned int lds_offset(const void* p) {
-  return (unsigned int)(uintptr_t)(const LDS_AS void*)p;
 }
 
 template <int CTRL>
@@ -502,7 +455,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         if (NCHK % C::NT == 0 || tid + i * C::NT < NCHK)
           *reinterpret_cast<u32x4*>(vw + (tid + i * C::NT) * 16) =
               u32x4{bf16x2_to_f16x2(w[i].x), bf16x2_to_f16x2(w[i].y), bf16x2_to_f16x2(w[i].z), bf16x2_to_f16x2(w[i].w)};
-      lds_barrier();
+      bar();
     }
 
     // ---- tree mask and tail (only tiles reaching past the context) ----
@@ -601,7 +554,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   }
 
   if constexpr (SCORE && RG > 1) {
-    lds_barrier();   // the last tile's parked sums
+    bar();   // the last tile's parked sums
     if (rg == 0 && t_end > t_begin) add_parked(t_end - 1);
   }
 
@@ -665,7 +618,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     for (int t0 = 0; t0 < TPW; t0 += RT) {
       // LDS-only barriers: the partial stores of the previous round may stay
       // in flight (__syncthreads would wait for them).
-      lds_barrier();  // the ring (or the previous round) is free
+      bar();  // the ring (or the previous round) is free
 #pragma unroll
       for (int u = 0; u < RT; ++u) {
         const int t = t0 + u;
@@ -683,7 +636,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
           reinterpret_cast<float*>(my + OFF_ML)[16 + l16] = l_run[t];
         }
       }
-      lds_barrier();
+      bar();
 #pragma unroll
       for (int u = 0; u < RT; ++u) {
         const int t = t0 + u;

@@ -82,10 +82,6 @@ constexpr float FIX_SCALE = 1099511627776.0f;  // 2^40
 static_assert(SCAP == H1, "the sorted list and the first-digit mass histogram share LDS");
 static_assert(H2 % PB == 0 && H1 % PB == 0, "bins split evenly over the threads");
 
-__device__ inline unsigned int f2key(float f) {
-  const unsigned int u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 __device__ inline float key2f(unsigned int k) {
   const unsigned int u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   return __uint_as_float(u);

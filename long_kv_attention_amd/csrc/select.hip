@@ -48,52 +48,11 @@ constexpr int HIST1_BITS = 12;
 constexpr int HIST1 = 1 << HIST1_BITS;  // bins of the first radix digit
 constexpr int HIST2_BITS = 10;
 constexpr int HIST2 = 1 << HIST2_BITS;  // bins of the second and third digits
-// Order-preserving map from float to uint32 (larger float -> larger key).
-__device__ inline unsigned int f2key(float f) {
-  const unsigned int u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 __device__ inline float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Lanes below the caller's in the wave.
-__device__ inline unsigned long long lanemask_lt() {
-  return (1ull << (threadIdx.x & 63)) - 1ull;
-}
 __device__ inline unsigned int popc64(unsigned long long x) { return (unsigned int)__popcll(x); }
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource (gfx9 layout): 48-bit base, stride 0, num_records bytes.
-// Reads at offsets >= num_records are out of range and do not touch memory.
-__device__ inline i32x4 buffer_desc(const void* base, unsigned int num_records) {
-  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
-  return i32x4{(int)(unsigned int)b, (int)((unsigned int)(b >> 32) & 0xffffu), (int)num_records, 0x00020000};
-}
-
-// One wave-wide asynchronous copy global -> LDS (16 B per lane) with the
-// non-temporal policy (K is streamed once): lane l's 16 bytes come from the
-// buffer at byte offset off + soff and land at LDS byte lds_off + 16 * l.
-// Callers order the LDS write with explicit vmcnt waits and barriers.
-__device__ inline void dma16_nt(i32x4 desc, unsigned int off, unsigned int soff, unsigned int lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc),
-                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
-}
-
-// The same copy with the default cache policy (data that other workgroups read too).
-__device__ inline void dma16(i32x4 desc, unsigned int off, unsigned int soff, unsigned int lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds_off)), "v"(off), "s"(desc),
-                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
-}
-
-template <int N>
-__device__ inline void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" :: "n"(N) : "memory");
-}
 
 // Scoring ring: two stages of 256-row tiles, 16 waves (measured at 8B / 100K:
 // 35.4 us; four stages of 128 rows: 36.0 us with 8 or 16 waves; two stages
@@ -147,7 +106,7 @@ __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const Selec
   const int ntiles = r1 > r0 ? (r1 - r0 + SC_ROWS - 1) / SC_ROWS : 0;
   const int64_t row_bytes = p.s_pos * 2;
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k + (int64_t)g * p.s_head);
-  const unsigned int ring_off = (unsigned int)(uintptr_t)(const __attribute__((address_space(3))) void*)ring;
+  const unsigned int ring_off = lds_offset(ring);
   // copy j of a tile (wave w issues j = w, w + SC_WAVES, ...) covers ROWS_PER_DMA dense rows
   const unsigned int loff = (unsigned int)((wave * ROWS_PER_DMA + lane / LPR) * row_bytes) + (lane % LPR) * 16;
   const unsigned int jj_step = (unsigned int)(SC_WAVES * ROWS_PER_DMA * row_bytes);

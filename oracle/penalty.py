@@ -5,9 +5,9 @@ Test infrastructure only (see the package docstring).
 Definition: TokenSwift summary §3.4 "Contextual Penalty and Random N-gram
 Selection" (a penalty on the tokens of the most recent W positions, instead of
 on every generated token), Appendix D.1 "Introduction of Different Sampling
-Algorithms" (top-p keeps the smallest set whose cumulative probability exceeds
-p, renormalised; min-p keeps tokens whose probability reaches p_base times the
-largest probability), Appendix F.1 (temperature). Hyper-parameters from the
+Algorithms" (top-p: with tokens sorted by probability, the shortest head of
+that order whose mass is above p, then renormalised; min-p: the tokens with
+p_i >= p_base * max_j p_j), Appendix F.1 (temperature). Hyper-parameters from the
 TokenSwift reproducibility checklist, Table 11 (penalty 1.2, penalty length
 1024, temperature 1.0, top-p 0.9, min-p 0.05).
 

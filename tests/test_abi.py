@@ -41,7 +41,7 @@ def test_library_exports_every_header_symbol():
     L = _lib()
     missing = [s for s in header_symbols() if not hasattr(L, s)]
     assert not missing, missing
-    assert L.ts_abi_version() == 105
+    assert L.ts_abi_version() == 106
 
 
 def test_workspace_queries_depend_on_shapes_only():
@@ -283,3 +283,87 @@ def test_binding_checks_tensors_before_any_launch():
         binding.penalty_sample(logits.t(), None, 1.2, 1.0, 0.9, 0.05)
     with pytest.raises(ValueError, match="shape"):
         binding.penalty_sample(logits, None, 1.2, 1.0, 0.9, 0.05, out=torch.zeros((4, 1000)))
+
+
+def test_partial_rows_query():
+    L = _lib()
+    assert L.ts_partial_kv_rows(100_000, 4, 4096, 64) == 4 + 4096 + 64
+    assert L.ts_partial_kv_rows(1000, 4, 5000, 8) == 1000       # budget past the candidates: every row
+    assert L.ts_partial_kv_rows(70, 4, 16, 64) == 70            # fewer candidates than the budget
+    assert L.ts_partial_kv_rows(3, 4, 16, 8) == 3               # shorter than the sink
+    assert L.ts_partial_kv_rows(0, 4, 16, 8) == 0
+    assert L.ts_partial_kv_rows(-1, 4, 16, 8) == -1
+    assert binding.partial_rows(5000, 4, 1, 64) == 69
+
+
+def _cpu_bf16(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def test_binding_checks_extents_before_any_launch():
+    """Every tensor's extent is checked against the scalars passed with it
+    (the library sees only pointers: a short tensor would be read or written
+    past its end). CPU tensors: the check fires before any pointer is taken."""
+    import torch
+
+    _lib()
+    q = _cpu_bf16(8, 4, 64)
+    k = _cpu_bf16(2, 100, 64)
+    # verification: n_ctx + T rows, matching channels, one parent per node
+    with pytest.raises(ValueError, match="the call needs 100"):
+        binding.verify_attn(q, k[:, :99], k[:, :99], 96, [-1, 0, 1, 2])
+    with pytest.raises(ValueError, match="channels"):
+        binding.verify_attn(q, _cpu_bf16(2, 100, 128), _cpu_bf16(2, 100, 128), 96, [-1, 0, 1, 2])
+    with pytest.raises(ValueError, match="parent has 3 entries"):
+        binding.verify_attn(q, k, k, 96, [-1, 0, 1])
+    with pytest.raises(ValueError, match="equal shapes"):
+        binding.verify_attn(q, k, _cpu_bf16(2, 99, 64), 96, [-1, 0, 1, 2])
+    with pytest.raises(ValueError, match="the call needs 100"):
+        binding.verify_attn_scored(q, k[:, :99], k[:, :99], 96, [-1, 0, 1, 2])
+    with pytest.raises(ValueError, match="scores must be float32"):
+        binding.verify_attn_scored(q, k, k, 96, [-1, 0, 1, 2], scores=torch.zeros((2, 95)))
+    # drafting: n_part + Tq rows of the partial cache
+    with pytest.raises(ValueError, match="the call needs 101"):
+        binding.draft_attn(q, k, k, 97)
+    # selection: n_ctx rows of the full cache, n_part rows of the partial cache, the scores buffer
+    kp = _cpu_bf16(2, 4 + 16 + 8, 64)
+    with pytest.raises(ValueError, match="the call needs 101"):
+        binding.partial_kv_select(q, k, k, 101, 4, 16, 8)
+    with pytest.raises(ValueError, match="the call needs 28"):
+        binding.partial_kv_select(q, k, k, 100, 4, 16, 8, k_part=kp[:, :27], v_part=kp[:, :27])
+    with pytest.raises(ValueError, match="heads"):
+        binding.partial_kv_select(q, k, k, 100, 4, 16, 8, k_part=_cpu_bf16(1, 28, 64), v_part=_cpu_bf16(1, 28, 64))
+    with pytest.raises(ValueError, match="scores must be float32"):
+        binding.partial_kv_select(q, k, k, 100, 4, 16, 8, want_scores=True, scores=torch.zeros((2, 99)))
+    with pytest.raises(ValueError, match="scores must be float32"):
+        binding.partial_kv_select(q, k, k, 100, 4, 16, 8, want_scores=True,
+                                  scores=torch.zeros((2, 100), dtype=torch.float16))
+    with pytest.raises(ValueError, match="row stride"):
+        binding.partial_kv_select(q, k, k, 100, 4, 16, 8, want_scores=True, scores=torch.zeros((100, 2)).t())
+    with pytest.raises(ValueError, match="the call needs 28"):
+        binding.partial_kv_select_scored(torch.zeros((2, 100)), k, k, 100, 4, 16, 8, k_part=kp[:, :27],
+                                         v_part=kp[:, :27])
+    with pytest.raises(ValueError, match="scores must be float32"):
+        binding.partial_kv_select_scored(torch.zeros((3, 100)), k, k, 100, 4, 16, 8)
+    # acceptance and commit: result of T + 2 entries, the tree rows inside the caches
+    tok = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="result must be"):
+        binding.tree_accept([-1, 0, 1, 2], tok, tok, result=torch.zeros(5, dtype=torch.int32))
+    with pytest.raises(ValueError, match="result must be"):
+        binding.kv_commit(torch.zeros(5, dtype=torch.int32), 4, k, k, 96)
+    with pytest.raises(ValueError, match="tree rows end at 101"):
+        binding.kv_commit(torch.zeros(6, dtype=torch.int32), 4, k, k, 97)
+    with pytest.raises(ValueError, match="heads and channels"):
+        binding.kv_commit(torch.zeros(6, dtype=torch.int32), 4, k, k, 96, _cpu_bf16(3, 40, 64),
+                          _cpu_bf16(3, 40, 64), 10)
+    with pytest.raises(ValueError, match="both k_part and v_part"):
+        binding.kv_commit(torch.zeros(6, dtype=torch.int32), 4, k, k, 96, _cpu_bf16(2, 40, 64), None, 10)
+    # n-gram tree outputs: T_max entries (info: 4)
+    win = torch.zeros(64, dtype=torch.int32)
+    with pytest.raises(ValueError, match="parent must be"):
+        binding.ngram_tree(win, 20, 1, T_max=24, parent=torch.zeros(23, dtype=torch.int32))
+    with pytest.raises(ValueError, match="node_token must be"):
+        binding.ngram_tree(win, 20, 1, T_max=24, node_token=torch.zeros(24, dtype=torch.int64))
+    with pytest.raises(ValueError, match="info must be"):
+        binding.ngram_tree(win, 20, 1, T_max=24, info=torch.zeros(3, dtype=torch.int32))

@@ -148,6 +148,29 @@ def test_full_size_sampled_heads(name, heads):
         _check_selection(x, g, sel, kp, vp, n_part, ref, n_ctx, c["n_sink"], c["n_recent"])
 
 
+@pytest.mark.parametrize("Hkv,T,n_ctx", [(4, 1, 3001), (4, 24, 3001), (4, 64, 3001), (4, 128, 3001),
+                                         (32, 24, 20_000)])
+def test_one_query_head_per_kv_head(Hkv, T, n_ctx):
+    """MHA (TokenSwift summary §4.2): one query head per KV head, so every
+    workgroup's rows are the T tree nodes of one head; the scores and the
+    selection from them against the oracle, the output against the plain call."""
+    Hq, d, budget = Hkv, 128, min(4096, n_ctx // 2)
+    banner(f"fused scores MHA Hkv={Hkv} T={T} n_ctx={n_ctx}")
+    x = attention_inputs(60 + T + Hkv, Hq, Hkv, d, n_ctx, T)
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    parent = tree_parent("chain", T) if T < 10 else tree_parent("tokenswift", T)
+    out, sc = ts.verify_attn_scored(q, k, v, n_ctx, parent)
+    plain = ts.verify_attn(q, k, v, n_ctx, parent)
+    sel, kp, vp, n_part = ts.partial_kv_select_scored(sc, k, v, n_ctx, 4, budget, 64)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), plain.cpu().numpy())
+    sc, sel, kp, vp = sc.cpu().numpy(), sel.cpu().numpy(), _host_u16(kp), _host_u16(vp)
+    for g in sorted({0, Hkv // 2, Hkv - 1}):
+        ref = _oracle_scores(x, n_ctx, Hq, Hkv, g, 4, budget, 64)
+        _check_scores(sc[g, :n_ctx], ref.scores[0])
+        _check_selection(x, g, sel, kp, vp, n_part, ref, n_ctx, 4, 64)
+
+
 def test_too_many_rows_per_head_is_refused():
     # 5 query heads per KV head x 64 nodes = 320 rows: more than one workgroup sums
     Hq, Hkv, d, T, n_ctx = 10, 2, 128, 64, 500

@@ -156,7 +156,22 @@ def test_full_budget_draft_equals_verification():
     assert rel_max_err(draft.cpu().numpy(), ref) <= 2e-3
 
 
-@pytest.mark.parametrize("name,heads", [("8b", [0, 6]), ("14b", [4]), ("1.5b", [1])])
+@pytest.mark.parametrize("Hq,Hkv,n_ctx,budget,T", [
+    (32, 32, 33_333, 4096, 24),   # the 7B layout: 8 blocks per head, chunks of two sub-chunks
+    (4, 4, 5000, 700, 24),
+    (4, 4, 1000, 100, 1),
+    (3, 3, 300, 500, 4),          # budget past the candidates
+])
+def test_one_query_head_per_kv_head(Hq, Hkv, n_ctx, budget, T):
+    """MHA (TokenSwift summary §4.2 measures MHA and GQA models): each KV
+    head's group is a single query head, so the grouped score of §3.3 is that
+    head's own products summed over the tree nodes."""
+    banner(f"select MHA Hq=Hkv={Hkv} n_ctx={n_ctx} B={budget} T={T}")
+    x = attention_inputs(50 + Hkv + T, Hq, Hkv, 128, n_ctx, T)
+    _check(x, n_ctx, Hq, Hkv, 4, budget, 64)
+
+
+@pytest.mark.parametrize("name,heads", [("8b", [0, 6]), ("14b", [4]), ("1.5b", [1]), ("7b", [0, 31])])
 def test_full_size_sampled_heads(name, heads):
     c = CONFIGS[name]
     banner(f"select full {name}")
