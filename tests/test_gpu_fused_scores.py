@@ -15,9 +15,9 @@ import torch
 
 import long_kv_attention_amd as ts
 from long_kv_attention_amd.binding import TSError
-from oracle import bf16_to_f64, partial_kv_select
+from oracle import bf16_to_f64, partial_kv_select, verify_attention
 from synth import CONFIGS, attention_inputs, tree_parent
-from tests.gpu_util import banner, dev_bf16
+from tests.gpu_util import banner, dev_bf16, rel_max_err
 
 pytestmark = pytest.mark.gpu
 
@@ -136,16 +136,27 @@ def test_full_size_sampled_heads(name, heads):
     q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
     n_ctx = c["n_ctx"]
     parent = tree_parent(c["tree"], c["T"])
+    # automatic and forced split counts: the output is bitwise the plain call's;
+    # scores, selection and output against the oracle
     out, sc = ts.verify_attn_scored(q, k, v, n_ctx, parent)
     plain = ts.verify_attn(q, k, v, n_ctx, parent)
     sel, kp, vp, n_part = ts.partial_kv_select_scored(sc, k, v, n_ctx, c["n_sink"], c["budget"], c["n_recent"])
+    out_f, sc_f = ts.verify_attn_scored(q, k, v, n_ctx, parent, n_split=7)
+    plain_f = ts.verify_attn(q, k, v, n_ctx, parent, n_split=7)
     torch.cuda.synchronize()
     assert torch.equal(out, plain)
+    assert torch.equal(out_f, plain_f)
+    assert torch.equal(sc, sc_f)   # each score is one workgroup's sum, whatever the split count
     sc, sel, kp, vp = sc.cpu().numpy(), sel.cpu().numpy(), _host_u16(kp), _host_u16(vp)
+    G = c["Hq"] // c["Hkv"]
+    out = out.cpu().numpy()
     for g in heads:
         ref = _oracle_scores(x, n_ctx, c["Hq"], c["Hkv"], g, c["n_sink"], c["budget"], c["n_recent"])
         _check_scores(sc[g], ref.scores[0])
         _check_selection(x, g, sel, kp, vp, n_part, ref, n_ctx, c["n_sink"], c["n_recent"])
+        oref = verify_attention(bf16_to_f64(x["q"][g * G:(g + 1) * G]), bf16_to_f64(x["k"][g:g + 1]),
+                                bf16_to_f64(x["v"][g:g + 1]), n_ctx, parent)
+        assert rel_max_err(out[g * G:(g + 1) * G], oref) <= 2e-3
 
 
 @pytest.mark.parametrize("Hkv,T,n_ctx", [(4, 1, 3001), (4, 24, 3001), (4, 64, 3001), (4, 128, 3001),
@@ -161,14 +172,21 @@ def test_one_query_head_per_kv_head(Hkv, T, n_ctx):
     parent = tree_parent("chain", T) if T < 10 else tree_parent("tokenswift", T)
     out, sc = ts.verify_attn_scored(q, k, v, n_ctx, parent)
     plain = ts.verify_attn(q, k, v, n_ctx, parent)
+    out_f, _ = ts.verify_attn_scored(q, k, v, n_ctx, parent, n_split=3)
+    plain_f = ts.verify_attn(q, k, v, n_ctx, parent, n_split=3)
     sel, kp, vp, n_part = ts.partial_kv_select_scored(sc, k, v, n_ctx, 4, budget, 64)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), plain.cpu().numpy())
+    np.testing.assert_array_equal(out_f.cpu().numpy(), plain_f.cpu().numpy())
+    out = out.cpu().numpy()
     sc, sel, kp, vp = sc.cpu().numpy(), sel.cpu().numpy(), _host_u16(kp), _host_u16(vp)
     for g in sorted({0, Hkv // 2, Hkv - 1}):
         ref = _oracle_scores(x, n_ctx, Hq, Hkv, g, 4, budget, 64)
         _check_scores(sc[g, :n_ctx], ref.scores[0])
         _check_selection(x, g, sel, kp, vp, n_part, ref, n_ctx, 4, 64)
+        oref = verify_attention(bf16_to_f64(x["q"][g:g + 1]), bf16_to_f64(x["k"][g:g + 1]), bf16_to_f64(x["v"][g:g + 1]),
+                                n_ctx, parent)
+        assert rel_max_err(out[g:g + 1], oref) <= 2e-3
 
 
 def test_too_many_rows_per_head_is_refused():
