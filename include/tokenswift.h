@@ -98,6 +98,31 @@ size_t ts_verify_attn_workspace_size(int32_t n_ctx, int32_t T, int32_t Hq, int32
                                      int32_t d, int32_t n_split);
 
 /*
+ * ts_verify_attn_noalloc -- ts_verify_attn with no workspace argument, for
+ * callers that cannot allocate device memory around the call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The split partials go to a scratch array the library holds in device
+ * memory (one copy per device, from the library's load until the process
+ * ends, ts_verify_attn_noalloc_max_scratch() bytes); the call itself
+ * allocates nothing. Every argument and the output as for ts_verify_attn;
+ * the output is bitwise what ts_verify_attn writes for the same arguments.
+ * A call whose ts_verify_attn_workspace_size(...) exceeds the scratch size
+ * returns TS_EWORKSPACE (use ts_verify_attn with a workspace then).
+ * All calls on one device share its scratch array: calls that may overlap
+ * on one device (different streams without ordering) race and must not be
+ * made; calls ordered on one stream are fine. Nothing in the scratch array
+ * needs to start at zero.
+ */
+int ts_verify_attn_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t T,
+                           const int32_t* parent, int32_t Hq, int32_t Hkv, int32_t d,
+                           float scale, float* out, int32_t n_split, void* stream);
+
+/* Bytes of the scratch array behind ts_verify_attn_noalloc (per device). */
+size_t ts_verify_attn_noalloc_max_scratch(void);
+
+/*
  * ts_verify_attn_scored -- ts_verify_attn that also writes the grouped key
  * scores of the committed rows, summed from the query-key products the
  * attention already forms (no second pass over the keys).

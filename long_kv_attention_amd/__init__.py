@@ -20,6 +20,7 @@ from .binding import (
     penalty_sample_eta,
     tree_accept,
     verify_attn,
+    verify_attn_noalloc,
     verify_attn_scored,
 )
 
@@ -28,6 +29,7 @@ __all__ = [
     "lib",
     "lib_path",
     "verify_attn",
+    "verify_attn_noalloc",
     "verify_attn_scored",
     "draft_attn",
     "partial_kv_select",

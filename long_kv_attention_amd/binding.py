@@ -24,6 +24,9 @@ _SIGNATURES = {
     "ts_verify_attn": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32p, c_i32, c_i32, c_i32,
                                c_f32, c_vp, c_i32, c_vp, c_sz, c_vp]),
     "ts_verify_attn_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "ts_verify_attn_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32p, c_i32, c_i32, c_i32,
+                                       c_f32, c_vp, c_i32, c_vp]),
+    "ts_verify_attn_noalloc_max_scratch": (c_sz, []),
     "ts_verify_attn_scored": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32p, c_i32, c_i32, c_i32,
                                       c_f32, c_vp, c_vp, c_i32, c_vp, c_sz, c_vp]),
     "ts_draft_attn": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp,
@@ -175,6 +178,21 @@ def verify_attn(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, ws=None,
     rc = L.ts_verify_attn(_ptr(q), _ptr(k), _ptr(v), s_head, s_pos, n_ctx, T, par, Hq, Hkv, d, float(scale),
                           _ptr(out), n_split, _ptr(wst), need, _stream(stream))
     _check("ts_verify_attn", rc)
+    return out
+
+
+def verify_attn_noalloc(q, k, v, n_ctx, parent, out, scale=0.0, n_split=0, stream=None):
+    """Tree verification attention with the library's own scratch
+    (ts_verify_attn_noalloc): no workspace, and ``out`` must be given, so the
+    call allocates nothing."""
+    Hq, T, d = _dense(q, torch.bfloat16, "q").shape
+    Hkv = k.shape[0]
+    s_head, s_pos = _cache_strides(k, v, rows=n_ctx + T, d=d)
+    par = _parent_array(parent, T)
+    _dense(out, torch.float32, "out", (Hq, T, d))
+    rc = lib().ts_verify_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), s_head, s_pos, n_ctx, T, par, Hq, Hkv, d,
+                                      float(scale), _ptr(out), n_split, _stream(stream))
+    _check("ts_verify_attn_noalloc", rc)
     return out
 
 

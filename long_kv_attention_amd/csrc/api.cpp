@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -130,11 +131,66 @@ int run_attention(const char* who, const uint16_t* q, const uint16_t* k, const u
   return ok();
 }
 
+// ---- allocation-free verification (ts_verify_attn_noalloc) ----
+// The split partials live in this file-scope device array instead of a
+// caller workspace: each device holds its own copy from module load until the
+// process ends. Host code uses the address hipGetSymbolAddress returns for the
+// current device, never the array's name (a host-side stand-in).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's copy of the scratch array (looked up once per device).
+int scratch_for_current_device(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TS_EHIP, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(TS_ENOTSUP, "%s: device %d beyond the %d supported", who, dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(TS_EHIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", who, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TS_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int ts_abi_version(void) { return 106; }
+int ts_abi_version(void) { return 107; }
+
+size_t ts_verify_attn_noalloc_max_scratch(void) { return NOALLOC_SCRATCH_BYTES; }
+
+int ts_verify_attn_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t s_head, int64_t s_pos,
+                           int32_t n_ctx, int32_t T, const int32_t* parent, int32_t Hq, int32_t Hkv, int32_t d,
+                           float scale, float* out, int32_t n_split, void* stream) {
+  const char* who = "ts_verify_attn_noalloc";
+  int rc = check_attention(who, q, k, v, out, s_head, s_pos, n_ctx, T, Hq, Hkv, d, scale, n_split);
+  if (rc) return rc;
+  if (!parent) return fail(TS_EINVAL, "%s: parent is null", who);
+  const size_t need = ts::attn_workspace_bytes(n_ctx + T, T, Hq, Hkv, d, n_split);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(TS_EWORKSPACE, "%s: this call needs %zu bytes of scratch, beyond the library's %zu", who, need,
+                NOALLOC_SCRATCH_BYTES);
+  uint64_t anc[2 * TS_MAX_TREE];
+  char why[160];
+  if (!build_masks(parent, T, anc, why, sizeof(why))) return fail(TS_EINVAL, "%s: %s", who, why);
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = scratch_for_current_device(who, &ws);
+    if (rc) return rc;
+  }
+  return run_attention(who, q, k, v, s_head, s_pos, n_ctx, T, anc, Hq, Hkv, d, scale, out, nullptr, n_split, ws,
+                       need, stream);
+}
 
 const char* ts_last_error(void) { return g_err; }
 

@@ -41,7 +41,7 @@ def test_library_exports_every_header_symbol():
     L = _lib()
     missing = [s for s in header_symbols() if not hasattr(L, s)]
     assert not missing, missing
-    assert L.ts_abi_version() == 106
+    assert L.ts_abi_version() == 107
 
 
 def test_workspace_queries_depend_on_shapes_only():
@@ -367,3 +367,19 @@ def test_binding_checks_extents_before_any_launch():
         binding.ngram_tree(win, 20, 1, T_max=24, node_token=torch.zeros(24, dtype=torch.int64))
     with pytest.raises(ValueError, match="info must be"):
         binding.ngram_tree(win, 20, 1, T_max=24, info=torch.zeros(3, dtype=torch.int32))
+
+
+def test_verify_attn_noalloc_rejects_before_any_launch():
+    L = _lib()
+    assert L.ts_verify_attn_noalloc_max_scratch() == 32 << 20
+    par = (ctypes.c_int32 * 3)(-1, 0, 1)
+    # 782 forced splits of a 100K-row cache need 158 MB of partials: beyond the scratch
+    par24 = (ctypes.c_int32 * 24)(-1, *range(23))
+    rc = L.ts_verify_attn_noalloc(FAKE, FAKE, FAKE, 128 * 200_000, 128, 100_000, 24, par24, 32, 8, 128, 0.0, FAKE,
+                                  10_000, None)
+    assert rc == EWORKSPACE and "scratch" in L.ts_last_error().decode()
+    assert L.ts_verify_attn_noalloc(FAKE, FAKE, FAKE, 128 * 200, 128, 100, 3, par, 8, 2, 96, 0.0, FAKE, 0,
+                                    None) == ENOTSUP
+    bad = (ctypes.c_int32 * 3)(-1, 0, 2)
+    assert L.ts_verify_attn_noalloc(FAKE, FAKE, FAKE, 128 * 200, 128, 100, 3, bad, 8, 2, 128, 0.0, FAKE, 1,
+                                    None) == EINVAL
