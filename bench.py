@@ -14,9 +14,11 @@ working set):
 The headline value is the verification attention time per layer-step,
 measured with HIP events around the layers' verification launches on the
 stream the library launches on. Inputs are seeded synthetic tensors of the
-model's shapes, resident in HBM before timing starts.
+model's shapes, resident in HBM before timing starts. The float64 oracle is
+timed beside every kernel on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8b] [--T 24] [--n-ctx 100000]
+    python bench.py --sweep      # one JSON line per workload cell (model classes, T and context sweeps)
 """
 
 import argparse
@@ -29,6 +31,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "tree-verify attn us/layer-step @100K ctx (8B GQA); achieved HBM GB/s vs peak"
+
+# The workload cells of the sweep: the 8B shape over every tree size and
+# context length of its sweep, and the other model classes at 100K rows with
+# their own trees.
+SWEEP = [("8b", T, L) for T in (24, 4, 64) for L in (100_000, 65_536, 32_768, 8_192)] + \
+        [("1.5b", 24, 100_000), ("7b", 24, 100_000), ("14b", 64, 100_000)]
 
 
 def parse():
@@ -45,8 +54,11 @@ def parse():
                     help="verification also writes the selection scores; the selection reads them (no K pass)")
     ap.add_argument("--eta", action="store_true",
                     help="eta-sampling (epsilon 3e-4, alpha sqrt(epsilon)) in place of top-p and min-p")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line per workload cell (fewer steps each; oracle beside every kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=None,
+                    help="oracle time budget per kernel (default 6 s, 2 s in the sweep)")
     ap.add_argument("--no-copy-bw", action="store_true",
                     help="skip the streaming-copy bandwidth measured after the timed steps")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -60,53 +72,95 @@ def verify_bytes(Hq, Hkv, d, n_ctx, T):
     return 2 * Hkv * (n_ctx + T) * d * 2 + Hq * T * d * 2 + Hq * T * d * 4
 
 
-def cpu_baseline(cfg, T, n_ctx, budget_s):
-    """Time the float64 oracle on the host on a bounded sample of one layer:
-    as many KV-head groups as fit in ~budget_s, scaled to the whole layer."""
-    import numpy as np
-    from oracle import bf16_to_f64, verify_attention
-    from synth import attention_inputs, tree_parent
-
+def _threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover - reporting only
-        threads = len(os.sched_getaffinity(0))
-    parent = tree_parent("tokenswift" if T > 4 else "chain", T)
-    G = cfg["Hq"] // cfg["Hkv"]
-    x = attention_inputs(cfg["seed"], G, 1, cfg["d"], n_ctx, T)  # one KV head and its query group
-    per_group = []
+        return len(os.sched_getaffinity(0))
+
+
+def _timed_samples(fn, n_max, budget_s):
+    """Run fn(i) for i = 0, 1, ... until budget_s has passed or n_max samples
+    are done (at least one); returns the per-sample times in seconds."""
+    times = []
     t_start = time.perf_counter()
-    while not per_group or (time.perf_counter() - t_start < budget_s and len(per_group) < cfg["Hkv"]):
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < n_max):
         t0 = time.perf_counter()
-        verify_attention(bf16_to_f64(x["q"]), bf16_to_f64(x["k"]), bf16_to_f64(x["v"]), n_ctx, parent)
-        per_group.append(time.perf_counter() - t0)
-    us_layer = float(np.mean(per_group)) * cfg["Hkv"] * 1e6
-    return {
-        "value": round(us_layer, 1),
-        "unit": "us/layer-step",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"{len(per_group)} KV-head group(s) of one layer (G={G} query heads x T={T}, {n_ctx} context rows, "
-                  f"float64 NumPy), mean time per group x {cfg['Hkv']} groups",
-    }
+        fn(len(times))
+        times.append(time.perf_counter() - t0)
+    return times
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of this path "
-              "is a design note, not a measured configuration.", file=sys.stderr)
-        sys.exit(2)
+def cpu_baselines(cfg, T, n_ctx, budget_s, kernels=("verify", "draft", "select", "penalty")):
+    """The float64 oracle on the host on a bounded sample of each kernel's
+    workload (whole KV-head groups of one layer, or whole logit rows), scaled
+    to the kernel's unit. Input generation is outside the timed region; the
+    bf16 -> float64 conversion is inside."""
+    import numpy as np
+    from oracle import bf16_to_f64, draft_attention, partial_kv_select, penalty_sample, verify_attention
+    from oracle.select import gather_partial
+    from synth import attention_inputs, penalty_inputs, tree_parent
 
+    out = {}
+    G, Hkv, d = cfg["Hq"] // cfg["Hkv"], cfg["Hkv"], cfg["d"]
+    threads = _threads()
+    parent = tree_parent("tokenswift" if T > 4 else "chain", T)
+    if "verify" in kernels:
+        x = attention_inputs(cfg["seed"], G, 1, d, n_ctx, T)   # one KV head and its query group
+        ts_ = _timed_samples(lambda i: verify_attention(bf16_to_f64(x["q"]), bf16_to_f64(x["k"]), bf16_to_f64(x["v"]),
+                                                        n_ctx, parent), Hkv, budget_s)
+        out["verify"] = {"value": round(float(np.mean(ts_)) * Hkv * 1e6, 1), "unit": "us/layer-step", "cores": threads,
+                         "kind": "oracle",
+                         "sample": f"{len(ts_)} KV-head group(s) of one layer (G={G} query heads x T={T}, {n_ctx} "
+                                   f"context rows, float64 NumPy), mean time per group x {Hkv} groups"}
+        del x
+    n_part = cfg["n_sink"] + cfg["budget"] + cfg["n_recent"]
+    if "draft" in kernels:
+        Tq = 4
+        x = attention_inputs(cfg["seed"] + 1, G, 1, d, n_part, Tq)
+        ts_ = _timed_samples(lambda i: draft_attention(bf16_to_f64(x["q"]), bf16_to_f64(x["k"]), bf16_to_f64(x["v"]),
+                                                       n_part), 64, budget_s)
+        out["draft"] = {"value": round(float(np.mean(ts_)) * Hkv * 1e6, 1), "unit": "us/layer-step", "cores": threads,
+                        "kind": "oracle",
+                        "sample": f"{len(ts_)} run(s) of one KV-head group (G={G} x Tq={Tq} over {n_part} partial "
+                                  f"rows), mean x {Hkv} groups"}
+        del x
+    if "select" in kernels:
+        x = attention_inputs(cfg["seed"] + 2, G, 1, d, n_ctx, T)
+
+        def select_and_gather(i):
+            r = partial_kv_select(bf16_to_f64(x["q"]), bf16_to_f64(x["k"]), n_ctx, 1, cfg["n_sink"], cfg["budget"],
+                                  cfg["n_recent"])
+            gather_partial(x["k"], x["v"], r.rows)
+
+        ts_ = _timed_samples(select_and_gather, Hkv, budget_s)
+        out["select"] = {"value": round(float(np.mean(ts_)) * Hkv * 1e6, 1), "unit": "us/layer-step", "cores": threads,
+                         "kind": "oracle",
+                         "sample": f"{len(ts_)} KV head(s) of one layer (scores of G={G} x T={T} queries over {n_ctx} "
+                                   f"rows, top-{cfg['budget']} selection and the row gather), mean x {Hkv} heads"}
+        del x
+    if "penalty" in kernels:
+        rows = T + 4
+        px = penalty_inputs(cfg["seed"], 1, cfg["V"], cfg["W"], sigma=cfg.get("sigma", 2.0))
+        ts_ = _timed_samples(lambda i: penalty_sample(px["logits"], px["window"], 1.2, 1.0, 0.9, 0.05, px["u"]), rows,
+                             budget_s)
+        out["penalty"] = {"value": round(float(np.mean(ts_)) * rows * 1e6, 1), "unit": "us/step", "cores": threads,
+                          "kind": "oracle",
+                          "sample": f"{len(ts_)} logit row(s) of V={cfg['V']} (window {cfg['W']}), mean x {rows} rows "
+                                    "per step"}
+    return out
+
+
+def run_cell(args, name, T, n_ctx, steps, warmup, copy_bw, cpu_budget, cpu_kernels):
+    """Time `steps` steps of one workload cell and return the result object."""
     import torch
     import long_kv_attention_amd as ts
     from synth import CONFIGS, ngram_window, tree_parent
 
-    cfg = dict(CONFIGS[args.config])
-    T = args.T or cfg["T"]
-    n_ctx = args.n_ctx or cfg["n_ctx"]
+    cfg = dict(CONFIGS[name])
     Hq, Hkv, d, layers = cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["layers"]
+    reselect = cfg.get("reselect", 1)
     Tq = 4                                   # drafting: the accepted token + 3 heads' tokens
     n_sink, budget, n_recent = cfg["n_sink"], cfg["budget"], cfg["n_recent"]
     n_part = n_sink + budget + n_recent
@@ -171,7 +225,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     # the committed tokens' window for the n-gram tree (repeated phrases, as generated text has)
     ng_window = torch.from_numpy(ngram_window(cfg["seed"], W, vocab=V, repeat=0.5, n_phrases=8)).to(dev)
     ng_head = torch.randint(0, V, (3, 3), generator=gen, device=dev, dtype=torch.int32)
@@ -212,6 +266,8 @@ def main():
         if e:
             e[2].record(stream)
         if not args.verify_only:
+            # timed every step; a cadence of `reselect` steps is applied to the
+            # per-step figure below
             for Ld in L:
                 if args.fused_scores:
                     ts.partial_kv_select_scored(Ld["sc"], Ld["k"], Ld["v"], n_ctx, n_sink, budget, n_recent,
@@ -238,20 +294,20 @@ def main():
         if e:
             e[6].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     def avg(i, j):
-        return sum(ev[s][i].elapsed_time(ev[s][j]) for s in range(args.steps)) / args.steps * 1e3  # us
+        return sum(ev[s][i].elapsed_time(ev[s][j]) for s in range(steps)) / steps * 1e3  # us
 
     verify_us = avg(0, 1) / layers
-    per_step = sorted(ev[s][0].elapsed_time(ev[s][1]) * 1e3 / layers for s in range(args.steps))
+    per_step = sorted(ev[s][0].elapsed_time(ev[s][1]) * 1e3 / layers for s in range(steps))
     verify_med = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     draft_us = avg(1, 2) / layers
     select_us = avg(2, 3) / layers
@@ -259,14 +315,19 @@ def main():
     commit_us = avg(4, 5)
     ngram_us = avg(5, 6)
     step_ms = avg(0, 6) / 1e3
+    # the partial cache is refreshed every `reselect` steps: its per-step share
+    step_ms_cadence = step_ms - select_us * layers * (1 - 1 / reselect) / 1e3
     vb = verify_bytes(Hq, Hkv, d, n_ctx, T)
     achieved = vb / (verify_us * 1e-6) / 1e9
+
+    del L, K, Vc, KP, VP
+    torch.cuda.empty_cache()
 
     # streaming-copy bandwidth measured in the same process after the timed
     # region (a secondary denominator next to the vendor peak): device-to-device
     # copies of 1 GiB, read + write bytes over event time
     copy_gbps = None
-    if not args.no_copy_bw:
+    if copy_bw:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -284,28 +345,29 @@ def main():
     if os.path.exists(tpath):
         try:
             tj = json.load(open(tpath))
-            key = f"{args.config}_L{n_ctx}_T{T}"
+            key = f"{name}_L{n_ctx}_T{T}"
             if tj.get("kernel_source_sha") == _attn_source_sha() and key in tj.get("bytes_per_launch", {}):
                 traffic = tj["bytes_per_launch"][key]
         except Exception:
             traffic = None
 
     res = {
-        "metric": "tree-verify attn us/layer-step @100K ctx (8B GQA); achieved HBM GB/s vs peak",
+        "metric": METRIC,
         "value": round(verify_us, 3),
         "unit": "us/layer-step",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}-class {'GQA' if Hq != Hkv else 'MHA'} tree verification, "
+        "config": {"workload": f"{name}-class {'GQA' if Hq != Hkv else 'MHA'} tree verification, "
                                f"{Hq} q / {Hkv} kv heads, d={d}, {n_ctx} context rows, T={T} tree nodes, {layers} layers",
                    "global_batch": 1, "seq_len": n_ctx, "tree_nodes": T, "layers": layers,
+                   "reselect_every": reselect,
                    "fused_scores": bool(args.fused_scores), "eta_sampling": bool(args.eta),
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -317,14 +379,53 @@ def main():
         "kernels_us": {"verify_per_layer": round(verify_us, 3),
                        "verify_per_layer_median": round(verify_med, 3), "verify_per_layer_min": round(per_step[0], 3),
                        "verify_per_layer_max": round(per_step[-1], 3), "draft_per_layer": round(draft_us, 3),
-                       "select_per_layer": round(select_us, 3), "penalty_per_step": round(penalty_us, 3),
+                       "select_per_layer": round(select_us, 3),
+                       "select_per_layer_per_step": round(select_us / reselect, 3),
+                       "penalty_per_step": round(penalty_us, 3),
                        "accept_commit_per_step": round(commit_us, 3), "ngram_tree_per_step": round(ngram_us, 3),
                        "verify_bytes_per_launch": vb},
+        "ms_per_step_with_reselect_cadence": round(step_ms_cadence, 4),
         "wall_s": round(wall, 3),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, T, n_ctx, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    if cpu_budget:
+        base = cpu_baselines(cfg, T, n_ctx, cpu_budget, cpu_kernels)
+        if "verify" in base:
+            res["cpu_baseline"] = base.pop("verify")
+        if base:
+            res["cpu_baseline_other_kernels"] = base
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of this path "
+              "is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    from synth import CONFIGS
+
+    if not args.sweep:
+        cfg = CONFIGS[args.config]
+        T = args.T or cfg["T"]
+        n_ctx = args.n_ctx or cfg["n_ctx"]
+        budget = None if args.no_cpu_baseline else (args.cpu_seconds or 6.0)
+        res = run_cell(args, args.config, T, n_ctx, args.steps, args.warmup, not args.no_copy_bw, budget,
+                       ("verify", "draft", "select", "penalty"))
+        print(json.dumps(res), flush=True)
+        return
+
+    # sweep: fewer steps per cell; the oracle beside the verification kernel in
+    # every cell and beside the other kernels once per model class
+    steps = min(args.steps, 8)
+    warmup = min(args.warmup, 2)
+    budget = None if args.no_cpu_baseline else (args.cpu_seconds or 2.0)
+    seen = set()
+    for name, T, n_ctx in SWEEP:
+        kernels = ("verify",) if name in seen else ("verify", "draft", "select", "penalty")
+        seen.add(name)
+        res = run_cell(args, name, T, n_ctx, steps, warmup, False, budget, kernels)
+        res["sweep_cell"] = f"{name}_L{n_ctx}_T{T}"
+        print(json.dumps(res), flush=True)
 
 
 def _gpu_env(torch):

@@ -23,7 +23,7 @@ CONFIGS = {
     "8b": dict(Hq=32, Hkv=8, d=128, n_ctx=100_000, T=24, tree="tokenswift", budget=4096,
                n_sink=4, n_recent=64, V=128256, W=1024, layers=32, seed=3, sigma=2.0),
     "14b": dict(Hq=40, Hkv=8, d=128, n_ctx=100_000, T=64, tree="tokenswift", budget=8192,
-                n_sink=4, n_recent=64, V=152064, W=1024, layers=48, seed=4, sigma=2.0),
+                n_sink=4, n_recent=64, V=152064, W=1024, layers=48, seed=4, sigma=2.0, reselect=64),
 }
 
 
