@@ -211,8 +211,8 @@ def run_cell(args, name, T, n_ctx, steps, warmup, copy_bw, cpu_budget, cpu_kerne
     lib = ts.lib()
     ws_v = torch.empty(max(1, lib.ts_verify_attn_workspace_size(n_ctx, T, Hq, Hkv, d, args.n_split)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(1, lib.ts_draft_attn_workspace_size(n_part, Tq, Hq, Hkv, d, 0)), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(max(1, lib.ts_partial_kv_select_workspace_size(n_ctx, T, Hq, Hkv, d, budget)), dtype=torch.uint8, device=dev)
-    ws_ss = torch.empty(max(1, lib.ts_partial_kv_select_scored_workspace_size(n_ctx, Hkv, d, budget)), dtype=torch.uint8, device=dev)
+    ws_s = torch.zeros(max(1, lib.ts_partial_kv_select_workspace_size(n_ctx, T, Hq, Hkv, d, budget)), dtype=torch.uint8, device=dev)
+    ws_ss = torch.zeros(max(1, lib.ts_partial_kv_select_scored_workspace_size(n_ctx, Hkv, d, budget)), dtype=torch.uint8, device=dev)
     z_out = torch.empty_like(logits)
     torch.cuda.synchronize()
 

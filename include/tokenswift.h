@@ -35,7 +35,10 @@
  *   returns a message for the calling thread.
  * - Workspace: each entry point has a *_workspace_size() query that depends
  *   on shapes only (no device needed). Pass at least that many bytes, 256-byte
- *   aligned. Workspace contents need not be initialised and are scratch.
+ *   aligned. Workspace contents need not be initialised and are scratch. The
+ *   selection calls leave a histogram in their workspace at zero for the
+ *   next call: a workspace reused from such a call (or zero-filled once)
+ *   saves the first call a recount of each KV head's scores.
  */
 #ifndef TOKENSWIFT_H
 #define TOKENSWIFT_H

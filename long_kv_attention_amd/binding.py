@@ -155,14 +155,16 @@ def partial_rows(n_ctx, n_sink, budget, n_recent):
     return n
 
 
-def _workspace(nbytes, device, ws):
+def _workspace(nbytes, device, ws, zeroed=False):
+    """The caller's workspace (checked for size) or a new one (zero-filled when
+    the call runs faster on a zero workspace: the selection's)."""
     if nbytes == 0:
         return None
     if ws is not None:
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes, need {nbytes}")
         return ws
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return (torch.zeros if zeroed else torch.empty)(nbytes, dtype=torch.uint8, device=device)
 
 
 def verify_attn(q, k, v, n_ctx, parent, scale=0.0, n_split=0, out=None, ws=None, stream=None):
@@ -267,7 +269,7 @@ def partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, k_part=None, v_p
     scores = _score_buffer(scores, Hkv, n_ctx, dev) if want_scores else None
     L = lib()
     need = L.ts_partial_kv_select_workspace_size(n_ctx, T, Hq, Hkv, d, budget)
-    wst = _workspace(need, dev, ws)
+    wst = _workspace(need, dev, ws, zeroed=True)
     n_part = ctypes.c_int32(-1)
     rc = L.ts_partial_kv_select(_ptr(q), T, _ptr(k), _ptr(v), s_head, s_pos, n_ctx, Hq, Hkv, d, n_sink, budget,
                                 n_recent, _ptr(sel_idx), _ptr(k_part), _ptr(v_part), sp_head, sp_pos,
@@ -303,7 +305,7 @@ def partial_kv_select_scored(scores, k, v, n_ctx, n_sink, budget, n_recent, k_pa
         _dense(sel_idx, torch.int32, "sel_idx", (Hkv, max(budget, 1)))
     L = lib()
     need = L.ts_partial_kv_select_scored_workspace_size(n_ctx, Hkv, d, budget)
-    wst = _workspace(need, dev, ws)
+    wst = _workspace(need, dev, ws, zeroed=True)
     n_part = ctypes.c_int32(-1)
     rc = L.ts_partial_kv_select_scored(_ptr(scores), _ptr(k), _ptr(v), s_head, s_pos, n_ctx, Hkv, d, n_sink, budget,
                                        n_recent, _ptr(sel_idx), _ptr(k_part), _ptr(v_part), sp_head, sp_pos,

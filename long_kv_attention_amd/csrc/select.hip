@@ -9,26 +9,34 @@
 // sink U selected U recent.
 //
 // Kernels (one stream, in order):
-//   1. clear     grid Hkv: clears the head's histograms.
-//   2. score     grid (chunks, Hkv): qbar_g in fp32 from the group's query
+//   1. score     grid (chunks, Hkv): qbar_g in fp32 from the group's query
 //                rows (copied to LDS while the first K tile is in flight),
 //                then one HBM pass over K. 16 lanes x 16 B per row (d=128),
 //                lane-local FMAs then a 16-lane reduction; the block also
 //                histograms the top 12 bits of each candidate's
 //                order-preserving key and adds its non-empty bins to the
-//                head's global histogram.
-//   3. cutbin    grid (nb, Hkv): every block finds the top-12-bit bin holding
+//                head's global histogram; the blocks also clear the head's
+//                second-digit histogram for pass 2.
+//   2. cutbin    grid (nb, Hkv): every block finds the top-12-bit bin holding
 //                the B'-th key, lists its chunk's keys in that bin, counts its
 //                keys in higher bins and adds the next 10 bits of its listed
 //                keys to the head's second-digit histogram; the blocks also
 //                share out the -1 padding of sel_idx and the copies of the
 //                sink and recent rows.
-//   4. emit      grid (nb, Hkv): every block takes the second digit from that
+//   3. emit      grid (nb, Hkv): every block takes the second digit from that
 //                histogram and the last one from the lists (exact cut), counts
 //                the rows taken by earlier blocks, writes its selected rows in
 //                ascending order and copies their K and V rows into the
-//                partial cache.
-// Passes 3 and 4 read the L2-resident scores, not K.
+//                partial cache; the blocks also clear the head's first-digit
+//                histogram for the next call (pass 2 does it when nothing is
+//                selected).
+// Passes 2 and 3 read the L2-resident scores, not K.
+//
+// The first-digit histogram is left at zero by every call, so no clearing
+// launch is needed. A workspace that does not hold a zero histogram (its
+// first use, or a call that did not complete) is caught by pass 2: the
+// histogram's total must be the head's candidate count, and when it is not,
+// each block rebuilds the head's histogram from the scores.
 //
 // With the scores given (computed by the verification pass over the same
 // queries), pass 2 becomes one read of the scores that fills the first-digit
@@ -81,7 +89,7 @@ __device__ inline float row16_sum(float x) {
 // ahead of the first K tile, so the sum runs while that tile is in flight.
 template <int D>
 __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const SelectParams p, unsigned int* ghist,
-                                                                    int rows_per_block) {
+                                                                    unsigned int* ghist2, int rows_per_block) {
   constexpr int NT = SC_WAVES * 64;
   constexpr int LPR = D / 8;                 // lanes per row
   constexpr int RPW = 64 / LPR;              // rows per wave per step
@@ -136,6 +144,8 @@ __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const Selec
   };
   issue_q(0);
   if (ntiles > 0) issue(0);
+  // the head's second-digit histogram, for pass 2 (nothing reads it before)
+  for (int b = blockIdx.x * NT + tid; b < HIST2; b += gridDim.x * NT) ghist2[g * HIST2 + b] = 0u;
   float qa[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // channels [8 sub', 8 sub' + 8) of this thread's row slots
   const int nqc = (qrows + QCH - 1) / QCH;
   for (int c = 0; c < nqc; ++c) {
@@ -224,21 +234,15 @@ __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const Selec
   }
 }
 
-// Clears the head's histograms (scores given: nothing else to prepare).
-__global__ __launch_bounds__(256) void select_clear_kernel(unsigned int* hist, unsigned int* hist2) {
-  const int g = blockIdx.x;
-  for (int b = threadIdx.x; b < HIST1; b += 256) hist[g * HIST1 + b] = 0u;
-  for (int b = threadIdx.x; b < HIST2; b += 256) hist2[g * HIST2 + b] = 0u;
-}
-
 // First-digit histogram of the given scores of the candidate rows: one block
 // per chunk of rows_per_block candidates of one KV head, LDS histogram, then
 // the non-empty bins added to the head's global histogram.
 __global__ __launch_bounds__(256) void select_hist_kernel(const SelectParams p, unsigned int* ghist,
-                                                         int rows_per_block) {
+                                                         unsigned int* ghist2, int rows_per_block) {
   __shared__ unsigned int lhist[HIST1];
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
+  for (int b = blockIdx.x * 256 + tid; b < HIST2; b += gridDim.x * 256) ghist2[g * HIST2 + b] = 0u;
   for (int b = tid; b < HIST1; b += 256) lhist[b] = 0u;
   __syncthreads();
   const int r0 = p.cand_lo + blockIdx.x * rows_per_block;
@@ -331,13 +335,14 @@ __device__ inline unsigned int block_exclusive_scan(unsigned int x, unsigned int
 // higher bins). Each thread owns nbins / NT consecutive bins.
 template <int NT>
 __device__ inline void find_bin(const unsigned int* hist, int nbins, unsigned int k, unsigned int* tmp, int* bin_out,
-                                unsigned int* above_out) {
+                                unsigned int* above_out, unsigned int* total_out = nullptr) {
   const int per = nbins / NT;
   const int hi_bin = nbins - 1 - threadIdx.x * per;   // thread t covers the t-th group from the top
   unsigned int s = 0;
   for (int i = 0; i < per; ++i) s += hist[hi_bin - i];
   unsigned int total;
   const unsigned int before = block_exclusive_scan<NT>(s, tmp, &total);
+  if (total_out) *total_out = total;
   if (before < k && k <= before + s) {
     unsigned int acc = before;
     for (int i = 0; i < per; ++i) {
@@ -490,11 +495,23 @@ __global__ __launch_bounds__(PT) void select_cutbin_kernel(const SelectParams p,
     copy_rows<D>(p, g, n_copy, item0 + stride, stride, pair);
   };
   if (k == 0) {
+    // nothing is selected, so no later pass runs: clear the first-digit
+    // histogram here (no block of this pass reads it)
+    for (int b = blockIdx.x * PT + tid; b < HIST1; b += nb * PT) ws.hist[g * HIST1 + b] = 0u;
     finish_copies();
     return;
   }
   bar();
-  find_bin<PT>(hist, HIST1, k, tmp, &s_bin, &s_above);
+  unsigned int total = 0;
+  find_bin<PT>(hist, HIST1, k, tmp, &s_bin, &s_above, &total);
+  if (total != (unsigned int)(p.cand_hi - p.cand_lo)) {
+    // the histogram did not start at zero: count this head's candidates here
+    for (int b = tid; b < HIST1; b += PT) hist[b] = 0u;
+    bar();
+    for (int j = p.cand_lo + tid; j < p.cand_hi; j += PT) atomicAdd(&hist[f2key(sc[j]) >> (32 - HIST1_BITS)], 1u);
+    bar();
+    find_bin<PT>(hist, HIST1, k, tmp, &s_bin, &s_above);
+  }
   const unsigned int bin = (unsigned int)s_bin;
   constexpr int SH2 = 32 - HIST1_BITS - HIST2_BITS;
   unsigned int n_hi = 0;   // this thread's keys in higher first-digit bins
@@ -575,6 +592,8 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
   int c0, c1;
   chunk_of(p, nb, blockIdx.x, &c0, &c1);
   const float* sc = p.scores + (int64_t)g * p.n_ctx;
+  // pass 2 has read the first-digit histogram: leave it at zero for the next call
+  for (int b = blockIdx.x * PT + tid; b < HIST1; b += nb * PT) ws.hist[g * HIST1 + b] = 0u;
   // Every load the cut needs goes out at once: lane b of every wave takes
   // block b's list length and higher-bin count, then the second-digit
   // histogram, each wave the first 64 slots of the lists of blocks wave,
@@ -790,7 +809,6 @@ size_t select_passes_workspace_bytes(int32_t n_ctx, int32_t Hkv) { return sel_ws
 
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   const SelWs ws = carve(p.sel_ws, p.Hkv, p.n_ctx);
-  hipLaunchKernelGGL(select_clear_kernel, dim3(p.Hkv), dim3(256), 0, stream, ws.hist, ws.hist2);
   if (p.scores_given) {
     const int n_cand = p.cand_hi - p.cand_lo;
     if (n_cand > 0) {
@@ -798,7 +816,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
       int rpb = (n_cand + chunks - 1) / chunks;
       if (rpb < 2048) rpb = 2048;
       chunks = (n_cand + rpb - 1) / rpb;
-      hipLaunchKernelGGL(select_hist_kernel, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, ws.hist, rpb);
+      hipLaunchKernelGGL(select_hist_kernel, dim3(chunks, p.Hkv), dim3(256), 0, stream, p, ws.hist, ws.hist2, rpb);
     }
   }
   if (!p.scores_given && p.n_ctx > 0) {
@@ -809,9 +827,11 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
     if (rpb < SC_ROWS) rpb = SC_ROWS;
     chunks = (p.n_ctx + rpb - 1) / rpb;
     if (p.d == 128)
-      hipLaunchKernelGGL(select_score_kernel<128>, dim3(chunks, p.Hkv), dim3(SC_WAVES * 64), 0, stream, p, ws.hist, rpb);
+      hipLaunchKernelGGL(select_score_kernel<128>, dim3(chunks, p.Hkv), dim3(SC_WAVES * 64), 0, stream, p, ws.hist,
+                         ws.hist2, rpb);
     else
-      hipLaunchKernelGGL(select_score_kernel<64>, dim3(chunks, p.Hkv), dim3(SC_WAVES * 64), 0, stream, p, ws.hist, rpb);
+      hipLaunchKernelGGL(select_score_kernel<64>, dim3(chunks, p.Hkv), dim3(SC_WAVES * 64), 0, stream, p, ws.hist,
+                         ws.hist2, rpb);
   }
   // the cut-bin pass always runs: it also pads sel_idx and copies the sink and recent rows
   const int nb = select_blocks_per_head(p.n_ctx, p.Hkv, p.n_sink, p.n_recent);

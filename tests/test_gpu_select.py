@@ -18,9 +18,9 @@ from tests.gpu_util import banner, dev_bf16, rel_max_err
 pytestmark = pytest.mark.gpu
 
 
-def _check(x, n_ctx, Hq, Hkv, n_sink, budget, n_recent, heads=None, strict=False):
+def _check(x, n_ctx, Hq, Hkv, n_sink, budget, n_recent, heads=None, strict=False, ws=None):
     q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
-    sel, kp, vp, n_part, sc = ts.partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, want_scores=True)
+    sel, kp, vp, n_part, sc = ts.partial_kv_select(q, k, v, n_ctx, n_sink, budget, n_recent, want_scores=True, ws=ws)
     torch.cuda.synchronize()
     sel, sc = sel.cpu().numpy(), sc.cpu().numpy()[:, :n_ctx]
     kp = kp.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -138,6 +138,31 @@ def test_many_query_rows_per_head(T, Hq, Hkv):
     banner(f"select T={T} Hq={Hq} Hkv={Hkv}")
     x = attention_inputs(40 + T, Hq, Hkv, 128, n_ctx, T)
     _check(x, n_ctx, Hq, Hkv, 4, 700, 64)
+
+
+@pytest.mark.parametrize("fill", [0xFF, 0x01])
+def test_workspace_not_at_zero(fill):
+    """The calls leave the first-digit histogram at zero for the next call;
+    a workspace that does not hold a zero histogram (first use, or filled
+    with other data) is recounted from the scores: exact either way, on two
+    calls in a row (the second with a smaller budget) and through the
+    scored entry point."""
+    n_ctx, Hq, Hkv = 20_000, 32, 8
+    banner(f"select on a workspace filled with {fill:#x}")
+    x = attention_inputs(81, Hq, Hkv, 128, n_ctx, 24)
+    need = ts.lib().ts_partial_kv_select_workspace_size(n_ctx, 24, Hq, Hkv, 128, 2000)
+    ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda:0")
+    _check(x, n_ctx, Hq, Hkv, 4, 2000, 64, ws=ws)
+    _check(x, n_ctx, Hq, Hkv, 4, 700, 64, ws=ws)
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    _, _, _, _, sc = ts.partial_kv_select(q, k, v, n_ctx, 4, 2000, 64, want_scores=True)
+    wss = torch.full((ts.lib().ts_partial_kv_select_scored_workspace_size(n_ctx, Hkv, 128, 2000),), fill,
+                     dtype=torch.uint8, device="cuda:0")
+    sel1 = ts.partial_kv_select_scored(sc, k, v, n_ctx, 4, 2000, 64, ws=wss)[0]
+    sel2 = ts.partial_kv_select_scored(sc, k, v, n_ctx, 4, 2000, 64, ws=wss)[0]
+    ref = ts.partial_kv_select(q, k, v, n_ctx, 4, 2000, 64)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(sel1, ref) and torch.equal(sel2, ref)
 
 
 def test_full_budget_draft_equals_verification():
