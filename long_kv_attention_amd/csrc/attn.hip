@@ -781,7 +781,10 @@ constexpr int KV_TILE = 128;  // split granularity in positions (a multiple of e
 // the rows go to several workgroups (grid.z) of 12 or 16 row tiles, whichever
 // pads fewer. Measured at 100K: T = 48 (12 row tiles) 132 us with (4, 2, 3)
 // against 164 us with four waves (4, 1, 3); T = 64 (16) 154 against 185 us
-// with (4, 1, 4); 14B T = 64 (20) 214 against 240 us with (4, 1, 5).
+// with (4, 1, 4); 14B T = 64 (20) 214 against 240 us with (4, 1, 5); the
+// 1.5B shape (9 row tiles) 46.1 us with (4, 2, 3) (three padded row tiles,
+// eight waves) against 48.0 us with six waves (3, 2, 3), whose SIMDs hold
+// two waves or one.
 KernelChoice choose(int nrt) {
   if (nrt <= 1) return {1, 4, 1};
   if (nrt == 2) return {1, 4, 2};
@@ -789,7 +792,6 @@ KernelChoice choose(int nrt) {
   if (nrt == 4) return {2, 4, 2};
   if (nrt <= 6) return {2, 4, 3};
   if (nrt <= 8) return {4, 2, 2};
-  if (nrt == 9) return {3, 2, 3};
   if (nrt <= 12) return {4, 2, 3};
   if (nrt <= 16) return {4, 2, 4};
   const int pad3 = (nrt + 11) / 12 * 12, pad4 = (nrt + 15) / 16 * 16;
@@ -820,7 +822,6 @@ hipError_t launch_split_d(const AttnParams& p, const KernelChoice& kc, int nz, h
   TS_CASE(2, 4, 2)
   TS_CASE(2, 4, 3)
   TS_CASE(4, 2, 2)
-  TS_CASE(3, 2, 3)
   TS_CASE(4, 2, 3)
   TS_CASE(4, 2, 4)
 #undef TS_CASE
