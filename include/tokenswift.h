@@ -88,8 +88,11 @@ extern "C" {
  *
  * Precision: q.k in bf16 x bf16 with float32 accumulation; softmax in
  * float32; probabilities and v enter the p.v product as float16 with float32
- * accumulation, so |v| must stay below 65504 (bf16 values beyond the float16
- * range are not supported).
+ * accumulation. Every bf16 value of v up to 65280 in magnitude is exact in
+ * float16; a value of 65536 or more (beyond the float16 range) converts to
+ * +-inf, so the output rows that see it come out non-finite in that channel
+ * (never a silently clamped value). The call still returns TS_OK: the
+ * library does not scan v.
  */
 int ts_verify_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                    int64_t s_head, int64_t s_pos, int32_t n_ctx, int32_t T,

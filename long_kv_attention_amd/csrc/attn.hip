@@ -55,6 +55,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -142,13 +143,14 @@ __device__ inline float group4_max(float x) {
   return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// bf16 pair (low, high halves of a 32-bit word) -> f16 pair. Exact for
-// |x| < 65504; larger magnitudes saturate to +-65504 (round toward zero).
+// bf16 pair (low, high halves of a 32-bit word) -> f16 pair in one
+// v_cvt_pk_f16_f32 (round to nearest even). Exact for bf16 values in the f16
+// normal range; magnitudes of 65536 and up (the next bf16 value past the f16
+// maximum) become +-inf, so such a V value makes the output rows that see it
+// non-finite instead of silently clamped.
 __device__ inline unsigned int bf16x2_to_f16x2(unsigned int w) {
-  float lo = __uint_as_float(w << 16);
-  float hi = __uint_as_float(w & 0xffff0000u);
-  auto h = __builtin_amdgcn_cvt_pkrtz(lo, hi);
-  return __builtin_bit_cast(unsigned int, h);
+  const f2v x = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector(x, f16x2));
 }
 
 template <int CTRL>

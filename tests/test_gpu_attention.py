@@ -130,6 +130,58 @@ def test_verify_rejects_bad_tree_on_device_path():
     assert e.value.code == -1
 
 
+def _bf16_bits(value):
+    """bfloat16 bit pattern of a value that bfloat16 holds exactly."""
+    b = np.array([value], dtype=np.float32).view(np.uint32)[0]
+    assert b & 0xFFFF == 0, value
+    return np.uint16(b >> 16)
+
+
+@pytest.mark.parametrize("n_split", [1, 0, 7])
+def test_v_at_the_float16_limit(n_split):
+    """V entries of +-65280, the largest bfloat16 magnitude inside the float16
+    range, go through the float16 P.V product unclamped (verification and
+    draft entry points)."""
+    banner(f"verify/draft V = +-65280 n_split={n_split}")
+    Hq, Hkv, d, n_ctx = 8, 2, 128, 3000
+    parent = tree_parent("tokenswift", 24)
+    x = attention_inputs(41, Hq, Hkv, d, n_ctx, len(parent))
+    rng = np.random.default_rng(41)
+    for _ in range(64):   # committed and tree rows, both signs
+        g, j, c = int(rng.integers(0, Hkv)), int(rng.integers(0, n_ctx + len(parent))), int(rng.integers(0, d))
+        x["v"][g, j, c] = _bf16_bits(65280.0 if rng.integers(0, 2) else -65280.0)
+    got = _run_verify(x, n_ctx, parent, n_split)
+    assert np.isfinite(got).all()
+    assert rel_max_err(got, _oracle(x, n_ctx, parent)) <= TOL
+    q, k, v = dev_bf16(x["q"][:, :4]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    gd = ts.draft_attn(q, k, v, n_ctx, n_split=n_split)
+    torch.cuda.synchronize()
+    refd = draft_attention(bf16_to_f64(x["q"][:, :4]), bf16_to_f64(x["k"]), bf16_to_f64(x["v"]), n_ctx)
+    assert rel_max_err(gd.cpu().numpy(), refd) <= TOL
+
+
+@pytest.mark.parametrize("n_split", [1, 0, 7])
+def test_v_beyond_float16_range_is_not_clamped(n_split):
+    """A V entry past the float16 range (2^20 in a committed row: every query
+    sees it) makes that channel of every output row of its KV head's group
+    non-finite instead of a silently clamped value; every other channel and
+    group still matches the oracle."""
+    banner(f"verify V = 2^20 n_split={n_split}")
+    Hq, Hkv, d, n_ctx = 8, 2, 128, 3000
+    G = Hq // Hkv
+    parent = tree_parent("tokenswift", 24)
+    x = attention_inputs(43, Hq, Hkv, d, n_ctx, len(parent))
+    g, j, c = 1, 1234, 5
+    x["v"][g, j, c] = _bf16_bits(2.0 ** 20)
+    got = _run_verify(x, n_ctx, parent, n_split)
+    assert not np.isfinite(got[g * G:(g + 1) * G, :, c]).any()
+    ok = np.ones(got.shape, dtype=bool)
+    ok[g * G:(g + 1) * G, :, c] = False
+    assert np.isfinite(got[ok]).all()
+    ref = _oracle(x, n_ctx, parent)
+    assert rel_max_err(got[ok], ref[ok]) <= TOL
+
+
 FULL = [("8b", 24, "tokenswift", [0, 5]), ("8b", 64, "tokenswift", [3]), ("8b", 4, "chain", [7]),
         ("1.5b", 24, "tokenswift", [1]), ("7b", 24, "tokenswift", [0, 31]), ("14b", 64, "tokenswift", [2]),
         ("8b", 88, "wide", [6]), ("8b", 128, "wide", [1])]
