@@ -46,12 +46,7 @@ __device__ inline u64 splitmix64(u64 seed, u64 j) {
 // holds one slot per wave. Every thread gets the total.
 __device__ inline int block_scan(int x, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_incl_scan(x);
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
   int before = 0, tot = 0;

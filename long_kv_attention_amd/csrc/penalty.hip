@@ -188,11 +188,7 @@ __device__ inline T block_sum(T x, T* red) {
 template <typename T>
 __device__ inline T block_scan(T x, T* red, T* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  T incl = x;
-  for (int off = 1; off < 64; off <<= 1) {
-    const T y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const T incl = wave_incl_scan(x);
   if (lane == 63) red[wave] = incl;
   bar();
   T pre = 0, tot = 0;

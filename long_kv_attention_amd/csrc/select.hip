@@ -310,12 +310,7 @@ template <int NT>
 __device__ inline unsigned int block_exclusive_scan(unsigned int x, unsigned int* tmp, unsigned int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  unsigned int incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const unsigned int incl = wave_incl_scan(x);
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
   unsigned int wave_prefix = 0, tot = 0;
@@ -526,12 +521,7 @@ __global__ __launch_bounds__(PT) void select_cutbin_kernel(const SelectParams p,
       n_hi += j0 + e < c1 && kb > bin;
     }
     // in-wave exclusive prefix of the list lengths; one LDS atomic per wave
-    unsigned int incl = nc;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
+    const unsigned int incl = wave_incl_scan(nc);
     unsigned int base = 0;
     if (lane == 63 && incl) base = atomicAdd(&s_n, incl);
     base = __shfl(base, 63) + incl - nc;
@@ -627,12 +617,7 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
 #pragma unroll
   for (int i = 0; i < PER; ++i) reinterpret_cast<u32x4*>(hist)[tid + i * PT] = h2v[i];
   // list offsets: every wave scans the list lengths (lanes >= nb hold 0)
-  unsigned int incl = cl;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const unsigned int incl = wave_incl_scan(cl);
   const unsigned int loff = incl - cl;   // lane b: offset of block b's list in the concatenation
   const unsigned int n = __builtin_amdgcn_readlane(incl, 63);
   if (wave == 0) {
@@ -674,12 +659,7 @@ __global__ __launch_bounds__(PT) void select_emit_kernel(const SelectParams p, i
       }
     }
     const unsigned int np = cl > 64 ? (cl - 1) / 64 : 0;   // pieces past the first 64 slots
-    unsigned int pend = np;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned int y = __shfl_up(pend, off);
-      if (lane >= off) pend += y;
-    }
+    const unsigned int pend = wave_incl_scan(np);
     const unsigned int n_pieces = __builtin_amdgcn_readlane(pend, 63);
     constexpr int BATCH = 8;
     for (unsigned int q0 = wave; q0 < n_pieces; q0 += (PT / 64) * BATCH) {

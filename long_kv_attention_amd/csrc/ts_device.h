@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 namespace ts {
 
 typedef unsigned long long u64;
@@ -18,6 +20,46 @@ __device__ inline void bar() {
 }
 
 __device__ inline u64 lanemask_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
+
+// Inclusive prefix sum over the 64 lanes of a wave, with no LDS round trip:
+// Hillis-Steele steps inside each 16-lane row by DPP row shifts (1, 2, 4, 8;
+// a lane shifted in from outside its row adds 0), then each lane adds the
+// totals of the rows below it, read from lanes 15, 31 and 47. Every lane of
+// the wave must be active. Exact for integers (the order of the additions
+// does not matter).
+template <int CTRL>
+__device__ inline unsigned int dpp_zero(unsigned int v) {
+  return (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ inline unsigned int wave_incl_scan(unsigned int x) {
+  x += dpp_zero<0x111>(x);   // row_shr:1
+  x += dpp_zero<0x112>(x);   // row_shr:2
+  x += dpp_zero<0x114>(x);   // row_shr:4
+  x += dpp_zero<0x118>(x);   // row_shr:8
+  const unsigned int r0 = (unsigned int)__builtin_amdgcn_readlane(x, 15);
+  const unsigned int r1 = (unsigned int)__builtin_amdgcn_readlane(x, 31);
+  const unsigned int r2 = (unsigned int)__builtin_amdgcn_readlane(x, 47);
+  const unsigned int lane = threadIdx.x & 63;
+  return x + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+}
+__device__ inline int wave_incl_scan(int x) { return (int)wave_incl_scan((unsigned int)x); }
+__device__ inline u64 wave_incl_scan(u64 x) {
+  auto shr = [](u64 v, auto c) {
+    constexpr int CTRL = decltype(c)::value;
+    return (u64)dpp_zero<CTRL>((unsigned int)v) | ((u64)dpp_zero<CTRL>((unsigned int)(v >> 32)) << 32);
+  };
+  x += shr(x, std::integral_constant<int, 0x111>{});
+  x += shr(x, std::integral_constant<int, 0x112>{});
+  x += shr(x, std::integral_constant<int, 0x114>{});
+  x += shr(x, std::integral_constant<int, 0x118>{});
+  auto at = [&](int l) {   // readlane returns a signed int: widen it unsigned
+    return (u64)(unsigned int)__builtin_amdgcn_readlane((unsigned int)x, l) |
+           ((u64)(unsigned int)__builtin_amdgcn_readlane((unsigned int)(x >> 32), l) << 32);
+  };
+  const u64 r0 = at(15), r1 = at(31), r2 = at(47);
+  const unsigned int lane = threadIdx.x & 63;
+  return x + (lane >= 16 ? r0 : 0ull) + (lane >= 32 ? r1 : 0ull) + (lane >= 48 ? r2 : 0ull);
+}
 
 #define LDS_AS __attribute__((address_space(3)))
 
