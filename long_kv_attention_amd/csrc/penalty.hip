@@ -497,7 +497,7 @@ __global__ __launch_bounds__(PB) void pen_z_kernel(const PenaltyParams p, int nb
       const int leader = __ffsll((long long)bm) - 1;
       unsigned int base = 0;
       if (lane == leader) base = atomicAdd(&s_n, (unsigned int)__popcll(bm));
-      base = __shfl(base, leader);
+      base = lane_value(base, leader);
       const unsigned int slot = base + (unsigned int)__popcll(bm & lanemask_lt());
       if (take && slot < (unsigned int)CAP_B) out[slot] = sort_key(w, i);
     }
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(PB) void pen_out_kernel(const PenaltyParams p, int 
         const int leader = __ffsll((long long)bm) - 1;
         unsigned int base = 0;
         if (lane == leader) base = atomicAdd(&s_n, (unsigned int)__popcll(bm));
-        base = __shfl(base, leader);
+        base = lane_value(base, leader);
         const unsigned int slot = base + (unsigned int)__popcll(bm & lanemask_lt());
         if (take && slot < (unsigned int)SCAP) list[slot] = e;
       }
@@ -1127,7 +1127,7 @@ __global__ __launch_bounds__(PB) void pen_eta_out_kernel(const PenaltyParams p, 
   const int lb = lane < nb ? ws.pl[row * NBR_MAX + lane] : -1;
   const u64 W = wave_reduce(wb, OpAdd());
   const u64 below = wave_reduce(lane < (int)blockIdx.x ? wb : 0ull, OpAdd());
-  const u64 inside = __shfl(wb, (int)blockIdx.x);
+  const u64 inside = lane_value(wb, (int)blockIdx.x);
   const int last = wave_reduce(lb, OpMaxI());
   Cut c;
   c.zmax = st.zmax;

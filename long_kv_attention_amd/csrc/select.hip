@@ -167,10 +167,13 @@ __global__ __launch_bounds__(SC_WAVES * 64) void select_score_kernel(const Selec
   }
   // row slots of a wave, then the waves, in a fixed order (deterministic);
   // the histogram's LDS holds the per-wave sums until it is cleared
+  static_assert(LPR == 8 || LPR == 16, "row slots of 8 or 16 lanes");
 #pragma unroll
-  for (int m = LPR; m < 64; m <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qa[e] += __shfl_xor(qa[e], m);
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (LPR == 8) qa[e] = xor_add<8>(qa[e]);
+    qa[e] = xor_add<16>(qa[e]);
+    qa[e] = xor_add<32>(qa[e]);
+  }
   static_assert(SC_WAVES * D <= HIST1, "per-wave sums fit the histogram's LDS");
   float* qpart = reinterpret_cast<float*>(lhist);
   if (lane < LPR)
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(PT) void select_cutbin_kernel(const SelectParams p,
     const unsigned int incl = wave_incl_scan(nc);
     unsigned int base = 0;
     if (lane == 63 && incl) base = atomicAdd(&s_n, incl);
-    base = __shfl(base, 63) + incl - nc;
+    base = lane_value(base, 63) + incl - nc;
     if (nc) {
 #pragma unroll
       for (int e = 0; e < RPT; ++e)

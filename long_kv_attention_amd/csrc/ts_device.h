@@ -43,6 +43,32 @@ __device__ inline unsigned int wave_incl_scan(unsigned int x) {
   return x + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
 }
 __device__ inline int wave_incl_scan(int x) { return (int)wave_incl_scan((unsigned int)x); }
+
+// x[l] + x[l ^ M] in every lane l, VALU only: the gfx950 row swaps for M = 16
+// and 32 (with both operands holding x, the two results are the two lanes'
+// values), a DPP row rotation by 8 inside 16-lane rows for M = 8. Float
+// addition is commutative, so both lanes of a pair get the same bits.
+template <int M>
+__device__ inline float xor_add(float x) {
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    static_assert(M == 8, "xor distances 8, 16, 32");
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  }
+}
+
+// The value lane `src` holds, in every lane (src wave-uniform), VALU only.
+__device__ inline unsigned int lane_value(unsigned int v, int src) {
+  return (unsigned int)__builtin_amdgcn_readlane((int)v, src);
+}
+__device__ inline u64 lane_value(u64 v, int src) {
+  return (u64)lane_value((unsigned int)v, src) | ((u64)lane_value((unsigned int)(v >> 32), src) << 32);
+}
 __device__ inline u64 wave_incl_scan(u64 x) {
   auto shr = [](u64 v, auto c) {
     constexpr int CTRL = decltype(c)::value;
