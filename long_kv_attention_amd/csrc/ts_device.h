@@ -3,8 +3,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
 namespace ts {
 
 typedef unsigned long long u64;
@@ -21,6 +19,14 @@ __device__ inline void bar() {
 
 __device__ inline u64 lanemask_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
 
+// The value lane `src` holds, in every lane (src wave-uniform), VALU only.
+__device__ inline unsigned int lane_value(unsigned int v, int src) {
+  return (unsigned int)__builtin_amdgcn_readlane((int)v, src);   // readlane's int, widened unsigned
+}
+__device__ inline u64 lane_value(u64 v, int src) {
+  return (u64)lane_value((unsigned int)v, src) | ((u64)lane_value((unsigned int)(v >> 32), src) << 32);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave, with no LDS round trip:
 // Hillis-Steele steps inside each 16-lane row by DPP row shifts (1, 2, 4, 8;
 // a lane shifted in from outside its row adds 0), then each lane adds the
@@ -31,18 +37,23 @@ template <int CTRL>
 __device__ inline unsigned int dpp_zero(unsigned int v) {
   return (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
-__device__ inline unsigned int wave_incl_scan(unsigned int x) {
+template <int CTRL>
+__device__ inline u64 dpp_zero(u64 v) {
+  return (u64)dpp_zero<CTRL>((unsigned int)v) | ((u64)dpp_zero<CTRL>((unsigned int)(v >> 32)) << 32);
+}
+template <typename T>
+__device__ inline T wave_incl_scan_t(T x) {
   x += dpp_zero<0x111>(x);   // row_shr:1
   x += dpp_zero<0x112>(x);   // row_shr:2
   x += dpp_zero<0x114>(x);   // row_shr:4
   x += dpp_zero<0x118>(x);   // row_shr:8
-  const unsigned int r0 = (unsigned int)__builtin_amdgcn_readlane(x, 15);
-  const unsigned int r1 = (unsigned int)__builtin_amdgcn_readlane(x, 31);
-  const unsigned int r2 = (unsigned int)__builtin_amdgcn_readlane(x, 47);
+  const T r0 = lane_value(x, 15), r1 = lane_value(x, 31), r2 = lane_value(x, 47);
   const unsigned int lane = threadIdx.x & 63;
-  return x + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+  return x + (lane >= 16 ? r0 : T(0)) + (lane >= 32 ? r1 : T(0)) + (lane >= 48 ? r2 : T(0));
 }
-__device__ inline int wave_incl_scan(int x) { return (int)wave_incl_scan((unsigned int)x); }
+__device__ inline unsigned int wave_incl_scan(unsigned int x) { return wave_incl_scan_t(x); }
+__device__ inline u64 wave_incl_scan(u64 x) { return wave_incl_scan_t(x); }
+__device__ inline int wave_incl_scan(int x) { return (int)wave_incl_scan_t((unsigned int)x); }
 
 // x[l] + x[l ^ M] in every lane l, VALU only: the gfx950 row swaps for M = 16
 // and 32 (with both operands holding x, the two results are the two lanes'
@@ -60,31 +71,6 @@ __device__ inline float xor_add(float x) {
     static_assert(M == 8, "xor distances 8, 16, 32");
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
   }
-}
-
-// The value lane `src` holds, in every lane (src wave-uniform), VALU only.
-__device__ inline unsigned int lane_value(unsigned int v, int src) {
-  return (unsigned int)__builtin_amdgcn_readlane((int)v, src);
-}
-__device__ inline u64 lane_value(u64 v, int src) {
-  return (u64)lane_value((unsigned int)v, src) | ((u64)lane_value((unsigned int)(v >> 32), src) << 32);
-}
-__device__ inline u64 wave_incl_scan(u64 x) {
-  auto shr = [](u64 v, auto c) {
-    constexpr int CTRL = decltype(c)::value;
-    return (u64)dpp_zero<CTRL>((unsigned int)v) | ((u64)dpp_zero<CTRL>((unsigned int)(v >> 32)) << 32);
-  };
-  x += shr(x, std::integral_constant<int, 0x111>{});
-  x += shr(x, std::integral_constant<int, 0x112>{});
-  x += shr(x, std::integral_constant<int, 0x114>{});
-  x += shr(x, std::integral_constant<int, 0x118>{});
-  auto at = [&](int l) {   // readlane returns a signed int: widen it unsigned
-    return (u64)(unsigned int)__builtin_amdgcn_readlane((unsigned int)x, l) |
-           ((u64)(unsigned int)__builtin_amdgcn_readlane((unsigned int)(x >> 32), l) << 32);
-  };
-  const u64 r0 = at(15), r1 = at(31), r2 = at(47);
-  const unsigned int lane = threadIdx.x & 63;
-  return x + (lane >= 16 ? r0 : 0ull) + (lane >= 32 ? r1 : 0ull) + (lane >= 48 ? r2 : 0ull);
 }
 
 #define LDS_AS __attribute__((address_space(3)))
