@@ -74,9 +74,15 @@ struct Cfg {
   static constexpr int LANES_PER_ROW = ROWB / 16;
   static constexpr int DMA_PER_TENSOR = TN / ROWS_PER_DMA;
   static constexpr int DMA_PER_STAGE = 2 * DMA_PER_TENSOR;
-  static constexpr int DMA_MIN_PER_WAVE = DMA_PER_STAGE / NW;  // every wave issues at least this many
-  static constexpr int DMA_T_PER_WAVE = (DMA_PER_TENSOR + NW - 1) / NW;  // per tensor, at most
-  static constexpr int DMA_T_MIN = DMA_PER_TENSOR / NW;                  // per tensor, at least
+  // Copies are issued by the first NI waves. With two waves per SIMD the
+  // first four (one per SIMD) take them all: a copy's issue can stall for
+  // tens of cycles while the memory pipeline is full, and the waves created
+  // first win the SIMD's issue arbitration and arrive at every barrier early,
+  // so those stalls stay off the later waves' path.
+  static constexpr int NI = NW >= 8 ? NW / 2 : NW;
+  static constexpr int DMA_MIN_PER_WAVE = DMA_PER_STAGE / NI;  // every issuing wave issues at least this many
+  static constexpr int DMA_T_PER_WAVE = (DMA_PER_TENSOR + NI - 1) / NI;  // per tensor, at most
+  static constexpr int DMA_T_MIN = DMA_PER_TENSOR / NI;                  // per tensor, at least
   static constexpr int ROWS_PER_BLOCK = RG * TPW * 16;
   static constexpr int KV_BYTES = STAGES * STAGE_BYTES;
   static constexpr int Q_BYTES = ROWS_PER_BLOCK * ROWB;    // the block's query rows
@@ -103,7 +109,7 @@ struct Cfg {
   static constexpr int MERGE_RT = MERGE_LDS / (NW * MSLOT) < TPW ? MERGE_LDS / (NW * MSLOT) : TPW;
   static_assert(MERGE_BYTES <= KV_BYTES, "split-local merge reuses the K/V ring");
   static_assert(CT % PG == 0, "merge splits the channel tiles evenly over position groups");
-  static_assert(DMA_MIN_PER_WAVE >= 1, "every wave takes part in staging");
+  static_assert(DMA_MIN_PER_WAVE >= 1, "every issuing wave takes part in staging");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 };
 
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 
   // ---- DMA staging of K and V tiles into ring slot tile % STAGES ----
   // Instruction j of a tensor covers ROWS_PER_DMA rows (j < DMA_PER_TENSOR),
-  // wave w issuing j = w, w + NW, ... Lane l writes physical chunk
+  // issuing wave w (w < NI) taking j = w, w + NI, ... Lane l writes physical chunk
   // l % LANES_PER_ROW of its row; it fetches the logical chunk that the
   // swizzle maps there (K: chunk ^ row, V: chunk ^ 2*row, both mod NCH), which
   // keeps the later fragment reads conflict-free. The per-lane byte offsets
@@ -224,20 +230,21 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   const int dma_row = lane / C::LANES_PER_ROW;
   const int dma_pc = lane % C::LANES_PER_ROW;
   const int64_t row_bytes = p.s_pos * 2;
-  // When a wave's successive copies are NW * ROWS_PER_DMA rows apart and that
+  // When a wave's successive copies are NI * ROWS_PER_DMA rows apart and that
   // is a multiple of the swizzle period, the lane offsets repeat and only a
   // uniform row offset (the copy's scalar offset) changes: one VGPR per tensor.
-  constexpr bool UNIFORM_STEP = (C::NW * C::ROWS_PER_DMA) % C::NCH == 0;
+  constexpr bool UNIFORM_STEP = (C::NI * C::ROWS_PER_DMA) % C::NCH == 0;
   constexpr int NOFF = UNIFORM_STEP ? 1 : C::DMA_T_PER_WAVE;
   unsigned int koff[NOFF], voff[NOFF];
 #pragma unroll
   for (int jj = 0; jj < NOFF; ++jj) {
-    const int r = (wave + jj * C::NW) * C::ROWS_PER_DMA + dma_row;
+    const int r = (wave + jj * C::NI) * C::ROWS_PER_DMA + dma_row;
     koff[jj] = (unsigned int)(r * row_bytes) + ((dma_pc ^ (r & (C::NCH - 1))) << 4);
     voff[jj] = (unsigned int)(r * row_bytes) + ((dma_pc ^ ((2 * r) & (C::NCH - 1))) << 4);
   }
-  const unsigned int jj_step = (unsigned int)(C::NW * C::ROWS_PER_DMA * row_bytes);
+  const unsigned int jj_step = (unsigned int)(C::NI * C::ROWS_PER_DMA * row_bytes);
   auto issue = [&](int tile, bool is_v) {
+    if (wave >= C::NI) return;
     const unsigned int slot = ring_off + (unsigned int)((tile % STAGES) * C::STAGE_BYTES + (is_v ? C::TILE_BYTES : 0));
     const int64_t tile_bytes = (int64_t)tile * TN * row_bytes;
     const int64_t rem = (int64_t)(rows_total - tile * TN) * row_bytes;
@@ -245,8 +252,8 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     const i32x4 desc = buffer_desc(reinterpret_cast<const unsigned char*>(is_v ? vbase : kbase) + tile_bytes, nrec);
 #pragma unroll
     for (int jj = 0; jj < C::DMA_T_PER_WAVE; ++jj) {
-      const int j = wave + jj * C::NW;
-      if (C::DMA_PER_TENSOR % C::NW == 0 || j < C::DMA_PER_TENSOR)
+      const int j = wave + jj * C::NI;
+      if (C::DMA_PER_TENSOR % C::NI == 0 || j < C::DMA_PER_TENSOR)
         dma16_nt(desc, is_v ? voff[UNIFORM_STEP ? 0 : jj] : koff[UNIFORM_STEP ? 0 : jj],
                  UNIFORM_STEP ? jj * jj_step : 0u, slot + j * 1024);
     }
@@ -284,10 +291,10 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       if (id / C::NCH >= q_rows) *reinterpret_cast<u32x4*>(qlds + id * 16) = u32x4{0u, 0u, 0u, 0u};
     const i32x4 qdesc = buffer_desc(p.q + ((int64_t)g * M + rt_blk * 16) * D, (unsigned int)(q_rows * C::ROWB));
 #pragma unroll
-    for (int jj = 0; jj < (QD + C::NW - 1) / C::NW; ++jj) {
-      const int j = wave + jj * C::NW;
+    for (int jj = 0; jj < (QD + C::NI - 1) / C::NI; ++jj) {
+      const int j = wave + jj * C::NI;
       const int r = j * C::ROWS_PER_DMA + dma_row;
-      if (QD % C::NW == 0 || j < QD)
+      if (wave < C::NI && (QD % C::NI == 0 || j < QD))
         dma16(qdesc, (unsigned int)(r * C::ROWB + ((dma_pc ^ (r & (C::NCH - 1))) << 4)), ring_off + C::KV_BYTES + j * 1024);
     }
   }
@@ -347,9 +354,11 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   //   K(t0) V(t0) ... K(t0+S-2) V(t0+S-2) K(t0+S-1) | V(t0+S-1) K(t0+S) | V(t0+S) K(t0+S+1) | ...
   // K(i) is waited for before S of tile i, V(i) only before P V, so V(i)
   // lands while S is computed. Copies issued after K(i): at most S-1 K tiles
-  // and S-1 V tiles (V(i) among them); after V(i): S-1 of each. A wave issues
-  // at least DMA_T_MIN copies per tensor tile, so waiting down to that many
-  // per later tile lands the tile while the later copies stay in flight.
+  // and S-1 V tiles (V(i) among them); after V(i): S-1 of each. An issuing
+  // wave issues at least DMA_T_MIN copies per tensor tile, so waiting down to
+  // that many per later tile lands the tile while the later copies stay in
+  // flight. The other waves have no copies outstanding (their waits pass at
+  // once) and see the tile through the barrier that follows each wait.
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (t_begin + st < t_end) {
