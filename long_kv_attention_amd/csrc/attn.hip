@@ -92,7 +92,10 @@ struct Cfg {
   static constexpr bool Q_REG = NW >= 8 && TPW <= 3;
   // With three or more row groups, each V fragment would be converted bf16 ->
   // f16 by that many waves: convert the tile once in LDS instead (one more
-  // barrier per tile; measured: T = 64 shapes -6%, no gain at RG = 2).
+  // barrier per tile; measured: T = 64 shapes -6% with every wave converting a
+  // share before the softmax, a further -3% with the issuing waves converting
+  // and the barrier after the softmax; at RG = 2 either form is slower than
+  // converting in registers).
   static constexpr bool V_SHARED = RG >= 3;
   static constexpr int ANC_BYTES = 2048;  // ancestor words of the tree nodes (two 64-lane copies)
   // fused scores: the row sums of row groups 1.. for row group 0 (32 positions per wave)
@@ -453,20 +456,30 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         if (tile * TN + ch / C::NCH >= rows_total) *reinterpret_cast<u32x4*>(vw + ch * 16) = u32x4{0u, 0u, 0u, 0u};
       __syncthreads();
     }
-    if constexpr (C::V_SHARED) {   // V(tile) bf16 -> f16 in place, each wave a share
-      unsigned char* vw = lds + (tile % STAGES) * C::STAGE_BYTES + C::TILE_BYTES;
-      constexpr int NCHK = C::TILE_BYTES / 16;
-      constexpr int CPL = (NCHK + C::NT - 1) / C::NT;
-      u32x4 w[CPL];
+    if constexpr (C::V_SHARED) {
+      // V(tile) bf16 -> f16 in place, by the issuing waves only: the later
+      // waves go on to their softmax meanwhile, and the barrier that makes
+      // the converted tile visible comes after the softmax.
+      if (wave < C::NI) {
+        unsigned char* vw = lds + (tile % STAGES) * C::STAGE_BYTES + C::TILE_BYTES;
+        constexpr int NTI = C::NI * 64;
+        constexpr int NCHK = C::TILE_BYTES / 16;
+        constexpr int CPL = (NCHK + NTI - 1) / NTI;
+        constexpr int BAT = CPL < 4 ? CPL : 4;   // chunks in registers at a time
+        static_assert(CPL % BAT == 0, "conversion batches");
 #pragma unroll
-      for (int i = 0; i < CPL; ++i)
-        if (NCHK % C::NT == 0 || tid + i * C::NT < NCHK) w[i] = *reinterpret_cast<const u32x4*>(vw + (tid + i * C::NT) * 16);
+        for (int i0 = 0; i0 < CPL; i0 += BAT) {
+          u32x4 w[BAT];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i)
-        if (NCHK % C::NT == 0 || tid + i * C::NT < NCHK)
-          *reinterpret_cast<u32x4*>(vw + (tid + i * C::NT) * 16) =
-              u32x4{bf16x2_to_f16x2(w[i].x), bf16x2_to_f16x2(w[i].y), bf16x2_to_f16x2(w[i].z), bf16x2_to_f16x2(w[i].w)};
-      bar();
+          for (int i = 0; i < BAT; ++i)
+            if (NCHK % NTI == 0 || tid + (i0 + i) * NTI < NCHK) w[i] = *reinterpret_cast<const u32x4*>(vw + (tid + (i0 + i) * NTI) * 16);
+#pragma unroll
+          for (int i = 0; i < BAT; ++i)
+            if (NCHK % NTI == 0 || tid + (i0 + i) * NTI < NCHK)
+              *reinterpret_cast<u32x4*>(vw + (tid + (i0 + i) * NTI) * 16) =
+                  u32x4{bf16x2_to_f16x2(w[i].x), bf16x2_to_f16x2(w[i].y), bf16x2_to_f16x2(w[i].z), bf16x2_to_f16x2(w[i].w)};
+        }
+      }
     }
 
     // ---- tree mask and tail (only tiles reaching past the context) ----
@@ -537,6 +550,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, f, lsum[t], 0, 0, 0);
     }
 
+    if constexpr (C::V_SHARED) bar();   // the converted V tile
     // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads, f16 from the shared
     //      conversion or bf16 -> f16 in registers) ----
     {
