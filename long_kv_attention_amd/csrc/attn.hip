@@ -513,17 +513,22 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     // Row tiles past M hold zero queries and are computed like the others (their
     // results are never stored), so the tile body has no per-tile branches and
     // the scheduler can overlap one tile's exponentials with another's MFMAs.
+    // A row's four lanes hold the same threshold, so whether any row must
+    // rescale follows from each lane's own maximum: the row maximum across
+    // the four lanes is formed only on the rare tiles that rescale.
     float mx[TPW];
     bool bump_any = false;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      mx[t] = group4_max(lane_max8(s[t][0], s[t][1]));
+      mx[t] = lane_max8(s[t][0], s[t][1]);
       bump_any |= mx[t] > thr(t);
     }
     // Lazy rescale: the reference max only moves when the tile max exceeds it
     // by more than 2^8 in probability, so p = exp2(s*c - m*c) stays <= 256
     // (exact enough in f16) and the O rescale is rare.
     if (__ballot(bump_any)) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) mx[t] = group4_max(mx[t]);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const bool bump = mx[t] > thr(t);
