@@ -91,11 +91,12 @@ struct Cfg {
   // read them from LDS each tile (registers are short).
   static constexpr bool Q_REG = NW >= 8 && TPW <= 3;
   // With three or more row groups, each V fragment would be converted bf16 ->
-  // f16 by that many waves: convert the tile once in LDS instead (one more
-  // barrier per tile; measured: T = 64 shapes -6% with every wave converting a
-  // share before the softmax, a further -3% with the issuing waves converting
-  // and the barrier after the softmax; at RG = 2 either form is slower than
-  // converting in registers).
+  // f16 by that many waves: convert the tile once in LDS instead (measured:
+  // T = 64 shapes -6% with every wave converting a share and a barrier before
+  // the softmax, a further -3% with the issuing waves converting and the
+  // barrier after the softmax, and -4% more with a counter of converted
+  // shares in place of that barrier; at RG = 2 converting in registers is
+  // faster).
   static constexpr bool V_SHARED = RG >= 3;
   static constexpr int ANC_BYTES = 2048;  // ancestor words of the tree nodes (two 64-lane copies)
   // fused scores: the row sums of row groups 1.. for row group 0 (32 positions per wave)
@@ -105,10 +106,12 @@ struct Cfg {
   static constexpr int CT_OUT = PG > 1 ? CT - CT / PG : CT;
   static constexpr int MSLOT = 64 * CT_OUT * 16 + 2 * 16 * 4;   // one wave's parked O^T of a row tile + m, l
   static constexpr int MERGE_BYTES = PG * RG * MSLOT;
-  static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES + ANC_BYTES + SC_BYTES;
+  // converted-tile counter of the shared V conversion
+  static constexpr int CNT_BYTES = V_SHARED ? 16 : 0;
+  static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES + ANC_BYTES + SC_BYTES + CNT_BYTES;
   // row tiles merged per round at the end of a split (all of LDS is free then)
   // (the score slots stay out of it: row group 0 may still read them)
-  static constexpr int MERGE_LDS = LDS_BYTES - SC_BYTES;
+  static constexpr int MERGE_LDS = LDS_BYTES - SC_BYTES - CNT_BYTES;
   static constexpr int MERGE_RT = MERGE_LDS / (NW * MSLOT) < TPW ? MERGE_LDS / (NW * MSLOT) : TPW;
   static_assert(MERGE_BYTES <= KV_BYTES, "split-local merge reuses the K/V ring");
   static_assert(CT % PG == 0, "merge splits the channel tiles evenly over position groups");
@@ -333,6 +336,10 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   // one after the loop) and stores; the slots are rewritten only after the
   // following second barrier.
   float* const sc_lds = reinterpret_cast<float*>(alds + C::ANC_BYTES);
+  unsigned int* const vcnt = reinterpret_cast<unsigned int*>(alds + C::ANC_BYTES + C::SC_BYTES);
+  const unsigned int cnt_lds = ring_off + (unsigned int)(C::KV_BYTES + C::Q_BYTES + C::ANC_BYTES + C::SC_BYTES);
+  if constexpr (C::V_SHARED)
+    if (tid == 0) *vcnt = 0u;   // seen by every wave through the first tile's barrier
   float sig_keep = 0.f;
   auto score_slot = [&]() {
     const int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -479,6 +486,9 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
               *reinterpret_cast<u32x4*>(vw + (tid + (i0 + i) * NTI) * 16) =
                   u32x4{bf16x2_to_f16x2(w[i].x), bf16x2_to_f16x2(w[i].y), bf16x2_to_f16x2(w[i].z), bf16x2_to_f16x2(w[i].w)};
         }
+        // this wave's share is written: count it (LDS operations of a wave complete in order)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0) __hip_atomic_fetch_add(vcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
 
@@ -555,7 +565,21 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, f, lsum[t], 0, 0, 0);
     }
 
-    if constexpr (C::V_SHARED) bar();   // the converted V tile
+    if constexpr (C::V_SHARED) {
+      // Wait until every issuing wave has counted its share of this tile's
+      // conversion, instead of a barrier: the issuing waves go on to P V while
+      // the later waves still run their softmax. Bounded (the shares are
+      // written right after the tile's second barrier, long before any wave
+      // gets here), so a wave never waits without end.
+      const unsigned int want = (unsigned int)(C::NI * (tile - t_begin + 1));
+      for (int spin = 0; spin < (1 << 16); ++spin) {
+        unsigned int v;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(cnt_lds) : "memory");
+        if (__builtin_amdgcn_readfirstlane(v) >= want) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      asm volatile("" ::: "memory");
+    }
     // ---- O^T += V^T P^T (V^T fragments by LDS transpose reads, f16 from the shared
     //      conversion or bf16 -> f16 in registers) ----
     {
