@@ -525,6 +525,11 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       }
     }
 
+    // the count of converted V shares, read now and used before P V (the
+    // read's latency passes during the softmax)
+    unsigned int cnt_seen = 0u;
+    if constexpr (C::V_SHARED)
+      cnt_seen = *(volatile LDS_AS unsigned int*)(LDS_AS unsigned char*)(unsigned char*)vcnt;
     // ---- tree mask and tail (only tiles reaching past the context) ----
     if ((tile + 1) * TN > n_ctx) {
       // a = offset into the tree rows; visible iff a committed row (a < 0)
@@ -605,7 +610,8 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       // written right after the tile's second barrier, long before any wave
       // gets here), so a wave never waits without end.
       const unsigned int want = (unsigned int)(C::NI * (tile - t_begin + 1));
-      for (int spin = 0; spin < (1 << 16); ++spin) {
+      // (the count read before the softmax is normally complete already)
+      for (int spin = 0; spin < (1 << 16) && __builtin_amdgcn_readfirstlane(cnt_seen) < want; ++spin) {
         unsigned int v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(cnt_lds) : "memory");
         if (__builtin_amdgcn_readfirstlane(v) >= want) break;
