@@ -106,8 +106,9 @@ struct Cfg {
   static constexpr int CT_OUT = PG > 1 ? CT - CT / PG : CT;
   static constexpr int MSLOT = 64 * CT_OUT * 16 + 2 * 16 * 4;   // one wave's parked O^T of a row tile + m, l
   static constexpr int MERGE_BYTES = PG * RG * MSLOT;
-  // converted-tile counter of the shared V conversion
-  static constexpr int CNT_BYTES = V_SHARED ? 16 : 0;
+  // count of the V tile's converted shares (shared conversion) or landed
+  // copies (two row groups without score sums), read by every wave before P V
+  static constexpr int CNT_BYTES = V_SHARED || (!SCORE && NW >= 8) ? 16 : 0;
   static constexpr int LDS_BYTES = KV_BYTES + Q_BYTES + ANC_BYTES + SC_BYTES + CNT_BYTES;
   // row tiles merged per round at the end of a split (all of LDS is free then)
   // (the score slots stay out of it: row group 0 may still read them)
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   float* const sc_lds = reinterpret_cast<float*>(alds + C::ANC_BYTES);
   unsigned int* const vcnt = reinterpret_cast<unsigned int*>(alds + C::ANC_BYTES + C::SC_BYTES);
   const unsigned int cnt_lds = ring_off + (unsigned int)(C::KV_BYTES + C::Q_BYTES + C::ANC_BYTES + C::SC_BYTES);
-  if constexpr (C::V_SHARED)
+  if constexpr (C::CNT_BYTES > 0)
     if (tid == 0) *vcnt = 0u;   // seen by every wave through the first tile's barrier
   float sig_keep = 0.f;
   auto score_slot = [&]() {
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       if (st > 0) issue(t_begin + st, false);   // K of the first tile went out first
       issue(t_begin + st, true);
     }
-  // One barrier per tile (shared V conversion without score sums, whose
+  // One barrier per tile (every eight-wave shape without score sums, whose
   // parked sums follow the two-barrier schedule): K and V of tile i+STAGES-1
   // go out together after the barrier of tile i, when every wave is done with
   // tile i-1 and its slot, so no second barrier is needed to refill a K slot
@@ -384,8 +385,12 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   // other waves see the converted tile through the counter below. The
   // issuing waves request the next pair only after their share of the
   // conversion, so the counter is complete before the other waves need it
-  // (14B -10%, 1.5B -4%, T = 64 -2%).
-  constexpr bool ONEBAR = C::V_SHARED && !SCORE;
+  // (14B -10%, 1.5B -4%, T = 64 -2%). With two row groups (each wave converts
+  // its V fragments in registers) the issuing waves count their landed V
+  // copies instead, before requesting the next pair (T = 24 at 100K -1.7 us,
+  // at 8K -0.7 us, although K of the next tile then has one tile's lead).
+  constexpr bool VCOUNT = !C::V_SHARED && !SCORE && C::NW >= 8;
+  constexpr bool ONEBAR = (C::V_SHARED && !SCORE) || VCOUNT;
   if (!ONEBAR && t_begin + STAGES - 1 < t_end) issue(t_begin + STAGES - 1, false);
 
   constexpr int NK = C::DMA_T_MIN, VS = STAGES - 2;
@@ -484,6 +489,17 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         if (tile * TN + ch / C::NCH >= rows_total) *reinterpret_cast<u32x4*>(vw + ch * 16) = u32x4{0u, 0u, 0u, 0u};
       __syncthreads();
     }
+    if constexpr (VCOUNT) {
+      if (wave < C::NI) {   // this wave's V copies of the tile landed: count them, then the next pair
+        if (later == 0 || VS < 1) wait_vm<0>();
+        else wait_vm<2 * NK>();
+        if (lane == 0) __hip_atomic_fetch_add(vcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (tile + STAGES - 1 < t_end) {
+          issue(tile + STAGES - 1, false);
+          issue(tile + STAGES - 1, true);
+        }
+      }
+    }
     if constexpr (C::V_SHARED) {
       // V(tile) bf16 -> f16 in place, by the issuing waves only: the later
       // waves go on to their softmax meanwhile and wait for the count of
@@ -525,10 +541,10 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       }
     }
 
-    // the count of converted V shares, read now and used before P V (the
-    // read's latency passes during the softmax)
+    // the count of converted V shares (or landed V copies), read now and used
+    // before P V (the read's latency passes during the softmax)
     unsigned int cnt_seen = 0u;
-    if constexpr (C::V_SHARED)
+    if constexpr (C::V_SHARED || VCOUNT)
       cnt_seen = *(volatile LDS_AS unsigned int*)(LDS_AS unsigned char*)(unsigned char*)vcnt;
     // ---- tree mask and tail (only tiles reaching past the context) ----
     if ((tile + 1) * TN > n_ctx) {
@@ -603,12 +619,12 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, f, lsum[t], 0, 0, 0);
     }
 
-    if constexpr (C::V_SHARED) {
+    if constexpr (C::V_SHARED || VCOUNT) {
       // Wait until every issuing wave has counted its share of this tile's
-      // conversion, instead of a barrier: the issuing waves go on to P V while
-      // the later waves still run their softmax. Bounded (the shares are
-      // written right after the tile's second barrier, long before any wave
-      // gets here), so a wave never waits without end.
+      // conversion (or its landed V copies), instead of a barrier: the
+      // issuing waves go on to P V while the later waves still run their
+      // softmax. Bounded (the counts come early in the tile, long before any
+      // wave gets here), so a wave never waits without end.
       const unsigned int want = (unsigned int)(C::NI * (tile - t_begin + 1));
       // (the count read before the softmax is normally complete already)
       for (int spin = 0; spin < (1 << 16) && __builtin_amdgcn_readfirstlane(cnt_seen) < want; ++spin) {
