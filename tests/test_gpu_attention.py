@@ -59,6 +59,8 @@ SHAPES = [
     (8, 2, 128, 65, "ts24"), (32, 8, 128, 1000, "chain4"), (12, 2, 128, 777, "ts24"), (32, 32, 128, 300, "ts24"),
     (40, 8, 128, 1500, "ts64"), (32, 8, 128, 2049, "ts64"), (8, 8, 64, 129, "rand17"), (6, 2, 64, 5000, "rand64"),
     (64, 2, 128, 333, "rand40"), (16, 1, 128, 96, "rand9"), (24, 4, 64, 4097, "ts24"),
+    # the headline grouping with several tiles per split and a ragged last tile
+    (32, 8, 128, 700, "ts24"),
     # trees past 64 nodes (two ancestor words per node)
     (8, 2, 128, 1000, "wide88"), (32, 8, 128, 3001, "wide88"), (8, 2, 64, 77, "rand128"), (4, 1, 128, 200, "chain128"),
     (40, 8, 128, 500, "rand100"), (8, 2, 128, 64, "rand65"),
@@ -88,7 +90,7 @@ def test_shapes_and_trees(shape):
     T = len(parent)
     banner(f"verify Hq={Hq} Hkv={Hkv} d={d} n_ctx={n_ctx} T={T}")
     x = attention_inputs(1000 + n_ctx, Hq, Hkv, d, n_ctx, T, cap=n_ctx + T + 64, poison_tail=True)
-    for n_split in (0, 3):
+    for n_split in (0, 1, 3):   # automatic, one split (every tile in one workgroup), three
         got = _run_verify(x, n_ctx, parent, n_split)
         ref = _oracle(x, n_ctx, parent)
         assert np.isfinite(got).all()
