@@ -359,7 +359,8 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     store_score(tl, v);
   };
 
-  // Ring schedule. K of tile i+STAGES is issued as soon as every wave has
+  // Ring schedule with two barriers per tile (the score variant). K of tile
+  // i+STAGES is issued as soon as every wave has
   // finished S = K Q^T of tile i; V of tile i+STAGES-1 once every wave has
   // finished P V of tile i-1. Issue order per wave is therefore
   //   K(t0) V(t0) ... K(t0+S-2) V(t0+S-2) K(t0+S-1) | V(t0+S-1) K(t0+S) | V(t0+S) K(t0+S+1) | ...
@@ -378,9 +379,9 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     }
   // One barrier per tile (every eight-wave shape without score sums, whose
   // parked sums follow the two-barrier schedule): K and V of tile i+STAGES-1
-  // go out together after the barrier of tile i, when every wave is done with
-  // tile i-1 and its slot, so no second barrier is needed to refill a K slot
-  // (measured: T = 64 -2%, 14B -3%, 1.5B -4%). Each issuing wave converts
+  // go out together during tile i, once every wave is past the barrier of
+  // tile i and so done with tile i-1 and its slot; no second barrier is
+  // needed to refill a K slot (measured: T = 64 -2%, 14B -3%, 1.5B -4%). Each issuing wave converts
   // exactly the V rows its own copies wrote, after waiting for them, and the
   // other waves see the converted tile through the counter below. The
   // issuing waves request the next pair only after their share of the
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       if (later == 0) wait_vm<NK>();
       else if (later == 1 || VS < 2) wait_vm<(1 + 2 * (VS < 1 ? VS : 1)) * NK>();
       else wait_vm<(1 + 2 * (VS < 2 ? VS : 2)) * NK>();
-      __builtin_amdgcn_s_barrier();  // K(tile) landed for every wave; tile-1 done everywhere; the next pair goes out after the V conversion
+      __builtin_amdgcn_s_barrier();  // K(tile) landed for every wave; tile-1 done everywhere
     } else {
       // K(i): later K tiles, plus V(i) and min(S-2, later) more V tiles
       if (later == 0) wait_vm<NK>();
