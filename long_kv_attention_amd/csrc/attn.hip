@@ -388,8 +388,10 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   // conversion, so the counter is complete before the other waves need it
   // (14B -10%, 1.5B -4%, T = 64 -2%). With two row groups (each wave converts
   // its V fragments in registers) the issuing waves count their landed V
-  // copies instead, before requesting the next pair (T = 24 at 100K -1.7 us,
-  // at 8K -0.7 us, although K of the next tile then has one tile's lead).
+  // copies instead (T = 24 at 100K -1.7 us, at 8K -0.7 us); K of the next
+  // tile goes out right after the barrier and V after the count (a further
+  // -0.6 and -0.5 us; both after the count: K then had less than one tile's
+  // lead; both at the barrier: +3 us).
   constexpr bool VCOUNT = !C::V_SHARED && !SCORE && C::NW >= 8;
   constexpr bool ONEBAR = (C::V_SHARED && !SCORE) || VCOUNT;
   if (!ONEBAR && t_begin + STAGES - 1 < t_end) issue(t_begin + STAGES - 1, false);
@@ -404,6 +406,8 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       else if (later == 1 || VS < 2) wait_vm<(1 + 2 * (VS < 1 ? VS : 1)) * NK>();
       else wait_vm<(1 + 2 * (VS < 2 ? VS : 2)) * NK>();
       __builtin_amdgcn_s_barrier();  // K(tile) landed for every wave; tile-1 done everywhere
+      if constexpr (VCOUNT)
+        if (tile + STAGES - 1 < t_end) issue(tile + STAGES - 1, false);
     } else {
       // K(i): later K tiles, plus V(i) and min(S-2, later) more V tiles
       if (later == 0) wait_vm<NK>();
@@ -491,14 +495,14 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       __syncthreads();
     }
     if constexpr (VCOUNT) {
-      if (wave < C::NI) {   // this wave's V copies of the tile landed: count them, then the next pair
-        if (later == 0 || VS < 1) wait_vm<0>();
-        else wait_vm<2 * NK>();
+      if (wave < C::NI) {   // this wave's V copies of the tile landed: count them, then V of the next tile
+        // (K of the next tile went out at the barrier: it may be in flight, with the earlier pairs)
+        if (later == 0) wait_vm<0>();
+        else if (VS < 1) wait_vm<NK>();
+        else if (later == 1) wait_vm<NK>();
+        else wait_vm<3 * NK>();
         if (lane == 0) __hip_atomic_fetch_add(vcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (tile + STAGES - 1 < t_end) {
-          issue(tile + STAGES - 1, false);
-          issue(tile + STAGES - 1, true);
-        }
+        if (tile + STAGES - 1 < t_end) issue(tile + STAGES - 1, true);
       }
     }
     if constexpr (C::V_SHARED) {
