@@ -215,7 +215,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   const int n_ctx = p.n_ctx;
   const int rows_total = n_ctx + T;
   const int ntiles_total = (rows_total + TN - 1) / TN;
-  const int tiles_per_split = p.rows_per_split / TN;   // rows_per_split is a multiple of 128
+  const int tiles_per_split = p.rows_per_split / TN;   // rows_per_split is a multiple of TN
   const int t_begin = split * tiles_per_split;
   const int t_end = min(t_begin + tiles_per_split, ntiles_total);
   const float c = p.scale_log2e;
@@ -800,12 +800,12 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 // the split groups merge across lanes with the gfx950 row / half swaps, in a
 // fixed order (bitwise repeatable). A split's weight is l_s * 2^((m_s - m) c)
 // and its normalised output enters with that weight.
-template <int D>
+template <int D, int U>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   constexpr int CPL = D / 16;               // channels per lane
   constexpr int CG = D / CPL;               // channel groups per row (16)
   constexpr int SG = 64 / CG;               // split groups per wave (4)
-  constexpr int U = 8;                      // splits in flight per lane
+  // U: splits in flight per lane
   static_assert(SG == 4, "one row per wave");
   typedef _Float16 hv __attribute__((ext_vector_type(CPL)));
   const int lane = threadIdx.x & 63;
@@ -887,7 +887,6 @@ struct KernelChoice {
   int rg, pg, tpw;
 };
 
-constexpr int KV_TILE = 128;  // split granularity in positions (a multiple of every kernel's tile)
 
 // Row tiles per KV head -> (row groups, position groups, row tiles per wave).
 // From 4 row tiles on the workgroup has 8 waves (two per SIMD); every choice
@@ -949,6 +948,15 @@ int row_blocks_for(int M) {
   return (nrt + per - 1) / per;
 }
 
+// Split granularity in positions: the K/V tile of the form the rows take
+// (32 positions per position group), so a split ends on a tile boundary and
+// the splits can be spread over every compute unit (the 1.5B shape, 64-position
+// tiles: 121 splits of 13 tiles per KV head instead of 112 of 14).
+int split_tile(int M) {
+  const KernelChoice kc = choose((M + 15) / 16);
+  return 32 * kc.pg;
+}
+
 }  // namespace
 
 int attn_row_blocks(int32_t T, int32_t Hq, int32_t Hkv) { return row_blocks_for((Hq / Hkv) * T); }
@@ -956,7 +964,8 @@ int attn_row_blocks(int32_t T, int32_t Hq, int32_t Hkv) { return row_blocks_for(
 int attn_auto_split(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d) {
   (void)d;
   const int M = (Hq / Hkv) * T;
-  const int ntiles = (rows_total + KV_TILE - 1) / KV_TILE;
+  const int tn = split_tile(M);
+  const int ntiles = (rows_total + tn - 1) / tn;
   const int nz = row_blocks_for(M);
   const int target_wg = 256;  // one resident workgroup on each of 256 compute units
   int s = (target_wg + Hkv * nz - 1) / (Hkv * nz);
@@ -967,15 +976,13 @@ int attn_auto_split(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int3
 
 void attn_split_plan(int32_t rows_total, int32_t T, int32_t Hq, int32_t Hkv, int32_t d,
                      int32_t n_split_req, int32_t* n_split_eff, int32_t* rows_per_split) {
-  (void)T;
-  (void)Hq;
-  (void)Hkv;
-  const int ntiles = (rows_total + KV_TILE - 1) / KV_TILE;
+  const int tn = split_tile((Hq / Hkv) * T);
+  const int ntiles = (rows_total + tn - 1) / tn;
   int s = n_split_req > 0 ? n_split_req : attn_auto_split(rows_total, T, Hq, Hkv, d);
   if (s > ntiles) s = ntiles;
   if (s < 1) s = 1;
   const int tps = (ntiles + s - 1) / s;
-  *rows_per_split = tps * KV_TILE;
+  *rows_per_split = tps * tn;
   *n_split_eff = (ntiles + tps - 1) / tps;
 }
 
@@ -996,10 +1003,19 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {
   hipError_t e = p.d == 128 ? launch_split_d<128>(p, kc, nz, stream) : launch_split_d<64>(p, kc, nz, stream);
   if (e != hipSuccess || p.n_split == 1) return e;
   const dim3 cgrid(p.Hkv * ((p.M + 3) / 4));   // one row per wave, four waves per block
-  if (p.d == 128)
-    hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, p);
+  // eight splits in flight per lane cover 32 splits in one round; more splits
+  // (few KV heads: 112 at the 1.5B shape) take all of a lane's loads at once
+  if (p.n_split <= 32) {
+    if (p.d == 128)
+      hipLaunchKernelGGL((attn_combine_kernel<128, 8>), cgrid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<64, 8>), cgrid, dim3(256), 0, stream, p);
+  } else {
+    if (p.d == 128)
+      hipLaunchKernelGGL((attn_combine_kernel<128, 32>), cgrid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<64, 32>), cgrid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ struct AttnParams {
   int32_t n_ctx, T, Hq, Hkv, d;
   int32_t M;             // rows per KV head = (Hq/Hkv) * T
   int32_t n_split;       // effective number of chunks per KV head
-  int32_t rows_per_split;  // cache rows per split (a multiple of 128)
+  int32_t rows_per_split;  // cache rows per split (a multiple of the kernel's K/V tile)
   float scale_log2e;     // softmax scale * log2(e)
   float* scores;         // [Hkv][n_ctx] grouped scores of the committed rows, or null
   uint64_t anc[256];     // words 2i, 2i+1: bit a set <=> tree node a is i or an ancestor of i
