@@ -267,8 +267,20 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   };
 
   // ---- queries: B operand of S^T = K Q^T, from LDS ----
-  const int rt_blk = blockIdx.z * (RG * TPW);   // first row tile of this block
-  const int rt0 = rt_blk + rg * TPW;            // first row tile of this wave
+  // Row tiles: the nrt tiles of the KV head are shared evenly over the
+  // gridDim.z blocks (at most RG * TPW each), and a block's R tiles go to its
+  // row groups as evenly as possible (contiguous runs, the first R % RG
+  // groups one tile more), so the SIMDs carry nearly the same work: wave w
+  // runs on SIMD w % 4, and with PG = 2 row groups r and r + 2 share two
+  // SIMDs. The 1.5B shape's 9 row tiles go 3 + 2 + 2 + 2 instead of
+  // 3 + 3 + 3 + 0, the 14B shape's 20 as two blocks of 10, not 12 + 8.
+  const int nrt = (M + 15) / 16;
+  const int per_blk = (nrt + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int rt_blk = blockIdx.z * per_blk;                  // first row tile of this block
+  const int R = min(per_blk, nrt - rt_blk);                 // its live row tiles (<= RG * TPW)
+  const int nl = __builtin_amdgcn_readfirstlane(R / RG + (rg < R % RG ? 1 : 0));   // this row group's
+  const int lrt0 = rg * (R / RG) + min(rg, R % RG);         // its first tile within the block
+  const int rt0 = rt_blk + lrt0;                            // its first row tile of the KV head
   // The block's query rows and the tree's ancestor words go to LDS by the
   // same asynchronous copy as K and V, before the K/V prologue: the first
   // tile's wait covers them, and no vector load is left pending into the loop
@@ -282,7 +294,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   if (t_begin < t_end) issue(t_begin, false);
   bool tile_on[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) tile_on[t] = (rt0 + t) * 16 < M;
+  for (int t = 0; t < TPW; ++t) tile_on[t] = t < nl;
   {
     // p is the kernel's only argument, so it starts the kernarg segment; its
     // ancestor words are read there (taking p's address would copy it to scratch)
@@ -398,6 +410,13 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
 
   constexpr int NK = C::DMA_T_MIN, VS = STAGES - 2;
   bf16x8 qreg[C::Q_REG ? TPW : 1][C::KSTEPS];
+  // The tile loop computes NL row tiles per wave: TPW, or (four row groups)
+  // TPW - 1 for the groups with fewer live tiles, so their SIMDs skip the
+  // padded tiles' products and exponentials. Each is one straight loop with
+  // no per-tile branches (tiles past a group's nl, if any, hold zero queries
+  // or another group's rows; their results are never stored).
+  auto tile_loop = [&](auto live) {
+  constexpr int NL = decltype(live)::value;
   for (int tile = t_begin; tile < t_end; ++tile) {
     const int later = min(STAGES - 1, t_end - 1 - tile);   // tiles issued after this one
     if constexpr (ONEBAR) {
@@ -426,10 +445,10 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     if constexpr (C::Q_REG) {
       if (tile == t_begin) {   // the queries have landed with the first K tile
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < NL; ++t)
 #pragma unroll
           for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            const int r = (rg * TPW + t) * 16 + l16;
+            const int r = (lrt0 + t) * 16 + l16;
             qreg[t][ks] = *reinterpret_cast<const bf16x8*>(qlds + r * C::ROWB + (((4 * ks + kg) ^ (r & (C::NCH - 1))) << 4));
           }
       }
@@ -437,7 +456,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     // ---- S^T = K Q^T over this wave's 32 positions ----
     f32x4 s[TPW][2];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NL; ++t) s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       bf16x8 kf[2];
@@ -447,12 +466,12 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         kf[pt] = *reinterpret_cast<const bf16x8*>(kl + row * C::ROWB + (((4 * ks + kg) ^ (row & (C::NCH - 1))) << 4));
       }
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
+      for (int t = 0; t < NL; ++t) {
         bf16x8 qv;
         if constexpr (C::Q_REG) {
           qv = qreg[t][ks];
         } else {
-          const int r = (rg * TPW + t) * 16 + l16;
+          const int r = (lrt0 + t) * 16 + l16;
           qv = *reinterpret_cast<const bf16x8*>(qlds + r * C::ROWB + (((4 * ks + kg) ^ (r & (C::NCH - 1))) << 4));
         }
         s[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qv, s[t][0], 0, 0, 0);
@@ -478,7 +497,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
         for (int j = 0; j < 8; ++j) {
           x[j] = s[0][j >> 2][j & 3];
 #pragma unroll
-          for (int t = 1; t < TPW; ++t) x[j] += s[t][j >> 2][j & 3];
+          for (int t = 1; t < NL; ++t) x[j] += s[t][j >> 2][j & 3];
         }
         const float sig = row16_scatter8(x, l16);
         if constexpr (RG == 1) store_score(tile, sig);
@@ -557,7 +576,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
       // or an ancestor-or-self tree node. Branch-free selects.
       const int a0 = tile * TN + 32 * pg + 4 * kg - n_ctx;
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
+      for (int t = 0; t < NL; ++t) {
         const int row = (rt0 + t) * 16 + l16;
         // bit j of win = tree node a0 + j visible to this row (two words per
         // node: nodes 0-63, 64-127); the lane's positions lie in [a0, a0 + 20)
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     float mx[TPW];
     bool bump_any = false;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
+    for (int t = 0; t < NL; ++t) {
       mx[t] = lane_max8(s[t][0], s[t][1]);
       bump_any |= mx[t] > thr(t);
     }
@@ -597,9 +616,9 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     // (exact enough in f16) and the O rescale is rare.
     if (__ballot(bump_any)) {
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) mx[t] = group4_max(mx[t]);
+      for (int t = 0; t < NL; ++t) mx[t] = group4_max(mx[t]);
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
+      for (int t = 0; t < NL; ++t) {
         const bool bump = mx[t] > thr(t);
         const float m_new = bump ? mx[t] : m_run[t];
         const float alpha = __builtin_amdgcn_exp2f((m_run[t] - m_new) * c);
@@ -612,7 +631,7 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
     }
     f16x8 pfrag[TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
+    for (int t = 0; t < NL; ++t) {
       const float nmc = -m_run[t] * c;
       f16x8 f;
 #pragma unroll
@@ -661,10 +680,18 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
           vf = __builtin_bit_cast(
               f16x8, u32x4{bf16x2_to_f16x2(wb.x), bf16x2_to_f16x2(wb.y), bf16x2_to_f16x2(wb.z), bf16x2_to_f16x2(wb.w)});
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < NL; ++t)
           o[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pfrag[t], o[t][ct], 0, 0, 0);
       }
     }
+  }
+
+  };
+  if constexpr (RG >= 4 && TPW >= 2) {
+    if (nl >= TPW) tile_loop(std::integral_constant<int, TPW>{});
+    else tile_loop(std::integral_constant<int, TPW - 1>{});
+  } else {
+    tile_loop(std::integral_constant<int, TPW>{});
   }
 
   if constexpr (SCORE && RG > 1) {
