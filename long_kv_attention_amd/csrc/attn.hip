@@ -269,17 +269,19 @@ __global__ __launch_bounds__(RG * PG * 64) void attn_split_kernel(const AttnPara
   // ---- queries: B operand of S^T = K Q^T, from LDS ----
   // Row tiles: the nrt tiles of the KV head are shared evenly over the
   // gridDim.z blocks (at most RG * TPW each), and a block's R tiles go to its
-  // row groups as evenly as possible (contiguous runs, the first R % RG
-  // groups one tile more), so the SIMDs carry nearly the same work: wave w
-  // runs on SIMD w % 4, and with PG = 2 row groups r and r + 2 share two
-  // SIMDs. The 1.5B shape's 9 row tiles go 3 + 2 + 2 + 2 instead of
-  // 3 + 3 + 3 + 0, the 14B shape's 20 as two blocks of 10, not 12 + 8.
+  // row groups as evenly as possible (contiguous runs; the last R % RG
+  // groups, whose waves issue no copies, take one tile more), so the SIMDs
+  // carry nearly the same work: wave w runs on SIMD w % 4, and with PG = 2
+  // row groups r and r + 2 share two SIMDs. The 1.5B shape's 9 row tiles go
+  // 2 + 2 + 2 + 3 instead of 3 + 3 + 3 + 0, the 14B shape's 20 as two blocks
+  // of 10 (2 + 2 + 3 + 3), not 12 + 8.
   const int nrt = (M + 15) / 16;
   const int per_blk = (nrt + (int)gridDim.z - 1) / (int)gridDim.z;
   const int rt_blk = blockIdx.z * per_blk;                  // first row tile of this block
   const int R = min(per_blk, nrt - rt_blk);                 // its live row tiles (<= RG * TPW)
-  const int nl = __builtin_amdgcn_readfirstlane(R / RG + (rg < R % RG ? 1 : 0));   // this row group's
-  const int lrt0 = rg * (R / RG) + min(rg, R % RG);         // its first tile within the block
+  const int xr = RG - R % RG;                               // groups before the ones with a tile more
+  const int nl = __builtin_amdgcn_readfirstlane(R / RG + (rg >= xr ? 1 : 0));   // this row group's
+  const int lrt0 = rg * (R / RG) + max(0, rg - xr);         // its first tile within the block
   const int rt0 = rt_blk + lrt0;                            // its first row tile of the KV head
   // The block's query rows and the tree's ancestor words go to LDS by the
   // same asynchronous copy as K and V, before the K/V prologue: the first
