@@ -64,6 +64,8 @@ SHAPES = [
     # trees past 64 nodes (two ancestor words per node)
     (8, 2, 128, 1000, "wide88"), (32, 8, 128, 3001, "wide88"), (8, 2, 64, 77, "rand128"), (4, 1, 128, 200, "chain128"),
     (40, 8, 128, 500, "rand100"), (8, 2, 128, 64, "rand65"),
+    # row blocks of unequal live row tiles: 25 tiles as 13 + 12, 17 as 9 + 8
+    (8, 2, 128, 777, "rand100"), (8, 2, 64, 1234, "rand68"),
 ]
 
 
