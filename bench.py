@@ -34,9 +34,11 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "tree-verify attn us/layer-step @100K ctx (8B GQA); achieved HBM GB/s vs peak"
 
 # The workload cells of the sweep: the 8B shape over every tree size and
-# context length of its sweep, and the other model classes at 100K rows with
-# their own trees.
+# context length of its sweep, the two wide trees (88 nodes: [1,9,9,9] plus
+# 20 n-gram chains; 128 nodes) at 100K rows, and the other model classes at
+# 100K rows with their own trees.
 SWEEP = [("8b", T, L) for T in (24, 4, 64) for L in (100_000, 65_536, 32_768, 8_192)] + \
+        [("8b", 88, 100_000), ("8b", 128, 100_000)] + \
         [("1.5b", 24, 100_000), ("7b", 24, 100_000), ("14b", 64, 100_000)]
 
 
@@ -105,7 +107,7 @@ def cpu_baselines(cfg, T, n_ctx, budget_s, kernels=("verify", "draft", "select",
     out = {}
     G, Hkv, d = cfg["Hq"] // cfg["Hkv"], cfg["Hkv"], cfg["d"]
     threads = _threads()
-    parent = tree_parent("tokenswift" if T > 4 else "chain", T)
+    parent = tree_parent("chain" if T <= 4 else ("wide" if T > 64 else "tokenswift"), T)   # the GPU step's tree
     if "verify" in kernels:
         x = attention_inputs(cfg["seed"], G, 1, d, n_ctx, T)   # one KV head and its query group
         ts_ = _timed_samples(lambda i: verify_attention(bf16_to_f64(x["q"]), bf16_to_f64(x["k"]), bf16_to_f64(x["v"]),
