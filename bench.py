@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / f16 matrix peak
 METRIC = "tree-verify attn us/layer-step @100K ctx (8B GQA); achieved HBM GB/s vs peak"
 
 # The workload cells of the sweep: the 8B shape over every tree size and
@@ -66,6 +67,12 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def verify_flops(Hq, d, n_ctx, T):
+    """Algorithmic flops of one verification launch: S = Q K^T and P V, two
+    multiply-adds per query row, cache row and channel each."""
+    return 4 * Hq * T * (n_ctx + T) * d
 
 
 def verify_bytes(Hq, Hkv, d, n_ctx, T):
@@ -353,6 +360,18 @@ def run_cell(args, name, T, n_ctx, steps, warmup, copy_bw, cpu_budget, cpu_kerne
         except Exception:
             traffic = None
 
+    # The call's bound by its arithmetic intensity against the ridge (peak flops
+    # over peak bandwidth, 312.5 flop/B): below it the HBM roofline, above it
+    # the matrix cores' (wide trees, the 14B shape).
+    vf = verify_flops(Hq, d, n_ctx, T)
+    if vf / vb <= MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    else:
+        tflops = vf / (verify_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "hbm_GBps": round(achieved, 1), "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4)}
     res = {
         "metric": METRIC,
         "value": round(verify_us, 3),
@@ -372,8 +391,7 @@ def run_cell(args, name, T, n_ctx, steps, warmup, copy_bw, cpu_budget, cpu_kerne
                    "reselect_every": reselect,
                    "fused_scores": bool(args.fused_scores), "eta_sampling": bool(args.eta),
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "roofline": roofline,
         "stream_copy": None if copy_gbps is None else
                        {"GBps": round(copy_gbps, 1), "bytes_per_copy": 2 * (1 << 30),
                         "verify_frac_of_copy": round(achieved / copy_gbps, 4)},
@@ -385,7 +403,7 @@ def run_cell(args, name, T, n_ctx, steps, warmup, copy_bw, cpu_budget, cpu_kerne
                        "select_per_layer_per_step": round(select_us / reselect, 3),
                        "penalty_per_step": round(penalty_us, 3),
                        "accept_commit_per_step": round(commit_us, 3), "ngram_tree_per_step": round(ngram_us, 3),
-                       "verify_bytes_per_launch": vb},
+                       "verify_bytes_per_launch": vb, "verify_flops_per_launch": vf},
         "ms_per_step_with_reselect_cadence": round(step_ms_cadence, 4),
         "wall_s": round(wall, 3),
     }
