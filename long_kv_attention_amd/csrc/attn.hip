@@ -26,9 +26,12 @@
 //                     LDS with ds_read_b64_tr_b16, converted bf16 -> f16 in
 //                     registers (or once per tile in LDS when three or more
 //                     row groups would each convert it).
-//   All global reads are asynchronous copies into LDS (queries first, then a
-//   STAGES-deep K/V ring with separate K and V refills); two barriers per
-//   tile (K landed / previous P V done, and V landed / K reads done).
+//   All global reads are asynchronous copies into LDS (the first K tile, the
+//   queries and the tree's ancestor words, then a STAGES-deep K/V ring).
+//   The eight-wave forms without score sums take one barrier per tile (K of
+//   the tile landed and the previous tile done everywhere) and a count in LDS
+//   of the landed or converted V tile before P V; the others take two (K
+//   landed / previous P V done, and V landed / K reads done).
 //   Splits write (max, sum, normalised output) partials, the output in f16
 //   (half the bytes of the split's stores and the combine's reads); a combine
 //   kernel merges them with the log-sum-exp rule. A single split normalises
