@@ -772,7 +772,10 @@ int select_blocks_per_head(int32_t n_ctx, int32_t Hkv, int32_t n_sink, int32_t n
   const int lo = n_sink < n_ctx ? n_sink : n_ctx;
   const int hi = n_ctx - n_recent > lo ? n_ctx - n_recent : lo;
   const int n = hi - lo;
-  int nb = (256 + Hkv - 1) / Hkv;           // about one block per compute unit over all heads
+  // about two blocks per compute unit over all heads (the emit pass holds two
+  // per CU): with many KV heads each block's share of the ranking and the
+  // gather halves (32 heads: 183 against 193 µs per call); no change at 8 heads
+  int nb = (512 + Hkv - 1) / Hkv;
   const int by_rows = (n + 1023) / 1024;    // at least 1024 rows per block
   if (nb > by_rows) nb = by_rows;
   if (nb > NB_MAX) nb = NB_MAX;
