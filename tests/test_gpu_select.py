@@ -121,11 +121,12 @@ def test_crowded_cut_bin_with_long_lists():
 
 
 def test_long_chunks_span_several_sub_chunks():
-    """300K rows over 8 KV heads: each block's chunk (about 9400 rows) spans
-    three 4096-row sub-chunks in the cut-bin and emit passes (later keys
-    reloaded, output runs carried across sub-chunks); sampled heads."""
-    n_ctx, Hq, Hkv = 300_000, 32, 8
-    banner("select 300K rows")
+    """600K rows over 8 KV heads (64 blocks per head): each block's chunk
+    (about 9400 rows) spans three 4096-row sub-chunks in the cut-bin and emit
+    passes (later keys reloaded, output runs carried across sub-chunks);
+    sampled heads."""
+    n_ctx, Hq, Hkv = 600_000, 32, 8
+    banner("select 600K rows")
     x = attention_inputs(31, Hq, Hkv, 128, n_ctx, 24)
     _check(x, n_ctx, Hq, Hkv, 4, 4096, 64, heads=[0, 7])
 
@@ -182,7 +183,7 @@ def test_full_budget_draft_equals_verification():
 
 
 @pytest.mark.parametrize("Hq,Hkv,n_ctx,budget,T", [
-    (32, 32, 33_333, 4096, 24),   # the 7B layout: 8 blocks per head, chunks of two sub-chunks
+    (32, 32, 66_666, 4096, 24),   # the 7B layout: 16 blocks per head, chunks of two sub-chunks
     (4, 4, 5000, 700, 24),
     (4, 4, 1000, 100, 1),
     (3, 3, 300, 500, 4),          # budget past the candidates
